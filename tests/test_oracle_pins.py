@@ -1,0 +1,369 @@
+"""Pins for the CPU oracle: each check ties it to something other than itself.
+
+Pins used: hand-worked fixtures under tests/golden (each cites its source),
+closed forms, exhaustive enumeration, brute-force loops over Python integers
+or Fractions on tiny inputs, and library routines where the oracle's step is a
+special case of one (the torch bf16 cast).
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import tabit_oracle as O
+import tabit_synth as S
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        for raw in f:
+            line = raw.split("#", 1)[0].strip()
+            if line:
+                yield line
+
+
+def _bits(vals):
+    """fp32-exact values -> bf16 bit patterns (the values are bf16-exact)."""
+    t = torch.tensor(vals, dtype=torch.float32).to(torch.bfloat16)
+    assert torch.equal(t.float(), torch.tensor(vals, dtype=torch.float32))
+    return S.bf16_bits(t)
+
+
+def _fp32_round(fr: Fraction) -> np.float32:
+    """Correctly rounded fp32 of a positive rational (exact, via neighbours)."""
+    f = np.float32(float(fr))            # within one ulp
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+    best = min(cands, key=lambda c: (abs(Fraction(float(c)) - fr),
+                                     int(np.array(c, np.float32).view(np.uint32)) & 1))
+    return np.float32(best)
+
+
+# ---------------------------------------------------------------- Hadamard
+def test_hadamard_golden_small():
+    mats, cur = {}, None
+    for line in _lines("hadamard_sylvester.txt"):
+        if line.startswith("H"):
+            cur = line
+            mats[cur] = []
+        else:
+            mats[cur].append([int(v) for v in line.split()])
+    for name, rows in mats.items():
+        n = int(name[1:])
+        assert np.array_equal(O.sylvester_hadamard(n), np.array(rows))
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16, 32, 64, 128])
+def test_hadamard_closed_form_and_orthogonality(n):
+    H = O.sylvester_hadamard(n)
+    closed = np.array([[(-1) ** bin(i & j).count("1") for j in range(n)] for i in range(n)])
+    assert np.array_equal(H, closed)
+    assert np.array_equal(H @ H.T, n * np.eye(n, dtype=np.int64))   # H H^T = n I
+    assert np.array_equal(H, H.T)
+
+
+# ---------------------------------------------------------------- FWHT
+@pytest.mark.parametrize("b", [2, 4, 32, 64, 128])
+def test_fwht_equals_blockdiag_matrix_on_small_integers(b):
+    rng = np.random.default_rng(b)
+    K = 4 * b
+    x = rng.integers(-8, 9, size=(5, K))
+    H = np.array([[(-1) ** bin(i & j).count("1") for j in range(b)] for i in range(b)])
+    ref = np.concatenate([x[:, j * b:(j + 1) * b] @ H for j in range(K // b)], axis=1)
+    got = O.block_fwht_f32(x.astype(np.float32), b)
+    assert np.array_equal(got.astype(np.int64), ref)
+
+
+@pytest.mark.parametrize("b", [32, 64, 128])
+def test_fwht_round_trip_and_block_independence(b):
+    rng = np.random.default_rng(7 + b)
+    x = rng.integers(-100, 101, size=(3, 3 * b)).astype(np.float32)
+    y = O.block_fwht_f32(O.block_fwht_f32(x, b), b)
+    assert np.array_equal(y, b * x)               # H H = b I: recovery by orthogonality
+    x2 = x.copy()
+    x2[:, :b] += 1                                # perturb only block 0
+    d = O.block_fwht_f32(x2, b) - O.block_fwht_f32(x, b)
+    assert np.all(d[:, b:] == 0) and np.any(d[:, :b] != 0)
+
+
+def test_fwht_identity_for_block_zero():
+    x = np.random.default_rng(0).standard_normal((2, 64)).astype(np.float32)
+    assert np.array_equal(O.block_fwht_f32(x, 0), x)
+
+
+def test_fwht_stage_order_golden():
+    lines = dict(l.split(" ", 1) for l in _lines("fwht_stage_order.txt"))
+
+    def parse(s):
+        return np.array([math.ldexp(float(m), int(e)) for m, e in
+                         (p.split() for p in s.split("|"))], dtype=np.float32)
+    got = O.block_fwht_f32(parse(lines["input"])[None, :], 4)[0]
+    assert np.array_equal(got.view(np.uint32), parse(lines["output"]).view(np.uint32))
+
+
+def test_rotated_product_identity():
+    """(X H)(W H)^T = b X W^T blockwise (exact on small integers)."""
+    rng = np.random.default_rng(3)
+    for b in (32, 64):
+        X = rng.integers(-5, 6, size=(4, 2 * b))
+        W = rng.integers(-5, 6, size=(6, 2 * b))
+        XH = O.block_fwht_f32(X.astype(np.float32), b).astype(np.int64)
+        WH = O.block_fwht_f32(W.astype(np.float32), b).astype(np.int64)
+        assert np.array_equal(XH @ WH.T, b * (X @ W.T))
+
+
+# ---------------------------------------------------------------- INT8 quantizer
+def test_int8_quant_golden():
+    for line in _lines("int8_quant_worked.txt"):
+        head, xs, qs, sc = [p.strip() for p in line.split("|")]
+        _, b = head.split()
+        x = [float(v) for v in xs.split()]
+        q_ref = np.array([int(v) for v in qs.split()], dtype=np.int8)
+        num, den = (int(v) for v in sc.split())
+        q, s = O.quantize_act_int8(_bits(x)[None, :], int(b))
+        assert np.array_equal(q[0], q_ref), line
+        assert s[0] == _fp32_round(Fraction(num, den)), line
+
+
+def test_int8_quant_properties():
+    rng = np.random.default_rng(11)
+    x = S.gen_activation(37, 256, seed=5)
+    bits = S.bf16_bits(x)
+    for b in (0, 32, 64, 128):
+        q, s = O.quantize_act_int8(bits, b)
+        y = O.block_fwht_f32(O.bf16_to_f32(bits), b)
+        a = np.max(np.abs(y), axis=1)
+        assert np.all(np.abs(q.astype(np.int32)) <= 127)
+        # the element of largest magnitude maps to +-127
+        idx = np.argmax(np.abs(y), axis=1)
+        assert np.all(np.abs(q[np.arange(37), idx].astype(np.int32)) == 127)
+        # every code is within half a step of y * r
+        r = (np.float32(127.0) / a).astype(np.float32)
+        assert np.all(np.abs(y * r[:, None] - q) <= 0.5 + 1e-6)
+        assert np.array_equal(s, (a / np.float32(127)).astype(np.float32))
+    del rng
+
+
+def test_int8_quant_zero_row_and_zero_block():
+    bits = np.zeros((2, 64), dtype=np.uint16)
+    bits[1] = S.bf16_bits(torch.ones(64, dtype=torch.bfloat16))
+    q, s = O.quantize_act_int8(bits, 32)
+    assert np.all(q[0] == 0) and s[0] == 0
+    assert s[1] > 0
+
+
+@pytest.mark.parametrize("b", [4, 16, 64])
+def test_normalization_folds_into_scale(b):
+    """Extracting the 1/sqrt(b) normalization into the fp scale changes no code.
+
+    HQ-DM section 2.1: the normalization leaves the integer core.  For these b,
+    sqrt(b) is a power of two, so the normalized transform is an exact scaling.
+    """
+    x = O.bf16_to_f32(S.bf16_bits(S.gen_activation(9, 4 * b, seed=b)))
+    y = O.block_fwht_f32(x, b)
+    q1, s1 = O._absmax_int8_codes(y)
+    q2, s2 = O._absmax_int8_codes(y / np.float32(math.sqrt(b)))
+    assert np.array_equal(q1, q2)
+    assert np.array_equal(s1, s2 * np.float32(math.sqrt(b)))
+
+
+def test_weight_scale_carries_inverse_block():
+    w = S.bf16_bits(S.gen_weight(8, 128, seed=1))
+    for b in (0, 32, 64):
+        q, s = O.quantize_weights_int8(w, b)
+        qa, sa = O.quantize_act_int8(w, b)
+        assert np.array_equal(q, qa)
+        assert np.array_equal(s, (sa / np.float32(max(b, 1))).astype(np.float32))
+
+
+# ---------------------------------------------------------------- LSB mask
+def test_lsb_golden():
+    for line in _lines("lsb_truncation.txt"):
+        w, k, exp = (int(v) for v in line.split())
+        assert int(O.lsb_truncate(np.array([w], np.int8), k)[0]) == exp, line
+
+
+def test_lsb_exhaustive():
+    w = np.arange(-128, 128, dtype=np.int64)
+    for k in range(8):
+        got = O.lsb_truncate(w.astype(np.int8), k).astype(np.int64)
+        for wi, gi in zip(w.tolist(), got.tolist()):
+            assert gi == (wi >> k) << k                      # arithmetic shift (Python int)
+            byte = (wi & 0xFF) & ((0xFF << k) & 0xFF)         # clear the k low bits of the byte
+            assert gi == (byte - 256 if byte & 0x80 else byte)
+    with pytest.raises(ValueError):
+        O.lsb_truncate(w.astype(np.int8), 8)
+
+
+# ---------------------------------------------------------------- GEMMs
+def _brute_gemm(X, W):
+    return [[sum(int(X[m][k]) * int(W[n][k]) for k in range(len(X[0]))) for n in range(len(W))]
+            for m in range(len(X))]
+
+
+@pytest.mark.parametrize("k", range(8))
+def test_masked_gemm_brute_force(k):
+    X = S.gen_int8((3, 40), seed=1, lo=-127, hi=127)
+    Wq = S.gen_int8((5, 40), seed=2, lo=-127, hi=127)
+    Wt = [[(int(w) >> k) << k for w in row] for row in Wq]
+    ref = _brute_gemm(X, Wt)
+    assert O.masked_gemm_i32(X, Wq, k).tolist() == ref
+    # bit-serial definition over the retained planes, brute force
+    ref_bp = [[sum(int(X[m][kk]) * sum(((int(Wq[n][kk]) & 0xFF) >> b & 1) * (-(1 << 7) if b == 7 else (1 << b))
+                                      for b in range(k, 8)) for kk in range(40)) for n in range(5)]
+              for m in range(3)]
+    assert O.bitplane_gemm_i32(X, Wq, k).tolist() == ref_bp
+
+
+def test_masked_k0_is_plain_int8_gemm():
+    X = S.gen_int8((4, 64), seed=3)
+    W = S.gen_int8((6, 64), seed=4, lo=-128, hi=127)
+    assert O.masked_gemm_i32(X, W, 0).tolist() == _brute_gemm(X, W)
+
+
+def test_bitplane_byte_identity_exhaustive():
+    for w in range(-128, 128):
+        for k in range(8):
+            planes = sum(((w & 0xFF) >> b & 1) * (-(1 << 7) if b == 7 else (1 << b)) for b in range(k, 8))
+            assert planes == (w >> k) << k
+
+
+@pytest.mark.parametrize("k", [0, 3, 5, 7])
+def test_bitplane_equals_masked_random(k):
+    X = S.gen_int8((33, 96), seed=10 + k)
+    W = S.gen_int8((17, 96), seed=20 + k, lo=-128, hi=127)
+    assert np.array_equal(O.bitplane_gemm_i32(X, W, k), O.masked_gemm_i32(X, W, k))
+
+
+def test_accumulator_bound_extreme():
+    K = 7680
+    X = np.full((1, K), -127, np.int8)
+    W = np.full((1, K), -128, np.int8)
+    assert int(O.masked_gemm_i32(X, W, 0)[0, 0]) == 127 * 128 * K
+
+
+# ---------------------------------------------------------------- epilogue
+def test_bf16_rne_matches_torch_cast():
+    rng = np.random.default_rng(5)
+    v = np.concatenate([
+        rng.standard_normal(100_000).astype(np.float32) * np.float32(1e3),
+        # exact ties: low 16 bits = 0x8000, with odd and even kept parts
+        (np.arange(1000, dtype=np.uint32) * np.uint32(0x10000) + np.uint32(0x3F808000)).view(np.float32),
+        np.array([0.0, -0.0, 1.0, -1.0, 3.3895314e38], dtype=np.float32),
+    ])
+    ref = S.bf16_bits(torch.from_numpy(v).to(torch.bfloat16))
+    assert np.array_equal(O.f32_to_bf16_bits(v), ref)
+
+
+def test_dequant_definition():
+    acc = np.array([[3, -5]], np.int32)
+    y = O.dequant(acc, np.array([0.5], np.float32), np.array([2.0, 0.25], np.float32))
+    assert y.tolist() == [[3.0, -0.625]]
+
+
+# ---------------------------------------------------------------- MXFP4
+def _e2m1_table():
+    dec, rnd = {}, []
+    for line in _lines("e2m1_table.txt"):
+        p = line.split()
+        if p[0] == "ROUND":
+            rnd.append((float(p[1]), int(p[2])))
+        else:
+            dec[int(p[0])] = float(p[1])
+    return dec, rnd
+
+
+def test_e2m1_decode_and_rounding_golden():
+    dec, rnd = _e2m1_table()
+    codes = np.arange(16)
+    assert O.e2m1_decode(codes).tolist() == [dec[c] for c in range(16)]
+    for v, c in rnd:
+        assert int(O.e2m1_encode(np.array([v]))[0]) == c, (v, c)
+
+
+def test_e2m1_encode_is_nearest_exhaustive_grid():
+    dec, _ = _e2m1_table()
+    vals = np.arange(-8.0, 8.0, 1 / 64)
+    codes = O.e2m1_encode(vals)
+    for v, c in zip(vals.tolist(), codes.tolist()):
+        d = abs(min(abs(v), 6.0) * (1 if v >= 0 else -1) - dec[c])
+        best = min(abs(min(abs(v), 6.0) * (1 if v >= 0 else -1) - x) for x in dec.values())
+        assert d == best
+
+
+def test_mx_block_golden():
+    lines = {l.split(" ", 1)[0]: l.split(" ", 1)[1] for l in _lines("mx_block_worked.txt")}
+    x = np.zeros((1, 32), np.float32)
+    vals = [float(v) for v in lines["x"].split()]
+    x[0, :len(vals)] = vals
+    packed, e8 = O.mx_quantize_rows(x, 0)
+    assert int(e8[0, 0]) == int(lines["e8m0"])
+    pk = [int(v) for v in lines["packed"].split()]
+    assert packed[0, :len(pk)].tolist() == pk and np.all(packed[0, len(pk):] == 0)
+
+
+def test_mx_scale_range_property():
+    """amax * 2^-X lies in [4, 8) for every nonzero block (OCP MX scale rule)."""
+    x = O.bf16_to_f32(S.bf16_bits(S.gen_activation(16, 256, seed=9)))
+    y = O.block_fwht_f32(x, 32).reshape(16, 8, 32).astype(np.float64)
+    _, e8 = O.mx_quantize_rows(x, 32)
+    amax = np.max(np.abs(y), axis=2)
+    r = amax * np.exp2(-(e8.astype(np.float64) - 127))
+    assert np.all((r >= 4) & (r < 8))
+
+
+def test_mx_zero_block():
+    packed, e8 = O.mx_quantize_rows(np.zeros((1, 64), np.float32), 32)
+    assert np.all(packed == 0) and np.all(e8 == 127)
+
+
+def test_mxfp4_gemm_brute_force_fractions():
+    dec, _ = _e2m1_table()
+    rng = np.random.default_rng(4)
+    xp = rng.integers(0, 256, size=(2, 32), dtype=np.uint8)
+    wp = rng.integers(0, 256, size=(3, 32), dtype=np.uint8)
+    xe = rng.integers(120, 135, size=(2, 2), dtype=np.uint8)
+    we = rng.integers(120, 135, size=(3, 2), dtype=np.uint8)
+
+    def elem(p, e, r, i):
+        byte = int(p[r, i // 2])
+        code = byte & 15 if i % 2 == 0 else byte >> 4
+        return Fraction(dec[code]) * Fraction(2) ** (int(e[r, i // 32]) - 127)
+    got = O.mxfp4_gemm(xp, xe, wp, we, 1 / 32)
+    for m in range(2):
+        for n in range(3):
+            ref = sum(elem(xp, xe, m, i) * elem(wp, we, n, i) for i in range(64)) / 32
+            assert Fraction(got[m, n]) == ref
+
+
+# ---------------------------------------------------------------- schedule + inputs
+def test_schedule_tables_deterministic():
+    for name, fn in S.WORKLOADS.items():
+        a, b = fn(), fn()
+        assert np.array_equal(a.k_bits, b.k_bits) and np.array_equal(a.fmt, b.fmt)
+        assert a.k_bits.shape == (a.steps, a.num_layers)
+        assert a.k_bits.max() <= 7
+    c2 = S.c2_pixart_sigma()
+    # early steps are biased to full precision
+    assert (c2.k_bits[0] == 0).mean() > (c2.k_bits[-1] == 0).mean()
+    c5 = S.c5_cogvideox()
+    assert 0.5 < c5.fmt.mean() < 0.7
+    assert O.schedule_lookup(c2.k_bits, c2.fmt, 3, 7) == (int(c2.k_bits[3, 7]), 0)
+
+
+def test_linear_int8_sanity_unpinned():
+    """Approximation quality vs the fp64 product: sanity only (parity unpinned)."""
+    x = S.gen_activation(16, 256, seed=1)
+    w = S.gen_weight(32, 256, seed=2)
+    ref = x.double().numpy() @ w.double().numpy().T
+    errs = []
+    for k in (0, 2, 4):
+        out = O.linear_int8(S.bf16_bits(x), S.bf16_bits(w), 64, k)
+        errs.append(np.linalg.norm(out["y"] - ref) / np.linalg.norm(ref))
+    assert errs[0] < 0.03 and errs[0] <= errs[1] <= errs[2]
+    out = O.linear_mxfp4(S.bf16_bits(x), S.bf16_bits(w), 32)
+    assert np.linalg.norm(out["y"] - ref) / np.linalg.norm(ref) < 0.3
