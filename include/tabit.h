@@ -1,0 +1,254 @@
+/*
+ * tabit.h -- C ABI of the timestep-adaptive-bit quantized linear for MI355X (gfx950).
+ *
+ * One quantized linear layer of a diffusion transformer whose weight
+ * precision changes per layer and per denoising step:
+ *
+ *   - TASQ (Temporal-Adaptive Bit Sparsification Quantization; gist.science
+ *     technical summary section 2 "Metodologia", and the newx.sg abstract):
+ *     one shared maximum-precision (8-bit) weight buffer is stored; a learned
+ *     per-(layer, stage) LSB mask truncates least-significant bits, giving an
+ *     effective precision of 8 - k without per-stage weight copies; switching
+ *     precision costs nothing because the engine simply reads fewer bit planes.
+ *   - HQ-DM (gist.science technical summary section 2.1): activations are
+ *     rotated by a block-diagonal Hadamard before symmetric quantization; the
+ *     Hadamard normalization is moved into the fp scales so the core is an
+ *     integer matrix product.
+ *   - 6Bit-Diffusion (gist.science technical summary section 2A): per layer
+ *     and step, INT8 for unstable layers or a 4-bit format for stable ones,
+ *     after a local block Hadamard.  The 4-bit format here is OCP MXFP4
+ *     (E2M1 elements, one E8M0 scale per 32), gfx950's native 4-bit format.
+ *
+ * Conventions (apply to every entry point):
+ *   Ownership   The caller allocates and owns every device buffer; the library
+ *               never allocates device memory.  A tabit_ctx owns host state only
+ *               (schedule table, last error text, options).
+ *   Layout      Row-major, K contiguous.  X is [M][K] (tokens x input features),
+ *               W is [N][K] (the nn.Linear layout), Y is [M][N].  bf16 values
+ *               are passed as their uint16_t bit patterns.
+ *   Streams     `stream` is a hipStream_t passed as void* (NULL = default
+ *               stream).  Work is enqueued asynchronously; nothing synchronizes.
+ *               No entry point allocates, frees or memsets, so calls may be
+ *               captured into a HIP graph.
+ *   Errors      Every int-returning call returns TABIT_OK or a negative
+ *               status.  Arguments are validated before any HIP call; a failed
+ *               validation launches nothing.  tabit_last_error(ctx) gives text.
+ *               Faults inside kernels surface at the caller's synchronize.
+ *   Threads     A ctx is not thread-safe; separate ctxs are independent.
+ *   Shapes      M >= 0 (M == 0 is a no-op), K % 32 == 0 and 32 <= K <= 32768,
+ *               N % 32 == 0 (N == 0 is a no-op), K % had_block == 0.
+ *               had_block in {0, 32, 64, 128} (0 = no rotation); the MXFP4
+ *               format takes had_block in {0, 32}.
+ *   Alignment   bf16/int8/fp4 matrices 16-byte aligned; fp32 vectors 4-byte.
+ *   Contract    Activations and weights must be rotated with the same
+ *               had_block; the library cannot detect a mismatch.  Inputs must
+ *               be finite with |x| * had_block below the fp32 range.
+ */
+#ifndef TABIT_H
+#define TABIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct tabit_ctx tabit_ctx;
+
+enum tabit_status {
+  TABIT_OK = 0,
+  TABIT_EINVAL = -1,   /* null pointer, unknown enum value, bad option          */
+  TABIT_ESHAPE = -2,   /* shape constraint violated (K % 32, N % 32, K % b, ...) */
+  TABIT_EALIGN = -3,   /* pointer not aligned as required                        */
+  TABIT_ERANGE = -4,   /* k outside [0, 7], block size not supported            */
+  TABIT_ENOSCHED = -5, /* no schedule installed, or (step, layer) outside it    */
+  TABIT_EHIP = -6,     /* HIP runtime error (launch or attribute query)          */
+  TABIT_ENOMEM = -7    /* host allocation failed                                 */
+};
+
+enum tabit_fmt { TABIT_FMT_INT8 = 0, TABIT_FMT_MXFP4 = 1 };
+enum tabit_path { TABIT_PATH_MASKED = 0, TABIT_PATH_BITSERIAL = 1 };
+
+/* Create / destroy a context (host memory only; makes no HIP call).
+ * tabit_create returns TABIT_EINVAL if out is NULL, TABIT_ENOMEM on failure. */
+int tabit_create(tabit_ctx** out);
+void tabit_destroy(tabit_ctx* ctx);
+
+/* Text of the last error recorded on ctx ("" if none).  The pointer stays valid
+ * until the next call on ctx.  ctx may be NULL (returns a static string). */
+const char* tabit_last_error(const tabit_ctx* ctx);
+
+/* Library version string, e.g. "tabit 0.1.0 gfx950". */
+const char* tabit_version(void);
+
+/*
+ * Offline weight preparation into the single shared buffer.
+ * TASQ section 2 (shared weight representation): one maximum-precision copy.
+ * HQ-DM section 2.1: the block Hadamard; the same block size must be used for
+ * the activations (the weights are rotated here so that both operands of the
+ * INT8 product are integer codes; (XH)(WH)^T = b X W^T, so w_scale carries 1/b).
+ *
+ * Per output row n: y = blockFWHT_b(W[n, :]) in fp32 (stages h = 1, 2, 4, ...),
+ * a = max|y|, codes = clamp(rint(y * (127/a)), -127, 127),
+ * w_scale[n] = (a / 127) / max(b, 1).  A zero row gives codes 0, scale 0.
+ *   w_bf16  device [N][K] bf16 input.
+ *   w_q     device [N][K] int8 output, w_scale device [N] fp32 output.
+ *   w_fp4   device [N][K/2] packed MXFP4 output (element 2i low nibble),
+ *   w_e8m0  device [N][K/32] E8M0 output; the MX copy for layers scheduled to
+ *           4 bits (6Bit-Diffusion section 2A).  Requires had_block in {0, 32}.
+ * Either pair may be NULL (both members of a pair together); not both pairs.
+ */
+int tabit_quantize_weights(tabit_ctx* ctx, const uint16_t* w_bf16, int N, int K, int had_block,
+                           int8_t* w_q, float* w_scale, uint8_t* w_fp4, uint8_t* w_e8m0,
+                           void* stream);
+
+/*
+ * Install the per-(step, layer) precision table (host copy into ctx).
+ * TASQ section 2: the Temporal-Spatial LSB mask M_{t,l} gives each layer and
+ * denoising stage its number k of truncated LSBs.  6Bit-Diffusion section 2A:
+ * INT8 or 4-bit chosen per layer and step.
+ *   k_bits  host [num_steps][num_layers], each in [0, 7] (effective bits 8 - k).
+ *   fmt     host [num_steps][num_layers] of TABIT_FMT_*, or NULL for all INT8.
+ * Makes no HIP call.  Errors: EINVAL (null / bad fmt), ERANGE (k > 7),
+ * ESHAPE (num_steps or num_layers < 1).
+ */
+int tabit_set_step_schedule(tabit_ctx* ctx, int num_steps, int num_layers,
+                            const uint8_t* k_bits, const uint8_t* fmt);
+
+/* Look up (k, fmt) for one (step, layer).  ENOSCHED when no table is
+ * installed or the pair is outside it.  Makes no HIP call. */
+int tabit_schedule_lookup(const tabit_ctx* ctx, int step, int layer, int* k_bits, int* fmt);
+
+/*
+ * Activation quantizer: fused block FWHT + per-token quantization.
+ * HQ-DM section 2.1 (X H, then quantize; unnormalized Hadamard) and section
+ * 2.2 (symmetric); 6Bit-Diffusion section 2A (local block Hadamard first).
+ *   fmt = TABIT_FMT_INT8:  per token m, y = blockFWHT_b(x_m) (fp32),
+ *       a = max|y|, x_q int8 [M][K] = clamp(rint(y * (127/a)), -127, 127),
+ *       x_scale fp32 [M] = a / 127 (0 for a zero row).
+ *   fmt = TABIT_FMT_MXFP4 (had_block 0 or 32): per block of 32, X =
+ *       clamp(floor(log2 amax) - 2, -127, 127); x_scale = uint8 E8M0 [M][K/32]
+ *       holding X + 127 (127 for a zero block); x_q = packed E2M1 [M][K/2] of
+ *       y * 2^-X, round to nearest even, saturating at 6.
+ *   x_bf16 device [M][K].  Outputs device, caller-owned.
+ */
+int tabit_hadamard_quant_act(tabit_ctx* ctx, const uint16_t* x_bf16, int M, int K, int had_block,
+                             int fmt, void* x_q, void* x_scale, void* stream);
+
+/*
+ * Masked W8A8 GEMM.  TASQ section 2: the operational weight at (step, layer)
+ * is the stored code with its k least-significant bits truncated,
+ * Q_M = (W >> k) << k (two's complement), applied to weight tiles as they are
+ * staged; the same kernel serves every k (k is a scalar argument).
+ *   acc[m][n] = sum_k x_q[m][k] * ((w_q[n][k] >> k_bits) << k_bits)   (int32, exact)
+ *   y[m][n]   = bf16_rne(((float)acc[m][n] * x_scale[m]) * w_scale[n])
+ * HQ-DM section 2.1: integer core, fp scales outside it.
+ *   x_q device int8 [M][K], x_scale fp32 [M], w_q int8 [N][K], w_scale fp32 [N].
+ *   y_bf16 device [M][N] (may be NULL), acc device int32 [M][N] (may be NULL);
+ *   at least one output.  k_bits in [0, 7].
+ */
+int tabit_masked_qgemm(tabit_ctx* ctx, const int8_t* x_q, const float* x_scale,
+                       const int8_t* w_q, const float* w_scale, int M, int N, int K, int k_bits,
+                       uint16_t* y_bf16, int32_t* acc, void* stream);
+
+/*
+ * Bit-plane (bit-serial) GEMM over the 8 - k retained weight planes.
+ * TASQ section 2 (Temporal-Precision Engine): in a bit-serial GEMM, cycles
+ * scale with the weight bit width; activations stay resident and only the
+ * selected weight planes are streamed.  Here the INT8 activation fragment is
+ * loaded once per K-tile and multiplied against each retained plane:
+ *   acc = sum_{b = k_bits}^{7} c_b * (x_q . W_b^T),  W_b = bit b of w_q,
+ *   c_b = 2^b (b < 7), -2^7 (sign plane).  Equals tabit_masked_qgemm exactly.
+ * Same arguments, layouts and errors as tabit_masked_qgemm.
+ */
+int tabit_qgemm_bitserial(tabit_ctx* ctx, const int8_t* x_q, const float* x_scale,
+                          const int8_t* w_q, const float* w_scale, int M, int N, int K, int k_bits,
+                          uint16_t* y_bf16, int32_t* acc, void* stream);
+
+/*
+ * MXFP4 (W4A4) GEMM for layer-steps scheduled to 4 bits (6Bit-Diffusion
+ * section 2A).  acc[m][n] = sum over 32-blocks j of 2^(xe[m][j] + we[n][j] - 254)
+ * * sum_i e2m1(x)*e2m1(w), accumulated in fp32 by the scaled matrix cores
+ * (order hardware-defined); y = bf16_rne(acc * out_scale).  With both operands
+ * rotated by H_32, out_scale = 1/32.
+ *   x_fp4 [M][K/2], x_e8m0 [M][K/32], w_fp4 [N][K/2], w_e8m0 [N][K/32] device.
+ *   y_bf16 [M][N] and/or acc_f32 [M][N] device outputs (at least one).
+ */
+int tabit_mxfp4_qgemm(tabit_ctx* ctx, const uint8_t* x_fp4, const uint8_t* x_e8m0,
+                      const uint8_t* w_fp4, const uint8_t* w_e8m0, int M, int N, int K,
+                      float out_scale, uint16_t* y_bf16, float* acc_f32, void* stream);
+
+/* Bytes of device workspace tabit_scheduled_linear needs for M x K activations
+ * (quantized codes plus scales, either format). */
+size_t tabit_act_workspace_bytes(int M, int K);
+
+/*
+ * One linear at denoising step `step`, layer `layer` (the per-step driver).
+ * TASQ section 2 / abstract: the learned schedule maps to execution with no
+ * switching overhead -- here a switch is one table lookup and a scalar kernel
+ * argument.  Looks up (k, fmt); INT8: quantizes x into act_ws and runs the
+ * masked GEMM (path = TABIT_PATH_MASKED) or the bit-plane GEMM
+ * (TABIT_PATH_BITSERIAL) with k; MXFP4: MX-quantizes x and runs the MXFP4 GEMM
+ * with out_scale 1/max(had_block, 1).
+ *   w_q/w_scale required for INT8 steps, w_fp4/w_e8m0 for MXFP4 steps.
+ *   act_ws device workspace of at least tabit_act_workspace_bytes(M, K),
+ *   16-byte aligned.  y_bf16 device [M][N].
+ */
+int tabit_scheduled_linear(tabit_ctx* ctx, int step, int layer, int path,
+                           const uint16_t* x_bf16, int M, int N, int K, int had_block,
+                           const int8_t* w_q, const float* w_scale,
+                           const uint8_t* w_fp4, const uint8_t* w_e8m0,
+                           void* act_ws, size_t act_ws_bytes, uint16_t* y_bf16, void* stream);
+
+/* One linear layer of a stack, for tabit_run_schedule. */
+typedef struct tabit_layer {
+  int M, N, K;               /* tokens, output and input features                     */
+  const int8_t* w_q;         /* device [N][K] INT8 codes (NULL if never INT8)         */
+  const float* w_scale;      /* device [N]                                            */
+  const uint8_t* w_fp4;      /* device [N][K/2] MXFP4 copy (NULL if never MXFP4)      */
+  const uint8_t* w_e8m0;     /* device [N][K/32]                                      */
+  uint16_t* y_bf16;          /* device [M][N] output                                  */
+} tabit_layer;
+
+/*
+ * Run steps [first_step, first_step + num_steps) of the installed schedule over
+ * a stack of layers: for each step t, for each layer l, the same work as
+ * tabit_scheduled_linear(t, l, ...) (TASQ section 2: the per-(layer, stage)
+ * precision is applied by reading the table, with no weight copy).
+ *   x_bf16      host array [num_steps][num_layers] of device pointers to the
+ *               layer inputs ([M][K] bf16 each).
+ *   gemm_events NULL, or a host array of 2 * num_steps * num_layers hipEvent_t
+ *               (passed as void*): events[2i] is recorded on `stream` right
+ *               before the GEMM of layer-step i and events[2i+1] right after,
+ *               so a caller can time the GEMM kernels alone.
+ *   num_layers must equal the schedule's layer count.  Validation covers every
+ *   layer before the first launch.
+ */
+int tabit_run_schedule(tabit_ctx* ctx, int first_step, int num_steps, const tabit_layer* layers,
+                       int num_layers, const uint16_t* const* x_bf16, int had_block, int path,
+                       void* act_ws, size_t act_ws_bytes, void* const* gemm_events, void* stream);
+
+/*
+ * Options (tests and tuning).  TABIT_OPT_GEMM_CONFIG forces the INT8 GEMM tile
+ * configuration (value = index from tabit_gemm_config_info, -1 = automatic);
+ * TABIT_OPT_MXFP4_CONFIG likewise for the MXFP4 GEMM.  EINVAL for an unknown
+ * option or value.  Makes no HIP call.
+ */
+enum tabit_option { TABIT_OPT_GEMM_CONFIG = 0, TABIT_OPT_MXFP4_CONFIG = 1 };
+int tabit_set_option(tabit_ctx* ctx, int option, int value);
+
+/* Describe INT8 GEMM tile configuration `index` (0 <= index < count): block
+ * tile BM x BN, split-K factor.  Returns the number of configurations when
+ * index < 0.  Makes no HIP call. */
+int tabit_gemm_config_info(int index, int* bm, int* bn, int* split_k);
+
+/* The configuration the automatic choice would take for (M, N, K) on a device
+ * with num_cus compute units (num_cus <= 0: 256).  Makes no HIP call. */
+int tabit_gemm_config_choose(int M, int N, int K, int num_cus);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TABIT_H */

@@ -1,0 +1,177 @@
+"""C-ABI library: loads, exports every declared symbol, host logic and argument validation.
+
+No test here launches a kernel: every call either touches host state only or
+fails validation before its first HIP call, so the suite runs without a GPU.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import tabit_synth as S
+import timestep_adaptive_bit_amd as T
+
+FAKE = 0x10000            # 16-byte aligned, never dereferenced (validation fails first)
+MISALIGNED = 0x10001
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return T.load()
+
+
+@pytest.fixture
+def ctx():
+    c = T.Context()
+    yield c
+    c.close()
+
+
+def test_every_header_symbol_is_exported(lib):
+    names = T.header_functions()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in T._lib._SIGNATURES, f"binding lacks {n}"
+
+
+def test_version_and_last_error(lib, ctx):
+    assert "gfx950" in T.version()
+    assert ctx.last_error() == ""
+    assert lib.tabit_last_error(None) == b"null tabit_ctx"
+    assert lib.tabit_create(None) == T.EINVAL
+
+
+def test_schedule_round_trip_all_workloads(ctx):
+    for fn in S.WORKLOADS.values():
+        w = fn()
+        ctx.set_step_schedule(w.k_bits, w.fmt)
+        for t in range(w.steps):
+            for l in range(0, w.num_layers, 7):
+                assert ctx.schedule_lookup(t, l) == (int(w.k_bits[t, l]), int(w.fmt[t, l]))
+
+
+def test_schedule_errors(ctx):
+    with pytest.raises(T.TabitError) as e:
+        ctx.schedule_lookup(0, 0)
+    assert e.value.status == T.ENOSCHED
+    with pytest.raises(T.TabitError) as e:
+        ctx.set_step_schedule(np.full((2, 3), 8))
+    assert e.value.status == T.ERANGE
+    with pytest.raises(T.TabitError) as e:
+        ctx.set_step_schedule(np.zeros((2, 3)), np.full((2, 3), 2))
+    assert e.value.status == T.EINVAL
+    ctx.set_step_schedule(np.zeros((2, 3)))
+    assert ctx.schedule_lookup(1, 2) == (0, 0)          # fmt NULL means all INT8
+    for t, l in ((-1, 0), (2, 0), (0, 3), (0, -1)):
+        with pytest.raises(T.TabitError) as e:
+            ctx.schedule_lookup(t, l)
+        assert e.value.status == T.ENOSCHED
+    st = T.load().tabit_set_step_schedule(ctx.handle, 0, 3, FAKE, None)
+    assert st == T.ESHAPE
+
+
+def _gemm(lib, ctx, fn, **kw):
+    a = dict(xq=FAKE, xs=FAKE, wq=FAKE, ws=FAKE, M=64, N=64, K=64, k=0, y=FAKE, acc=None)
+    a.update(kw)
+    return getattr(lib, fn)(ctx.handle, a["xq"], a["xs"], a["wq"], a["ws"], a["M"], a["N"], a["K"],
+                            a["k"], a["y"], a["acc"], None)
+
+
+@pytest.mark.parametrize("fn", ["tabit_masked_qgemm", "tabit_qgemm_bitserial"])
+def test_gemm_validation(lib, ctx, fn):
+    cases = [
+        (dict(k=8), T.ERANGE), (dict(k=-1), T.ERANGE),
+        (dict(K=33), T.ESHAPE), (dict(K=0), T.ESHAPE), (dict(K=65536), T.ESHAPE),
+        (dict(N=48), T.ESHAPE), (dict(N=-32), T.ESHAPE), (dict(M=-1), T.ESHAPE),
+        (dict(xq=None), T.EINVAL), (dict(ws=None), T.EINVAL), (dict(y=None, acc=None), T.EINVAL),
+        (dict(xq=MISALIGNED), T.EALIGN), (dict(y=FAKE + 8), T.EALIGN),
+        (dict(xs=FAKE + 2), T.EALIGN),
+        (dict(M=0), T.OK), (dict(N=0), T.OK),        # empty problems are no-ops
+    ]
+    for kw, want in cases:
+        assert _gemm(lib, ctx, fn, **kw) == want, (kw, ctx.last_error())
+    assert lib.tabit_masked_qgemm(None, FAKE, FAKE, FAKE, FAKE, 1, 32, 32, 0, FAKE, None, None) == T.EINVAL
+
+
+def test_quant_act_validation(lib, ctx):
+    def q(M=4, K=64, b=0, fmt=0, x=FAKE, xq=FAKE, xs=FAKE):
+        return lib.tabit_hadamard_quant_act(ctx.handle, x, M, K, b, fmt, xq, xs, None)
+    assert q(b=16) == T.ERANGE
+    assert q(b=256, K=512) == T.ERANGE
+    assert q(b=64, K=96) == T.ESHAPE
+    assert q(K=48) == T.ESHAPE
+    assert q(K=65536) == T.ESHAPE
+    assert q(fmt=2) == T.EINVAL
+    assert q(fmt=1, b=64) == T.ERANGE
+    assert q(x=None) == T.EINVAL
+    assert q(xq=MISALIGNED) == T.EALIGN
+    assert q(M=0) == T.OK
+
+
+def test_quantize_weights_validation(lib, ctx):
+    def w(N=32, K=64, b=0, wq=FAKE, ws=FAKE, wf=None, we=None):
+        return lib.tabit_quantize_weights(ctx.handle, FAKE, N, K, b, wq, ws, wf, we, None)
+    assert w(wq=None) == T.EINVAL                       # pair given half
+    assert w(wq=None, ws=None) == T.EINVAL              # nothing requested
+    assert w(wf=FAKE) == T.EINVAL
+    assert w(wf=FAKE, we=FAKE, b=64) == T.ERANGE        # MX copy needs b in {0, 32}
+    assert w(b=128, K=64) == T.ESHAPE
+    assert w(N=0) == T.OK
+
+
+def test_mxfp4_validation(lib, ctx):
+    def m(M=32, N=32, K=64, y=FAKE, acc=None, s=1.0):
+        return lib.tabit_mxfp4_qgemm(ctx.handle, FAKE, FAKE, FAKE, FAKE, M, N, K, s, y, acc, None)
+    assert m(K=40) == T.ESHAPE
+    assert m(N=40) == T.ESHAPE
+    assert m(y=None) == T.EINVAL
+    assert m(s=float("nan")) == T.EINVAL
+    assert m(M=0) == T.OK
+
+
+def test_scheduled_linear_validation(lib, ctx):
+    def s(step=0, layer=0, path=0, M=8, N=32, K=64, b=0, wq=FAKE, ws_=FAKE, wf=None, we=None,
+          ws=FAKE, nbytes=1 << 20):
+        return lib.tabit_scheduled_linear(ctx.handle, step, layer, path, FAKE, M, N, K, b, wq, ws_,
+                                          wf, we, ws, nbytes, FAKE, None)
+    assert s() == T.ENOSCHED
+    ctx.set_step_schedule(np.array([[0, 3]]), np.array([[0, 1]]))
+    assert s(path=5) == T.EINVAL
+    assert s(step=1) == T.ENOSCHED
+    assert s(nbytes=10) == T.ESHAPE
+    assert s(wq=None) == T.EINVAL                        # INT8 step without INT8 weights
+    assert s(layer=1) == T.EINVAL                        # MXFP4 step without the MX copy
+    assert s(layer=1, wf=FAKE, we=FAKE, b=64) == T.ERANGE
+    assert s(ws=MISALIGNED) == T.EALIGN
+    assert s(M=0) == T.OK
+
+
+def test_workspace_bytes():
+    for M, K in ((1, 32), (64, 1152), (17776, 7680)):
+        n = T.act_workspace_bytes(M, K)
+        assert n >= M * K + 4 * M and n % 256 == 0
+    assert T.act_workspace_bytes(0, 64) == 0
+
+
+def test_options_and_configs(ctx):
+    n = T.gemm_config_info()
+    assert n >= 1
+    for i in range(n):
+        bm, bn, sk = T.gemm_config_info(i)
+        assert bm % 16 == 0 and bn % 16 == 0 and sk >= 1
+        ctx.set_option(T.OPT_GEMM_CONFIG, i)
+    ctx.set_option(T.OPT_GEMM_CONFIG, -1)
+    with pytest.raises(T.TabitError):
+        ctx.set_option(T.OPT_GEMM_CONFIG, n)
+    with pytest.raises(T.TabitError):
+        ctx.set_option(99, 0)
+    for M, N, K in ((64, 1152, 1152), (4096, 3456, 1152), (17776, 7680, 1920)):
+        assert 0 <= T.gemm_config_choose(M, N, K) < n
+
+
+def test_product_path_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(T._lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(T._lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        T._lib.load()

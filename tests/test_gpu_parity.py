@@ -1,0 +1,236 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: integer and byte outputs (INT8 codes, E2M1 codes, E8M0 bytes, int32
+accumulators) bit-exact; fp32 scales bit-exact; bf16 outputs within 1e-2
+relative elementwise (the epilogue is three correctly rounded fp32 steps and a
+bf16 rounding, so the error is below 2^-8 relative everywhere and exactly 0 at
+zero); the MXFP4 GEMM (fp32 accumulation in hardware order) within 1e-2
+relative plus a floor of 1e-3 * max|y|, and its fp32 accumulator within
+1e-5 of the sum of |terms|.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import tabit_oracle as O
+import tabit_synth as S
+import timestep_adaptive_bit_amd as T
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    c = T.Context()
+    yield c
+    c.close()
+
+
+def _bits(t_cpu):
+    return S.bf16_bits(t_cpu)
+
+
+def _np(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _bf16_np(t):
+    torch.cuda.synchronize()
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def assert_bf16_close(y_gpu, y_ref, rel=1e-2):
+    err = np.abs(y_gpu - y_ref)
+    bad = err > rel * np.abs(y_ref) + 1e-30
+    assert not bad.any(), (f"{bad.sum()} of {bad.size} bf16 outputs off; worst "
+                           f"{err[bad].max() if bad.any() else 0} at ref {y_ref[bad][:4]}")
+
+
+def edge_activation(M, K, seed):
+    """Seeded activations with zero rows, a huge row, a tiny row and exact ties."""
+    x = S.gen_activation(M, K, seed).float()
+    if M >= 4:
+        x[0] = 0.0
+        x[1] *= 1e30
+        x[2] *= 1e-30
+        x[3] = 0.0
+        x[3, : min(K, 8)] = torch.tensor([127.0, 2.5, -3.5, 0.5, -0.5, 1.5, -126.5, 64.0])[: min(K, 8)]
+    return x.to(torch.bfloat16)
+
+
+# ------------------------------------------------------------ quantizers
+QUANT_SHAPES = [(1, 32), (17, 128), (64, 1152), (129, 2240), (300, 4608), (37, 5600), (5, 7680)]
+
+
+@pytest.mark.parametrize("M,K", QUANT_SHAPES)
+@pytest.mark.parametrize("b", [0, 32, 64, 128])
+def test_quant_act_int8_bit_exact(ctx, M, K, b):
+    if b and K % b:
+        pytest.skip("K not a multiple of the block")
+    x = edge_activation(M, K, seed=M * 7 + K + b)
+    q_ref, s_ref = O.quantize_act_int8(_bits(x), b)
+    q, s = ctx.hadamard_quant_act(x.to(DEV), b, T.FMT_INT8)
+    np.testing.assert_array_equal(_np(q), q_ref)
+    np.testing.assert_array_equal(_np(s).view(np.uint32), s_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("N,K,b", [(32, 64, 0), (96, 1152, 64), (640, 2240, 32), (130 * 32, 128, 128)])
+def test_quantize_weights_bit_exact(ctx, N, K, b):
+    w = S.gen_weight(N, K, seed=N + K)
+    q_ref, s_ref = O.quantize_weights_int8(_bits(w), b)
+    out = ctx.quantize_weights(w.to(DEV), b, int8=True, mx=(b in (0, 32)))
+    np.testing.assert_array_equal(_np(out["w_q"]), q_ref)
+    np.testing.assert_array_equal(_np(out["w_scale"]).view(np.uint32), s_ref.view(np.uint32))
+    if b in (0, 32):
+        f_ref, e_ref = O.mx_quantize_rows(O.bf16_to_f32(_bits(w)), b)
+        np.testing.assert_array_equal(_np(out["w_fp4"]), f_ref)
+        np.testing.assert_array_equal(_np(out["w_e8m0"]), e_ref)
+
+
+@pytest.mark.parametrize("M,K", [(1, 32), (17, 128), (64, 1920), (333, 7680)])
+@pytest.mark.parametrize("b", [0, 32])
+def test_quant_act_mxfp4_bit_exact(ctx, M, K, b):
+    x = edge_activation(M, K, seed=3 * M + K + b)
+    f_ref, e_ref = O.mx_quantize_rows(O.bf16_to_f32(_bits(x)), b)
+    f, e = ctx.hadamard_quant_act(x.to(DEV), b, T.FMT_MXFP4)
+    np.testing.assert_array_equal(_np(e), e_ref)
+    np.testing.assert_array_equal(_np(f), f_ref)
+
+
+# ------------------------------------------------------------ INT8 GEMMs
+GEMM_SHAPES = [(1, 32, 32), (17, 96, 96), (64, 640, 1152), (129, 96, 1120), (300, 416, 2240),
+               (513, 288, 160)]
+
+
+def _gemm_inputs(M, N, K, seed):
+    xq = S.gen_int8((M, K), seed)
+    wq = S.gen_int8((N, K), seed + 1)
+    # extremes: a row of -127 activations against a row of -128 / +127 weights
+    xq[0, :] = -127
+    if N >= 2:
+        wq[0, :] = -128
+        wq[1, :] = 127
+    sa = S.gen_scales(M, seed + 2)
+    sw = S.gen_scales(N, seed + 3)
+    return xq, wq, sa, sw
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_masked_and_bitserial_gemm_bit_exact(ctx, M, N, K):
+    """Every tile configuration, every k: int32 bit-exact, bf16 within tolerance."""
+    xq, wq, sa, sw = _gemm_inputs(M, N, K, seed=M + N + K)
+    dx, dw = torch.from_numpy(xq).to(DEV), torch.from_numpy(wq).to(DEV)
+    dsa, dsw = torch.from_numpy(sa).to(DEV), torch.from_numpy(sw).to(DEV)
+    refs = {}
+    for k in range(8):
+        acc_ref = O.masked_gemm_i32(xq, wq, k)
+        refs[k] = (acc_ref, O.dequant(acc_ref, sa, sw))
+    bp_refs = {k: O.bitplane_gemm_i32(xq, wq, k) for k in (0, 3, 7)}
+    try:
+        for cfg in range(T.gemm_config_info()):
+            ctx.set_option(T.OPT_GEMM_CONFIG, cfg)
+            for k in range(8):
+                acc_ref, y_ref = refs[k]
+                y, acc = ctx.masked_qgemm(dx, dsa, dw, dsw, k, want_acc=True)
+                np.testing.assert_array_equal(_np(acc), acc_ref, err_msg=f"cfg {cfg} k {k}")
+                assert_bf16_close(_bf16_np(y), y_ref)
+                yb, accb = ctx.qgemm_bitserial(dx, dsa, dw, dsw, k, want_acc=True)
+                np.testing.assert_array_equal(_np(accb), bp_refs.get(k, acc_ref),
+                                              err_msg=f"bitserial cfg {cfg} k {k}")
+                assert_bf16_close(_bf16_np(yb), y_ref)
+    finally:
+        ctx.set_option(T.OPT_GEMM_CONFIG, -1)
+
+
+def test_gemm_y_only_and_acc_only(ctx):
+    xq, wq, sa, sw = _gemm_inputs(70, 64, 256, seed=5)
+    d = [torch.from_numpy(a).to(DEV) for a in (xq, sa, wq, sw)]
+    y, acc = ctx.masked_qgemm(d[0], d[1], d[2], d[3], 2, want_y=True, want_acc=False)
+    assert acc is None
+    assert_bf16_close(_bf16_np(y), O.dequant(O.masked_gemm_i32(xq, wq, 2), sa, sw))
+    y, acc = ctx.masked_qgemm(d[0], d[1], d[2], d[3], 2, want_y=False, want_acc=True)
+    assert y is None
+    np.testing.assert_array_equal(_np(acc), O.masked_gemm_i32(xq, wq, 2))
+
+
+def test_precision_switch_is_a_scalar(ctx):
+    """Alternating k between calls on one weight buffer matches each k's own result."""
+    xq, wq, sa, sw = _gemm_inputs(64, 128, 512, seed=9)
+    d = [torch.from_numpy(a).to(DEV) for a in (xq, sa, wq, sw)]
+    outs = [ctx.masked_qgemm(d[0], d[1], d[2], d[3], k, want_acc=True)[1] for k in (0, 5, 1, 7, 0, 3)]
+    for k, acc in zip((0, 5, 1, 7, 0, 3), outs):
+        np.testing.assert_array_equal(_np(acc), O.masked_gemm_i32(xq, wq, k))
+    np.testing.assert_array_equal(_np(d[2]), wq)        # the shared buffer is never modified
+
+
+# ------------------------------------------------------------ MXFP4 GEMM
+def _check_mx(y_gpu, acc_gpu, xf, xe, wf, we, scale):
+    xa = O.mx_unpack(xf, xe)
+    wa = O.mx_unpack(wf, we)
+    exact = xa @ wa.T
+    absum = np.abs(xa) @ np.abs(wa).T
+    if acc_gpu is not None:
+        assert np.all(np.abs(acc_gpu - exact) <= 1e-5 * absum + 1e-30)
+    y_ref = exact * scale
+    if y_gpu is not None:
+        err = np.abs(y_gpu - y_ref)
+        assert np.all(err <= 1e-2 * np.abs(y_ref) + 1e-3 * np.abs(y_ref).max() + 1e-30)
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2])
+@pytest.mark.parametrize("M,N,K", [(1, 32, 32), (17, 96, 96), (300, 416, 2240), (129, 64, 1920)])
+def test_mxfp4_gemm(ctx, cfg, M, N, K):
+    rng = np.random.default_rng(M * N + K)
+    xf = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    wf = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    xe = rng.integers(118, 136, size=(M, K // 32), dtype=np.uint8)
+    we = rng.integers(118, 136, size=(N, K // 32), dtype=np.uint8)
+    d = [torch.from_numpy(a).to(DEV) for a in (xf, xe, wf, we)]
+    ctx.set_option(T.OPT_MXFP4_CONFIG, cfg)
+    try:
+        y, acc = ctx.mxfp4_qgemm(*d, 1 / 32, want_acc=True)
+        _check_mx(_bf16_np(y), _np(acc).astype(np.float64), xf, xe, wf, we, 1 / 32)
+    finally:
+        ctx.set_option(T.OPT_MXFP4_CONFIG, -1)
+
+
+# ------------------------------------------------------------ whole linear, schedule driver
+def test_single_linear_config_full(ctx):
+    """64 tokens x 1152, W 1152x1152, b = 64, 4 steps k = [0, 2, 4, 3], both paths, in full."""
+    wl = S.c1_single_linear()
+    layer = wl.layers[0]
+    w = S.gen_weight(layer.N, layer.K, seed=0)
+    wts = ctx.quantize_weights(w.to(DEV), wl.had_block, int8=True)
+    wq_ref, sw_ref = O.quantize_weights_int8(_bits(w), wl.had_block)
+    np.testing.assert_array_equal(_np(wts["w_q"]), wq_ref)
+    ctx.set_step_schedule(wl.k_bits, wl.fmt)
+    ws = torch.empty(T.act_workspace_bytes(layer.M, layer.K), dtype=torch.uint8, device=DEV)
+    for t in range(wl.steps):
+        x = S.gen_activation(layer.M, layer.K, seed=S.activation_seed(t, layer.K))
+        ref = O.linear_int8(_bits(x), _bits(w), wl.had_block, int(wl.k_bits[t, 0]))
+        for path in (T.PATH_MASKED, T.PATH_BITSERIAL):
+            y = ctx.scheduled_linear(t, 0, x.to(DEV), wts, wl.had_block, ws, path=path)
+            assert_bf16_close(_bf16_np(y), ref["y"])
+        # the intermediate products, bit-exact
+        xq, sa = ctx.hadamard_quant_act(x.to(DEV), wl.had_block)
+        np.testing.assert_array_equal(_np(xq), ref["x_q"])
+        _, acc = ctx.masked_qgemm(xq, sa, wts["w_q"], wts["w_scale"], int(wl.k_bits[t, 0]),
+                                  want_acc=True)
+        np.testing.assert_array_equal(_np(acc), ref["acc"])
+
+
+def test_scheduled_linear_mxfp4_step(ctx):
+    M, N, K = 96, 128, 1920
+    x = S.gen_activation(M, K, seed=1)
+    w = S.gen_weight(N, K, seed=2)
+    wts = ctx.quantize_weights(w.to(DEV), 32, int8=True, mx=True)
+    ctx.set_step_schedule(np.array([[0, 2]]), np.array([[1, 0]]))
+    ws = torch.empty(T.act_workspace_bytes(M, K), dtype=torch.uint8, device=DEV)
+    y = ctx.scheduled_linear(0, 0, x.to(DEV), wts, 32, ws)
+    ref = O.linear_mxfp4(_bits(x), _bits(w), 32)
+    _check_mx(_bf16_np(y), None, ref["x_fp4"], ref["x_e8m0"], ref["w_fp4"], ref["w_e8m0"], 1 / 32)
+    y2 = ctx.scheduled_linear(0, 1, x.to(DEV), wts, 32, ws)
+    assert_bf16_close(_bf16_np(y2), O.linear_int8(_bits(x), _bits(w), 32, 2)["y"])

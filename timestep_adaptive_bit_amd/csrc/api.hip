@@ -1,0 +1,433 @@
+// extern "C" entry points of libtabit (declared in include/tabit.h).
+//
+// Every entry point validates its arguments completely before the first HIP
+// call, records a message on the context for any failure, and enqueues its
+// kernels on the caller's stream.  No device memory is allocated here.
+#include "../../include/tabit.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <new>
+
+#include "tabit_internal.h"
+
+namespace {
+
+constexpr int kMaxK = 32768;
+
+int fail(tabit_ctx* ctx, int status, const char* fmt, ...) {
+  if (ctx != nullptr) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    ctx->err = buf;
+  }
+  return status;
+}
+
+int hip_status(tabit_ctx* ctx, hipError_t e, const char* what) {
+  if (e == hipSuccess) return TABIT_OK;
+  return fail(ctx, TABIT_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool valid_block(int b) { return b == 0 || b == 32 || b == 64 || b == 128; }
+
+int check_k_shape(tabit_ctx* ctx, int M, int K, int had_block) {
+  if (M < 0) return fail(ctx, TABIT_ESHAPE, "M must be >= 0 (got %d)", M);
+  if (K < 32 || K > kMaxK || K % 32 != 0)
+    return fail(ctx, TABIT_ESHAPE, "K must be a multiple of 32 in [32, %d] (got %d)", kMaxK, K);
+  if (!valid_block(had_block))
+    return fail(ctx, TABIT_ERANGE, "had_block must be 0, 32, 64 or 128 (got %d)", had_block);
+  if (had_block > 0 && K % had_block != 0)
+    return fail(ctx, TABIT_ESHAPE, "K (%d) must be a multiple of had_block (%d)", K, had_block);
+  return TABIT_OK;
+}
+
+int check_gemm(tabit_ctx* ctx, const void* xq, const void* xs, const void* wq, const void* ws,
+               int M, int N, int K, const void* y, const void* acc) {
+  if (xq == nullptr || xs == nullptr || wq == nullptr || ws == nullptr)
+    return fail(ctx, TABIT_EINVAL, "null input pointer");
+  if (y == nullptr && acc == nullptr) return fail(ctx, TABIT_EINVAL, "no output requested");
+  if (M < 0) return fail(ctx, TABIT_ESHAPE, "M must be >= 0 (got %d)", M);
+  if (N < 0 || N % 32 != 0)
+    return fail(ctx, TABIT_ESHAPE, "N must be a non-negative multiple of 32 (got %d)", N);
+  if (K < 32 || K > kMaxK || K % 32 != 0)
+    return fail(ctx, TABIT_ESHAPE, "K must be a multiple of 32 in [32, %d] (got %d)", kMaxK, K);
+  if (!aligned(xq, 16) || !aligned(wq, 16) || (y && !aligned(y, 16)) || (acc && !aligned(acc, 16)))
+    return fail(ctx, TABIT_EALIGN, "matrices must be 16-byte aligned");
+  return TABIT_OK;
+}
+
+int gemm_i8_common(tabit_ctx* ctx, bool bitserial, const int8_t* x_q, const float* x_scale,
+                   const int8_t* w_q, const float* w_scale, int M, int N, int K, int k_bits,
+                   uint16_t* y, int32_t* acc, void* stream) {
+  if (ctx == nullptr) return TABIT_EINVAL;
+  int st = check_gemm(ctx, x_q, x_scale, w_q, w_scale, M, N, K, y, acc);
+  if (st != TABIT_OK) return st;
+  if (!aligned(x_scale, 4) || !aligned(w_scale, 4))
+    return fail(ctx, TABIT_EALIGN, "scales must be 4-byte aligned");
+  if (k_bits < 0 || k_bits > 7) return fail(ctx, TABIT_ERANGE, "k_bits must be in [0, 7] (got %d)", k_bits);
+  if (M == 0 || N == 0) return TABIT_OK;
+  int cfg = ctx->force_gemm_cfg;
+  if (cfg < 0) cfg = tabit::gemm_config_choose(M, N, K, tabit::device_num_cus());
+  return hip_status(ctx,
+                    tabit::launch_gemm_i8(cfg, bitserial, x_q, x_scale, w_q, w_scale, M, N, K,
+                                          k_bits, y, acc, static_cast<hipStream_t>(stream)),
+                    bitserial ? "qgemm_bitserial launch" : "masked_qgemm launch");
+}
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+}  // namespace
+
+namespace tabit {
+
+int device_num_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+}  // namespace tabit
+
+extern "C" {
+
+int tabit_create(tabit_ctx** out) {
+  if (out == nullptr) return TABIT_EINVAL;
+  tabit_ctx* c = new (std::nothrow) tabit_ctx();
+  if (c == nullptr) return TABIT_ENOMEM;
+  *out = c;
+  return TABIT_OK;
+}
+
+void tabit_destroy(tabit_ctx* ctx) { delete ctx; }
+
+const char* tabit_last_error(const tabit_ctx* ctx) {
+  if (ctx == nullptr) return "null tabit_ctx";
+  return ctx->err.c_str();
+}
+
+const char* tabit_version(void) { return "tabit 0.1.0 gfx950"; }
+
+int tabit_quantize_weights(tabit_ctx* ctx, const uint16_t* w_bf16, int N, int K, int had_block,
+                           int8_t* w_q, float* w_scale, uint8_t* w_fp4, uint8_t* w_e8m0,
+                           void* stream) {
+  if (ctx == nullptr) return TABIT_EINVAL;
+  if (w_bf16 == nullptr) return fail(ctx, TABIT_EINVAL, "null weight pointer");
+  const bool want_i8 = w_q != nullptr || w_scale != nullptr;
+  const bool want_mx = w_fp4 != nullptr || w_e8m0 != nullptr;
+  if (want_i8 && (w_q == nullptr || w_scale == nullptr))
+    return fail(ctx, TABIT_EINVAL, "w_q and w_scale must be given together");
+  if (want_mx && (w_fp4 == nullptr || w_e8m0 == nullptr))
+    return fail(ctx, TABIT_EINVAL, "w_fp4 and w_e8m0 must be given together");
+  if (!want_i8 && !want_mx) return fail(ctx, TABIT_EINVAL, "no output requested");
+  int st = check_k_shape(ctx, N, K, had_block);
+  if (st != TABIT_OK) return st;
+  if (want_mx && had_block != 0 && had_block != 32)
+    return fail(ctx, TABIT_ERANGE, "the MXFP4 copy takes had_block 0 or 32 (got %d)", had_block);
+  if (!aligned(w_bf16, 16) || (w_q && !aligned(w_q, 16)) || (w_fp4 && !aligned(w_fp4, 16)) ||
+      (w_scale && !aligned(w_scale, 4)))
+    return fail(ctx, TABIT_EALIGN, "misaligned pointer");
+  if (N == 0) return TABIT_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (want_i8) {
+    const float div = (float)(had_block > 0 ? had_block : 1);
+    st = hip_status(ctx, tabit::launch_quant_int8(w_bf16, N, K, had_block, div, w_q, w_scale, s),
+                    "quantize_weights launch");
+    if (st != TABIT_OK) return st;
+  }
+  if (want_mx)
+    return hip_status(ctx, tabit::launch_quant_mx(w_bf16, N, K, had_block, w_fp4, w_e8m0, s),
+                      "quantize_weights (mxfp4) launch");
+  return TABIT_OK;
+}
+
+int tabit_set_step_schedule(tabit_ctx* ctx, int num_steps, int num_layers, const uint8_t* k_bits,
+                            const uint8_t* fmt) {
+  if (ctx == nullptr) return TABIT_EINVAL;
+  if (k_bits == nullptr) return fail(ctx, TABIT_EINVAL, "null k_bits table");
+  if (num_steps < 1 || num_layers < 1)
+    return fail(ctx, TABIT_ESHAPE, "schedule must be at least 1 x 1 (got %d x %d)", num_steps, num_layers);
+  const size_t n = (size_t)num_steps * (size_t)num_layers;
+  for (size_t i = 0; i < n; ++i) {
+    if (k_bits[i] > 7) return fail(ctx, TABIT_ERANGE, "k_bits[%zu] = %d outside [0, 7]", i, k_bits[i]);
+    if (fmt != nullptr && fmt[i] != TABIT_FMT_INT8 && fmt[i] != TABIT_FMT_MXFP4)
+      return fail(ctx, TABIT_EINVAL, "fmt[%zu] = %d is not a known format", i, fmt[i]);
+  }
+  try {
+    ctx->k_bits.assign(k_bits, k_bits + n);
+    if (fmt != nullptr)
+      ctx->fmt.assign(fmt, fmt + n);
+    else
+      ctx->fmt.assign(n, (uint8_t)TABIT_FMT_INT8);
+  } catch (...) {
+    ctx->k_bits.clear();
+    ctx->fmt.clear();
+    ctx->steps = ctx->layers = 0;
+    return fail(ctx, TABIT_ENOMEM, "schedule allocation failed");
+  }
+  ctx->steps = num_steps;
+  ctx->layers = num_layers;
+  return TABIT_OK;
+}
+
+int tabit_schedule_lookup(const tabit_ctx* ctx, int step, int layer, int* k_bits, int* fmt) {
+  if (ctx == nullptr || k_bits == nullptr || fmt == nullptr) return TABIT_EINVAL;
+  tabit_ctx* c = const_cast<tabit_ctx*>(ctx);
+  if (ctx->steps == 0) return fail(c, TABIT_ENOSCHED, "no schedule installed");
+  if (step < 0 || step >= ctx->steps || layer < 0 || layer >= ctx->layers)
+    return fail(c, TABIT_ENOSCHED, "(step %d, layer %d) outside the %d x %d schedule", step, layer,
+                ctx->steps, ctx->layers);
+  const size_t i = (size_t)step * ctx->layers + layer;
+  *k_bits = ctx->k_bits[i];
+  *fmt = ctx->fmt[i];
+  return TABIT_OK;
+}
+
+int tabit_hadamard_quant_act(tabit_ctx* ctx, const uint16_t* x_bf16, int M, int K, int had_block,
+                             int fmt, void* x_q, void* x_scale, void* stream) {
+  if (ctx == nullptr) return TABIT_EINVAL;
+  if (x_bf16 == nullptr || x_q == nullptr || x_scale == nullptr)
+    return fail(ctx, TABIT_EINVAL, "null pointer");
+  if (fmt != TABIT_FMT_INT8 && fmt != TABIT_FMT_MXFP4)
+    return fail(ctx, TABIT_EINVAL, "unknown fmt %d", fmt);
+  int st = check_k_shape(ctx, M, K, had_block);
+  if (st != TABIT_OK) return st;
+  if (fmt == TABIT_FMT_MXFP4 && had_block != 0 && had_block != 32)
+    return fail(ctx, TABIT_ERANGE, "MXFP4 takes had_block 0 or 32 (got %d)", had_block);
+  if (!aligned(x_bf16, 16) || !aligned(x_q, 16) || (fmt == TABIT_FMT_INT8 && !aligned(x_scale, 4)))
+    return fail(ctx, TABIT_EALIGN, "misaligned pointer");
+  if (M == 0) return TABIT_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fmt == TABIT_FMT_INT8)
+    return hip_status(ctx,
+                      tabit::launch_quant_int8(x_bf16, M, K, had_block, 1.0f,
+                                               static_cast<int8_t*>(x_q),
+                                               static_cast<float*>(x_scale), s),
+                      "hadamard_quant_act launch");
+  return hip_status(ctx,
+                    tabit::launch_quant_mx(x_bf16, M, K, had_block, static_cast<uint8_t*>(x_q),
+                                           static_cast<uint8_t*>(x_scale), s),
+                    "hadamard_quant_act (mxfp4) launch");
+}
+
+int tabit_masked_qgemm(tabit_ctx* ctx, const int8_t* x_q, const float* x_scale, const int8_t* w_q,
+                       const float* w_scale, int M, int N, int K, int k_bits, uint16_t* y_bf16,
+                       int32_t* acc, void* stream) {
+  return gemm_i8_common(ctx, false, x_q, x_scale, w_q, w_scale, M, N, K, k_bits, y_bf16, acc,
+                        stream);
+}
+
+int tabit_qgemm_bitserial(tabit_ctx* ctx, const int8_t* x_q, const float* x_scale,
+                          const int8_t* w_q, const float* w_scale, int M, int N, int K, int k_bits,
+                          uint16_t* y_bf16, int32_t* acc, void* stream) {
+  return gemm_i8_common(ctx, true, x_q, x_scale, w_q, w_scale, M, N, K, k_bits, y_bf16, acc,
+                        stream);
+}
+
+int tabit_mxfp4_qgemm(tabit_ctx* ctx, const uint8_t* x_fp4, const uint8_t* x_e8m0,
+                      const uint8_t* w_fp4, const uint8_t* w_e8m0, int M, int N, int K,
+                      float out_scale, uint16_t* y_bf16, float* acc_f32, void* stream) {
+  if (ctx == nullptr) return TABIT_EINVAL;
+  int st = check_gemm(ctx, x_fp4, x_e8m0, w_fp4, w_e8m0, M, N, K, y_bf16, acc_f32);
+  if (st != TABIT_OK) return st;
+  if (!(out_scale == out_scale)) return fail(ctx, TABIT_EINVAL, "out_scale is NaN");
+  if (M == 0 || N == 0) return TABIT_OK;
+  int cfg = ctx->force_mx_cfg;
+  if (cfg < 0) cfg = tabit::mx_config_choose(M, N, K, tabit::device_num_cus());
+  return hip_status(ctx,
+                    tabit::launch_gemm_mxfp4(cfg, x_fp4, x_e8m0, w_fp4, w_e8m0, M, N, K, out_scale,
+                                             y_bf16, acc_f32, static_cast<hipStream_t>(stream)),
+                    "mxfp4_qgemm launch");
+}
+
+size_t tabit_act_workspace_bytes(int M, int K) {
+  if (M <= 0 || K <= 0) return 0;
+  const size_t mk = (size_t)M * (size_t)K;
+  const size_t i8 = align256(mk) + align256((size_t)M * 4);
+  const size_t mx = align256(mk / 2) + align256(mk / 32);
+  return i8 > mx ? i8 : mx;
+}
+
+int tabit_scheduled_linear(tabit_ctx* ctx, int step, int layer, int path, const uint16_t* x_bf16,
+                           int M, int N, int K, int had_block, const int8_t* w_q,
+                           const float* w_scale, const uint8_t* w_fp4, const uint8_t* w_e8m0,
+                           void* act_ws, size_t act_ws_bytes, uint16_t* y_bf16, void* stream) {
+  if (ctx == nullptr) return TABIT_EINVAL;
+  if (path != TABIT_PATH_MASKED && path != TABIT_PATH_BITSERIAL)
+    return fail(ctx, TABIT_EINVAL, "unknown path %d", path);
+  int k = 0, fmt = 0;
+  int st = tabit_schedule_lookup(ctx, step, layer, &k, &fmt);
+  if (st != TABIT_OK) return st;
+  if (x_bf16 == nullptr || y_bf16 == nullptr || act_ws == nullptr)
+    return fail(ctx, TABIT_EINVAL, "null pointer");
+  st = check_k_shape(ctx, M, K, had_block);
+  if (st != TABIT_OK) return st;
+  if (N < 0 || N % 32 != 0)
+    return fail(ctx, TABIT_ESHAPE, "N must be a non-negative multiple of 32 (got %d)", N);
+  if (!aligned(act_ws, 16)) return fail(ctx, TABIT_EALIGN, "act_ws must be 16-byte aligned");
+  if (act_ws_bytes < tabit_act_workspace_bytes(M, K))
+    return fail(ctx, TABIT_ESHAPE, "act_ws holds %zu bytes, %zu needed", act_ws_bytes,
+                tabit_act_workspace_bytes(M, K));
+  if (fmt == TABIT_FMT_INT8) {
+    if (w_q == nullptr || w_scale == nullptr)
+      return fail(ctx, TABIT_EINVAL, "step %d layer %d is INT8 but w_q/w_scale are null", step, layer);
+  } else {
+    if (w_fp4 == nullptr || w_e8m0 == nullptr)
+      return fail(ctx, TABIT_EINVAL, "step %d layer %d is MXFP4 but w_fp4/w_e8m0 are null", step, layer);
+    if (had_block != 0 && had_block != 32)
+      return fail(ctx, TABIT_ERANGE, "MXFP4 takes had_block 0 or 32 (got %d)", had_block);
+  }
+  if (M == 0 || N == 0) return TABIT_OK;
+  uint8_t* ws = static_cast<uint8_t*>(act_ws);
+  const size_t mk = (size_t)M * (size_t)K;
+  if (fmt == TABIT_FMT_INT8) {
+    int8_t* xq = reinterpret_cast<int8_t*>(ws);
+    float* sa = reinterpret_cast<float*>(ws + align256(mk));
+    st = tabit_hadamard_quant_act(ctx, x_bf16, M, K, had_block, TABIT_FMT_INT8, xq, sa, stream);
+    if (st != TABIT_OK) return st;
+    return gemm_i8_common(ctx, path == TABIT_PATH_BITSERIAL, xq, sa, w_q, w_scale, M, N, K, k,
+                          y_bf16, nullptr, stream);
+  }
+  uint8_t* xf = ws;
+  uint8_t* xe = ws + align256(mk / 2);
+  st = tabit_hadamard_quant_act(ctx, x_bf16, M, K, had_block, TABIT_FMT_MXFP4, xf, xe, stream);
+  if (st != TABIT_OK) return st;
+  return tabit_mxfp4_qgemm(ctx, xf, xe, w_fp4, w_e8m0, M, N, K,
+                           1.0f / (float)(had_block > 0 ? had_block : 1), y_bf16, nullptr, stream);
+}
+
+int tabit_run_schedule(tabit_ctx* ctx, int first_step, int num_steps, const tabit_layer* layers,
+                       int num_layers, const uint16_t* const* x_bf16, int had_block, int path,
+                       void* act_ws, size_t act_ws_bytes, void* const* gemm_events, void* stream) {
+  if (ctx == nullptr) return TABIT_EINVAL;
+  if (layers == nullptr || x_bf16 == nullptr || act_ws == nullptr)
+    return fail(ctx, TABIT_EINVAL, "null pointer");
+  if (path != TABIT_PATH_MASKED && path != TABIT_PATH_BITSERIAL)
+    return fail(ctx, TABIT_EINVAL, "unknown path %d", path);
+  if (ctx->steps == 0) return fail(ctx, TABIT_ENOSCHED, "no schedule installed");
+  if (num_layers != ctx->layers)
+    return fail(ctx, TABIT_ESHAPE, "%d layers given, schedule has %d", num_layers, ctx->layers);
+  if (num_steps < 0 || first_step < 0 || first_step + num_steps > ctx->steps)
+    return fail(ctx, TABIT_ENOSCHED, "steps [%d, %d) outside the %d-step schedule", first_step,
+                first_step + num_steps, ctx->steps);
+  if (!aligned(act_ws, 16)) return fail(ctx, TABIT_EALIGN, "act_ws must be 16-byte aligned");
+  if (!valid_block(had_block))
+    return fail(ctx, TABIT_ERANGE, "had_block must be 0, 32, 64 or 128 (got %d)", had_block);
+  // validate everything before the first launch
+  for (int l = 0; l < num_layers; ++l) {
+    const tabit_layer& L = layers[l];
+    int st = check_k_shape(ctx, L.M, L.K, had_block);
+    if (st != TABIT_OK) return st;
+    if (L.N < 0 || L.N % 32 != 0)
+      return fail(ctx, TABIT_ESHAPE, "layer %d: N must be a non-negative multiple of 32", l);
+    if (L.y_bf16 == nullptr || !aligned(L.y_bf16, 16))
+      return fail(ctx, TABIT_EINVAL, "layer %d: missing or misaligned output", l);
+    if (act_ws_bytes < tabit_act_workspace_bytes(L.M, L.K))
+      return fail(ctx, TABIT_ESHAPE, "layer %d: act_ws holds %zu bytes, %zu needed", l,
+                  act_ws_bytes, tabit_act_workspace_bytes(L.M, L.K));
+    for (int t = first_step; t < first_step + num_steps; ++t) {
+      const size_t i = (size_t)t * ctx->layers + l;
+      const uint16_t* x = x_bf16[(size_t)(t - first_step) * num_layers + l];
+      if (x == nullptr || !aligned(x, 16))
+        return fail(ctx, TABIT_EINVAL, "step %d layer %d: missing or misaligned input", t, l);
+      if (ctx->fmt[i] == TABIT_FMT_INT8) {
+        if (L.w_q == nullptr || L.w_scale == nullptr || !aligned(L.w_q, 16))
+          return fail(ctx, TABIT_EINVAL, "layer %d: INT8 step %d without INT8 weights", l, t);
+      } else {
+        if (L.w_fp4 == nullptr || L.w_e8m0 == nullptr || !aligned(L.w_fp4, 16))
+          return fail(ctx, TABIT_EINVAL, "layer %d: MXFP4 step %d without the MX copy", l, t);
+        if (had_block != 0 && had_block != 32)
+          return fail(ctx, TABIT_ERANGE, "MXFP4 takes had_block 0 or 32 (got %d)", had_block);
+      }
+    }
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(act_ws);
+  const int num_cus = tabit::device_num_cus();
+  for (int t = first_step; t < first_step + num_steps; ++t) {
+    for (int l = 0; l < num_layers; ++l) {
+      const tabit_layer& L = layers[l];
+      const size_t li = (size_t)(t - first_step) * num_layers + l;
+      const size_t i = (size_t)t * ctx->layers + l;
+      const uint16_t* x = x_bf16[li];
+      hipEvent_t e0 = gemm_events ? static_cast<hipEvent_t>(gemm_events[2 * li]) : nullptr;
+      hipEvent_t e1 = gemm_events ? static_cast<hipEvent_t>(gemm_events[2 * li + 1]) : nullptr;
+      if (L.M == 0 || L.N == 0) continue;
+      const size_t mk = (size_t)L.M * (size_t)L.K;
+      hipError_t e;
+      if (ctx->fmt[i] == TABIT_FMT_INT8) {
+        int8_t* xq = reinterpret_cast<int8_t*>(ws);
+        float* sa = reinterpret_cast<float*>(ws + align256(mk));
+        e = tabit::launch_quant_int8(x, L.M, L.K, had_block, 1.0f, xq, sa, s);
+        if (e != hipSuccess) return hip_status(ctx, e, "run_schedule quantizer launch");
+        if (e0 && (e = hipEventRecord(e0, s)) != hipSuccess) return hip_status(ctx, e, "event record");
+        int cfg = ctx->force_gemm_cfg >= 0 ? ctx->force_gemm_cfg
+                                           : tabit::gemm_config_choose(L.M, L.N, L.K, num_cus);
+        e = tabit::launch_gemm_i8(cfg, path == TABIT_PATH_BITSERIAL, xq, sa, L.w_q, L.w_scale, L.M,
+                                  L.N, L.K, ctx->k_bits[i], L.y_bf16, nullptr, s);
+        if (e != hipSuccess) return hip_status(ctx, e, "run_schedule GEMM launch");
+      } else {
+        uint8_t* xf = ws;
+        uint8_t* xe = ws + align256(mk / 2);
+        e = tabit::launch_quant_mx(x, L.M, L.K, had_block, xf, xe, s);
+        if (e != hipSuccess) return hip_status(ctx, e, "run_schedule MX quantizer launch");
+        if (e0 && (e = hipEventRecord(e0, s)) != hipSuccess) return hip_status(ctx, e, "event record");
+        int cfg = ctx->force_mx_cfg >= 0 ? ctx->force_mx_cfg
+                                         : tabit::mx_config_choose(L.M, L.N, L.K, num_cus);
+        e = tabit::launch_gemm_mxfp4(cfg, xf, xe, L.w_fp4, L.w_e8m0, L.M, L.N, L.K,
+                                     1.0f / (float)(had_block > 0 ? had_block : 1), L.y_bf16,
+                                     nullptr, s);
+        if (e != hipSuccess) return hip_status(ctx, e, "run_schedule MXFP4 GEMM launch");
+      }
+      if (e1 && (e = hipEventRecord(e1, s)) != hipSuccess) return hip_status(ctx, e, "event record");
+    }
+  }
+  return TABIT_OK;
+}
+
+int tabit_set_option(tabit_ctx* ctx, int option, int value) {
+  if (ctx == nullptr) return TABIT_EINVAL;
+  switch (option) {
+    case TABIT_OPT_GEMM_CONFIG:
+      if (value < -1 || value >= tabit::gemm_config_count())
+        return fail(ctx, TABIT_EINVAL, "GEMM config %d out of range", value);
+      ctx->force_gemm_cfg = value;
+      return TABIT_OK;
+    case TABIT_OPT_MXFP4_CONFIG:
+      if (value < -1 || value >= tabit::mx_config_count())
+        return fail(ctx, TABIT_EINVAL, "MXFP4 config %d out of range", value);
+      ctx->force_mx_cfg = value;
+      return TABIT_OK;
+    default:
+      return fail(ctx, TABIT_EINVAL, "unknown option %d", option);
+  }
+}
+
+int tabit_gemm_config_info(int index, int* bm, int* bn, int* split_k) {
+  if (index < 0) return tabit::gemm_config_count();
+  if (index >= tabit::gemm_config_count() || bm == nullptr || bn == nullptr || split_k == nullptr)
+    return TABIT_EINVAL;
+  const tabit::GemmConfig c = tabit::gemm_config(index);
+  *bm = c.bm;
+  *bn = c.bn;
+  *split_k = c.split_k;
+  return TABIT_OK;
+}
+
+int tabit_gemm_config_choose(int M, int N, int K, int num_cus) {
+  return tabit::gemm_config_choose(M, N, K, num_cus);
+}
+
+}  // extern "C"

@@ -1,0 +1,286 @@
+// Activation / weight quantizers for gfx950.
+//
+// INT8: per row, unnormalized block Walsh-Hadamard transform (fp32; stages
+// h = 1, 2, 4, ... so every output is a fixed sequence of IEEE additions),
+// row absmax, one correctly rounded division r = 127/a, codes
+// rint(y*r) clamped to +-127.  HQ-DM (gist.science summary, section 2.1):
+// rotate X by a block-diagonal Hadamard, quantize XH, keep the Hadamard
+// normalization in the fp scale.  Section 2.2: symmetric quantization.
+//
+// MXFP4: per block of 32, optional FWHT32, E8M0 scale 2^X with
+// X = floor(log2 amax) - 2, E2M1 codes of y*2^-X rounded to nearest even.
+// 6Bit-Diffusion (gist.science summary, section 2A): local block Hadamard
+// before 4-bit quantization; OCP MX v1.0 defines the format.
+//
+// Data layout: the workgroup's rows are contiguous in memory, so the
+// workgroup sees them as one flat run of 16-element chunks; chunk c of the run
+// lives in thread (c mod 256), register slot (c / 256).  Loads and stores are
+// 16-byte, fully coalesced.  A Hadamard block of b elements spans b/16
+// consecutive, aligned lanes, so the cross-lane FWHT stages are lane-XOR
+// exchanges (DPP within a quad, ds_swizzle beyond).
+#include "tabit_internal.h"
+
+namespace tabit {
+namespace {
+
+constexpr int QT = 256;  // threads per workgroup
+
+template <int MASK>
+__device__ __forceinline__ float lane_xor(float v) {
+  int i = __float_as_int(v);
+  if constexpr (MASK == 1) {
+    i = __builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  } else if constexpr (MASK == 2) {
+    i = __builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  } else {
+    i = __builtin_amdgcn_ds_swizzle(i, (MASK << 10) | 0x1F);  // bit mode: lane ^ MASK
+  }
+  return __int_as_float(i);
+}
+
+// One cross-lane butterfly stage: the lane holding the first element of each
+// pair keeps first + second, its partner keeps first - second.
+template <int MASK>
+__device__ __forceinline__ void cross_stage(float (&v)[16], int lane) {
+  const bool second = (lane & MASK) != 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float o = lane_xor<MASK>(v[e]);
+    v[e] = second ? (o - v[e]) : (v[e] + o);
+  }
+}
+
+// Unnormalized FWHT of one 16-element chunk, stages h = 1, 2, 4, 8 in registers,
+// then h = 16, 32, 64 across lanes as the block size requires.
+template <int B>
+__device__ __forceinline__ void fwht_chunk(float (&v)[16], int lane) {
+  if constexpr (B > 0) {
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 16; i += 2 * h) {
+#pragma unroll
+        for (int j = i; j < i + h; ++j) {
+          const float a = v[j], b = v[j + h];
+          v[j] = a + b;
+          v[j + h] = a - b;
+        }
+      }
+    }
+    if constexpr (B >= 32) cross_stage<1>(v, lane);
+    if constexpr (B >= 64) cross_stage<2>(v, lane);
+    if constexpr (B >= 128) cross_stage<4>(v, lane);
+  }
+}
+
+__device__ __forceinline__ void load_chunk(const uint16_t* p, float (&v)[16]) {
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+  const uint4 a = q[0], b = q[1];
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+__device__ __forceinline__ uint32_t pack4_i8(float a, float b, float c, float d, float r) {
+  const int qa = (int)__builtin_amdgcn_fmed3f(rintf(a * r), -127.0f, 127.0f);
+  const int qb = (int)__builtin_amdgcn_fmed3f(rintf(b * r), -127.0f, 127.0f);
+  const int qc = (int)__builtin_amdgcn_fmed3f(rintf(c * r), -127.0f, 127.0f);
+  const int qd = (int)__builtin_amdgcn_fmed3f(rintf(d * r), -127.0f, 127.0f);
+  return (uint32_t)(qa & 0xFF) | ((uint32_t)(qb & 0xFF) << 8) | ((uint32_t)(qc & 0xFF) << 16) |
+         ((uint32_t)qd << 24);
+}
+
+// Row of a chunk index (c < 2^16, cr < 2^12): float estimate, then exact fix-up.
+__device__ __forceinline__ int row_of(int c, int cr, float inv_cr) {
+  int r = (int)((float)c * inv_cr);
+  if (r * cr > c) --r;
+  if ((r + 1) * cr <= c) ++r;
+  return r;
+}
+
+template <int B, int CPT>
+__global__ void __launch_bounds__(QT)
+quant_int8_kernel(const uint16_t* __restrict__ x, int M, int K, int rows_per_wg, float scale_div,
+                  int8_t* __restrict__ q, float* __restrict__ scale) {
+  __shared__ unsigned s_amax[QT * CPT / 2];
+  __shared__ float s_r[QT * CPT / 2];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int r0 = blockIdx.x * rows_per_wg;
+  const int rows = min(rows_per_wg, M - r0);
+  const int cr = K >> 4;
+  const int nchunks = rows * cr;
+  const float inv_cr = 1.0f / (float)cr;
+  const size_t base = (size_t)r0 * (size_t)K;
+
+  float v[CPT][16];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = i * QT + tid;
+    if (c < nchunks) {
+      load_chunk(x + base + (size_t)c * 16, v[i]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[i][e] = 0.0f;
+    }
+  }
+  for (int t = tid; t < rows; t += QT) s_amax[t] = 0u;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) fwht_chunk<B>(v[i], lane);
+  __syncthreads();
+
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = i * QT + tid;
+    if (c < nchunks) {
+      float m = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(v[i][e]));
+      // non-negative floats order like their bit patterns
+      atomicMax(&s_amax[row_of(c, cr, inv_cr)], __float_as_uint(m));
+    }
+  }
+  __syncthreads();
+  for (int t = tid; t < rows; t += QT) {
+    const float a = __uint_as_float(s_amax[t]);
+    s_r[t] = a > 0.0f ? 127.0f / a : 0.0f;
+    scale[r0 + t] = (a / 127.0f) / scale_div;
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = i * QT + tid;
+    if (c < nchunks) {
+      const float r = s_r[row_of(c, cr, inv_cr)];
+      uint4 o;
+      o.x = pack4_i8(v[i][0], v[i][1], v[i][2], v[i][3], r);
+      o.y = pack4_i8(v[i][4], v[i][5], v[i][6], v[i][7], r);
+      o.z = pack4_i8(v[i][8], v[i][9], v[i][10], v[i][11], r);
+      o.w = pack4_i8(v[i][12], v[i][13], v[i][14], v[i][15], r);
+      *reinterpret_cast<uint4*>(q + base + (size_t)c * 16) = o;
+    }
+  }
+}
+
+// E2M1 code of t (already scaled by 2^-X): nearest of {0,.5,1,1.5,2,3,4,6},
+// ties to the even mantissa bit, saturating at 6; -0 encodes as +0.
+__device__ __forceinline__ uint32_t e2m1_code(float t) {
+  const float m = fabsf(t);
+  uint32_t c = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) +
+               (uint32_t)(m >= 1.75f) + (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) +
+               (uint32_t)(m > 5.0f);
+  if (t < 0.0f && c != 0u) c |= 8u;
+  return c;
+}
+
+template <int B, int CPT>
+__global__ void __launch_bounds__(QT)
+quant_mx_kernel(const uint16_t* __restrict__ x, long long nchunks, uint8_t* __restrict__ qf,
+                uint8_t* __restrict__ e8) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const long long c = ((long long)blockIdx.x * CPT + i) * QT + tid;
+    const bool valid = c < nchunks;
+    float v[16];
+    if (valid) {
+      load_chunk(x + c * 16, v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[e] = 0.0f;
+    }
+    fwht_chunk<B>(v, lane);
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(v[e]));
+    m = fmaxf(m, lane_xor<1>(m));  // the 32-block spans this lane and its XOR-1 partner
+    const uint32_t bits = __float_as_uint(m);
+    const int ex = (int)((bits >> 23) & 0xFFu);
+    int X;
+    if (m == 0.0f) {
+      X = 0;
+    } else if (ex == 0) {
+      X = -127;  // subnormal amax: floor(log2) <= -127
+    } else {
+      X = min(max(ex - 127 - 2, -127), 127);
+    }
+    const float inv = __uint_as_float((uint32_t)(127 - X) << 23);  // 2^-X, exact
+    uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) lo |= e2m1_code(v[e] * inv) << (4 * e);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hi |= e2m1_code(v[8 + e] * inv) << (4 * e);
+    if (valid) {
+      *reinterpret_cast<uint2*>(qf + c * 8) = make_uint2(lo, hi);
+      if ((c & 1) == 0) e8[c >> 1] = (uint8_t)(X + 127);
+    }
+  }
+}
+
+template <int B>
+hipError_t dispatch_int8_cpt(int cpt, int grid, int rows, const uint16_t* x, int M, int K,
+                             float scale_div, int8_t* q, float* scale, hipStream_t s) {
+  switch (cpt) {
+    case 1: quant_int8_kernel<B, 1><<<grid, QT, 0, s>>>(x, M, K, rows, scale_div, q, scale); break;
+    case 2: quant_int8_kernel<B, 2><<<grid, QT, 0, s>>>(x, M, K, rows, scale_div, q, scale); break;
+    case 4: quant_int8_kernel<B, 4><<<grid, QT, 0, s>>>(x, M, K, rows, scale_div, q, scale); break;
+    default: quant_int8_kernel<B, 8><<<grid, QT, 0, s>>>(x, M, K, rows, scale_div, q, scale); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_int8(const uint16_t* x, int M, int K, int had_block, float scale_div,
+                             int8_t* q, float* scale, hipStream_t stream) {
+  if (M <= 0) return hipSuccess;
+  const int cr = K / 16;
+  // Chunks per thread: the smallest of 1, 2, 4, 8 that keeps >= 90% of the
+  // workgroup's slots busy with whole rows; otherwise the best utilization.
+  int best_cpt = 8;
+  double best_util = -1.0;
+  for (int cpt : {1, 2, 4, 8}) {
+    const int slots = QT * cpt;
+    if (slots < cr) continue;
+    const int rows = slots / cr;
+    const double util = (double)(rows * cr) / slots;
+    if (util >= 0.9) {
+      best_cpt = cpt;
+      break;
+    }
+    if (util > best_util) {
+      best_util = util;
+      best_cpt = cpt;
+    }
+  }
+  const int rows = (QT * best_cpt) / cr;
+  const int grid = (M + rows - 1) / rows;
+  switch (had_block) {
+    case 0: return dispatch_int8_cpt<0>(best_cpt, grid, rows, x, M, K, scale_div, q, scale, stream);
+    case 32: return dispatch_int8_cpt<32>(best_cpt, grid, rows, x, M, K, scale_div, q, scale, stream);
+    case 64: return dispatch_int8_cpt<64>(best_cpt, grid, rows, x, M, K, scale_div, q, scale, stream);
+    default: return dispatch_int8_cpt<128>(best_cpt, grid, rows, x, M, K, scale_div, q, scale, stream);
+  }
+}
+
+hipError_t launch_quant_mx(const uint16_t* x, int M, int K, int had_block, uint8_t* q_fp4,
+                           uint8_t* e8m0, hipStream_t stream) {
+  if (M <= 0) return hipSuccess;
+  constexpr int CPT = 4;
+  const long long nchunks = (long long)M * K / 16;
+  const long long per_wg = (long long)QT * CPT;
+  const int grid = (int)((nchunks + per_wg - 1) / per_wg);
+  if (had_block == 32) {
+    quant_mx_kernel<32, CPT><<<grid, QT, 0, stream>>>(x, nchunks, q_fp4, e8m0);
+  } else {
+    quant_mx_kernel<0, CPT><<<grid, QT, 0, stream>>>(x, nchunks, q_fp4, e8m0);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tabit

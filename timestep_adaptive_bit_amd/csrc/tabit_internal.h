@@ -1,0 +1,59 @@
+// Internal declarations shared by the HIP translation units of libtabit.
+// Not part of the public ABI (see include/tabit.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+namespace tabit {
+
+// ---------------------------------------------------------------- quantizers
+// Per-row INT8 quantization with an optional block FWHT (activations and
+// weights).  scale_div divides the per-row scale a/127 (1 for activations,
+// max(b, 1) for weights).
+hipError_t launch_quant_int8(const uint16_t* x, int M, int K, int had_block, float scale_div,
+                             int8_t* q, float* scale, hipStream_t stream);
+
+// MXFP4 quantization (block 32, optional FWHT32).
+hipError_t launch_quant_mx(const uint16_t* x, int M, int K, int had_block,
+                           uint8_t* q_fp4, uint8_t* e8m0, hipStream_t stream);
+
+// ---------------------------------------------------------------- INT8 GEMM
+struct GemmConfig {
+  int bm, bn, split_k;
+};
+int gemm_config_count();
+GemmConfig gemm_config(int index);
+int gemm_config_choose(int M, int N, int K, int num_cus);
+
+hipError_t launch_gemm_i8(int cfg, bool bitserial, const int8_t* xq, const float* sa,
+                          const int8_t* wq, const float* sw, int M, int N, int K, int kbits,
+                          uint16_t* y, int32_t* acc, hipStream_t stream);
+
+// ---------------------------------------------------------------- MXFP4 GEMM
+int mx_config_count();
+GemmConfig mx_config(int index);
+int mx_config_choose(int M, int N, int K, int num_cus);
+
+hipError_t launch_gemm_mxfp4(int cfg, const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
+                             const uint8_t* we, int M, int N, int K, float out_scale,
+                             uint16_t* y, float* acc, hipStream_t stream);
+
+// Compute units of the current device (cached per device id).
+int device_num_cus();
+
+}  // namespace tabit
+
+struct tabit_ctx {
+  std::string err;
+  int steps = 0;
+  int layers = 0;
+  std::vector<uint8_t> k_bits;
+  std::vector<uint8_t> fmt;
+  int force_gemm_cfg = -1;
+  int force_mx_cfg = -1;
+};
