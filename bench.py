@@ -119,6 +119,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=512)
     ap.add_argument("--no-events", action="store_true", help="skip per-GEMM event timing")
+    ap.add_argument("--no-tune", action="store_true", help="skip the warm-up tile autotuning")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -172,6 +173,28 @@ def main() -> int:
     for t in range(Tn):
         for li, layer in enumerate(wl.layers):
             x_ptrs[t * L + li] = xs[(t, layer.M, layer.K)].data_ptr()
+
+    # ---- warm-up tuning: time every tile configuration once per distinct GEMM shape
+    tuned = {}
+    if not args.no_tune:
+        for li, layer in enumerate(wl.layers):
+            for fmt in sorted(set(int(f) for f in wl.fmt[:, li])):
+                key = (fmt, layer.M, layer.N, layer.K)
+                if key in tuned:
+                    continue
+                x = xs[(0, layer.M, layer.K)]
+                if fmt == 0:
+                    xq, xs_ = ctx.hadamard_quant_act(x, b, T.FMT_INT8)
+                    tuned[key] = ctx.autotune_gemm(path, xq, xs_, weights[li]["w_q"],
+                                                   weights[li]["w_scale"], layer.M, layer.N,
+                                                   layer.K, 2, ys[li], reps=3)
+                else:
+                    xf, xe = ctx.hadamard_quant_act(x, b, T.FMT_MXFP4)
+                    tuned[key] = ctx.autotune_gemm(T.PATH_MXFP4_GEMM, xf, xe, weights[li]["w_fp4"],
+                                                   weights[li]["w_e8m0"], layer.M, layer.N,
+                                                   layer.K, 0, ys[li], reps=3)
+                del x
+        torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev).cuda_stream
     hip = Hip()
@@ -264,6 +287,8 @@ def main() -> int:
         "frac_of_int8_peak": round(value / INT8_PEAK_TOPS, 4),
         "roofline": roofline,
         "detail": detail,
+        "tuned_tiles": {f"{'mxfp4' if k[0] else 'int8'} {k[1]}x{k[2]}x{k[3]}": T.gemm_config_info(v)[:2]
+                        if k[0] == 0 else v for k, v in tuned.items()},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows)

@@ -230,6 +230,22 @@ int tabit_run_schedule(tabit_ctx* ctx, int first_step, int num_steps, const tabi
                        void* act_ws, size_t act_ws_bytes, void* const* gemm_events, void* stream);
 
 /*
+ * Autotune the tile configuration for one GEMM problem: time every
+ * configuration of the GEMM `path` (TABIT_PATH_MASKED, TABIT_PATH_BITSERIAL, or
+ * 2 for the MXFP4 GEMM) on the caller's buffers, `reps` launches each, and
+ * remember the fastest for (path, M, N, K) in ctx; later calls with that shape
+ * on that path use it (an explicit TABIT_OPT_*_CONFIG still wins).  The
+ * buffers follow the layouts of tabit_masked_qgemm (path 0/1: x_q int8,
+ * x_scale fp32, w_q int8, w_scale fp32) or tabit_mxfp4_qgemm (path 2: x_fp4,
+ * x_e8m0, w_fp4, w_e8m0); y_bf16 [M][N] receives scratch results.
+ * Synchronizes `stream` to read the timings: call it outside graph capture,
+ * e.g. during warm-up.  *best_cfg (may be NULL) receives the winner.
+ */
+int tabit_autotune_gemm(tabit_ctx* ctx, int path, const void* x_q, const void* x_scale,
+                        const void* w_q, const void* w_scale, int M, int N, int K, int k_bits,
+                        uint16_t* y_bf16, int reps, int* best_cfg, void* stream);
+
+/*
  * Options (tests and tuning).  TABIT_OPT_GEMM_CONFIG forces the INT8 GEMM tile
  * configuration (value = index from tabit_gemm_config_info, -1 = automatic);
  * TABIT_OPT_MXFP4_CONFIG likewise for the MXFP4 GEMM.  EINVAL for an unknown

@@ -22,6 +22,7 @@ OK, EINVAL, ESHAPE, EALIGN, ERANGE, ENOSCHED, EHIP, ENOMEM = 0, -1, -2, -3, -4, 
 FMT_INT8, FMT_MXFP4 = 0, 1
 PATH_MASKED, PATH_BITSERIAL = 0, 1
 OPT_GEMM_CONFIG, OPT_MXFP4_CONFIG = 0, 1
+PATH_MXFP4_GEMM = 2
 
 _c_int, _c_void_p, _c_size_t, _c_float = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
 _PINT = ctypes.POINTER(ctypes.c_int)
@@ -51,6 +52,9 @@ _SIGNATURES = {
                                         _c_void_p, _c_void_p, _c_size_t, _c_void_p, _c_void_p]),
     "tabit_run_schedule": (_c_int, [_c_void_p, _c_int, _c_int, _c_void_p, _c_int, _c_void_p,
                                     _c_int, _c_int, _c_void_p, _c_size_t, _c_void_p, _c_void_p]),
+    "tabit_autotune_gemm": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                     _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_int, _PINT,
+                                     _c_void_p]),
     "tabit_set_option": (_c_int, [_c_void_p, _c_int, _c_int]),
     "tabit_gemm_config_info": (_c_int, [_c_int, _PINT, _PINT, _PINT]),
     "tabit_gemm_config_choose": (_c_int, [_c_int, _c_int, _c_int, _c_int]),
@@ -342,3 +346,13 @@ class Context:
             act_ws.numel() * act_ws.element_size(),
             None if gemm_events is None else ctypes.cast(gemm_events, ctypes.c_void_p), stream)
         self._check(st)
+
+    def autotune_gemm(self, path: int, x_q, x_scale, w_q, w_scale, M: int, N: int, K: int,
+                      k_bits: int, y: torch.Tensor, reps: int = 3) -> int:
+        """Time every tile configuration for (path, M, N, K); the ctx keeps the fastest."""
+        best = ctypes.c_int(-1)
+        st = self._lib.tabit_autotune_gemm(self._h, path, x_q.data_ptr(), x_scale.data_ptr(),
+                                           w_q.data_ptr(), w_scale.data_ptr(), M, N, K, k_bits,
+                                           y.data_ptr(), reps, ctypes.byref(best), _stream(y.device))
+        self._check(st)
+        return best.value

@@ -73,6 +73,7 @@ int gemm_i8_common(tabit_ctx* ctx, bool bitserial, const int8_t* x_q, const floa
   if (k_bits < 0 || k_bits > 7) return fail(ctx, TABIT_ERANGE, "k_bits must be in [0, 7] (got %d)", k_bits);
   if (M == 0 || N == 0) return TABIT_OK;
   int cfg = ctx->force_gemm_cfg;
+  if (cfg < 0) cfg = ctx->tuned_cfg(bitserial ? 1 : 0, M, N, K);
   if (cfg < 0) cfg = tabit::gemm_config_choose(M, N, K, tabit::device_num_cus());
   return hip_status(ctx,
                     tabit::launch_gemm_i8(cfg, bitserial, x_q, x_scale, w_q, w_scale, M, N, K,
@@ -245,6 +246,7 @@ int tabit_mxfp4_qgemm(tabit_ctx* ctx, const uint8_t* x_fp4, const uint8_t* x_e8m
   if (!(out_scale == out_scale)) return fail(ctx, TABIT_EINVAL, "out_scale is NaN");
   if (M == 0 || N == 0) return TABIT_OK;
   int cfg = ctx->force_mx_cfg;
+  if (cfg < 0) cfg = ctx->tuned_cfg(2, M, N, K);
   if (cfg < 0) cfg = tabit::mx_config_choose(M, N, K, tabit::device_num_cus());
   return hip_status(ctx,
                     tabit::launch_gemm_mxfp4(cfg, x_fp4, x_e8m0, w_fp4, w_e8m0, M, N, K, out_scale,
@@ -373,8 +375,9 @@ int tabit_run_schedule(tabit_ctx* ctx, int first_step, int num_steps, const tabi
         e = tabit::launch_quant_int8(x, L.M, L.K, had_block, 1.0f, xq, sa, s);
         if (e != hipSuccess) return hip_status(ctx, e, "run_schedule quantizer launch");
         if (e0 && (e = hipEventRecord(e0, s)) != hipSuccess) return hip_status(ctx, e, "event record");
-        int cfg = ctx->force_gemm_cfg >= 0 ? ctx->force_gemm_cfg
-                                           : tabit::gemm_config_choose(L.M, L.N, L.K, num_cus);
+        int cfg = ctx->force_gemm_cfg;
+        if (cfg < 0) cfg = ctx->tuned_cfg(path == TABIT_PATH_BITSERIAL ? 1 : 0, L.M, L.N, L.K);
+        if (cfg < 0) cfg = tabit::gemm_config_choose(L.M, L.N, L.K, num_cus);
         e = tabit::launch_gemm_i8(cfg, path == TABIT_PATH_BITSERIAL, xq, sa, L.w_q, L.w_scale, L.M,
                                   L.N, L.K, ctx->k_bits[i], L.y_bf16, nullptr, s);
         if (e != hipSuccess) return hip_status(ctx, e, "run_schedule GEMM launch");
@@ -384,8 +387,9 @@ int tabit_run_schedule(tabit_ctx* ctx, int first_step, int num_steps, const tabi
         e = tabit::launch_quant_mx(x, L.M, L.K, had_block, xf, xe, s);
         if (e != hipSuccess) return hip_status(ctx, e, "run_schedule MX quantizer launch");
         if (e0 && (e = hipEventRecord(e0, s)) != hipSuccess) return hip_status(ctx, e, "event record");
-        int cfg = ctx->force_mx_cfg >= 0 ? ctx->force_mx_cfg
-                                         : tabit::mx_config_choose(L.M, L.N, L.K, num_cus);
+        int cfg = ctx->force_mx_cfg;
+        if (cfg < 0) cfg = ctx->tuned_cfg(2, L.M, L.N, L.K);
+        if (cfg < 0) cfg = tabit::mx_config_choose(L.M, L.N, L.K, num_cus);
         e = tabit::launch_gemm_mxfp4(cfg, xf, xe, L.w_fp4, L.w_e8m0, L.M, L.N, L.K,
                                      1.0f / (float)(had_block > 0 ? had_block : 1), L.y_bf16,
                                      nullptr, s);
@@ -394,6 +398,61 @@ int tabit_run_schedule(tabit_ctx* ctx, int first_step, int num_steps, const tabi
       if (e1 && (e = hipEventRecord(e1, s)) != hipSuccess) return hip_status(ctx, e, "event record");
     }
   }
+  return TABIT_OK;
+}
+
+int tabit_autotune_gemm(tabit_ctx* ctx, int path, const void* x_q, const void* x_scale,
+                        const void* w_q, const void* w_scale, int M, int N, int K, int k_bits,
+                        uint16_t* y_bf16, int reps, int* best_cfg, void* stream) {
+  if (ctx == nullptr) return TABIT_EINVAL;
+  if (path < 0 || path > 2) return fail(ctx, TABIT_EINVAL, "unknown GEMM path %d", path);
+  if (y_bf16 == nullptr) return fail(ctx, TABIT_EINVAL, "autotune needs y_bf16");
+  if (reps < 1) return fail(ctx, TABIT_EINVAL, "reps must be >= 1");
+  int st = check_gemm(ctx, x_q, x_scale, w_q, w_scale, M, N, K, y_bf16, nullptr);
+  if (st != TABIT_OK) return st;
+  if (k_bits < 0 || k_bits > 7) return fail(ctx, TABIT_ERANGE, "k_bits must be in [0, 7] (got %d)", k_bits);
+  if (M == 0 || N == 0) return TABIT_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int n = path == 2 ? tabit::mx_config_count() : tabit::gemm_config_count();
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  if (e != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return hip_status(ctx, e, "autotune event create");
+  }
+  auto launch = [&](int cfg) {
+    if (path == 2)
+      return tabit::launch_gemm_mxfp4(cfg, static_cast<const uint8_t*>(x_q),
+                                      static_cast<const uint8_t*>(x_scale),
+                                      static_cast<const uint8_t*>(w_q),
+                                      static_cast<const uint8_t*>(w_scale), M, N, K, 1.0f, y_bf16,
+                                      nullptr, s);
+    return tabit::launch_gemm_i8(cfg, path == 1, static_cast<const int8_t*>(x_q),
+                                 static_cast<const float*>(x_scale), static_cast<const int8_t*>(w_q),
+                                 static_cast<const float*>(w_scale), M, N, K, k_bits, y_bf16,
+                                 nullptr, s);
+  };
+  int best = -1;
+  float best_ms = 0.0f;
+  for (int cfg = 0; cfg < n && e == hipSuccess; ++cfg) {
+    e = launch(cfg);                                     // warm-up
+    if (e == hipSuccess) e = hipEventRecord(e0, s);
+    for (int r = 0; r < reps && e == hipSuccess; ++r) e = launch(cfg);
+    if (e == hipSuccess) e = hipEventRecord(e1, s);
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    float ms = 0.0f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+    if (e == hipSuccess && (best < 0 || ms < best_ms)) {
+      best = cfg;
+      best_ms = ms;
+    }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (e != hipSuccess) return hip_status(ctx, e, "autotune");
+  ctx->tuned[std::make_tuple(path, M, N, K)] = best;
+  if (best_cfg) *best_cfg = best;
   return TABIT_OK;
 }
 

@@ -8,253 +8,210 @@
 // significant bits; the same kernel serves every k (k is a scalar argument).
 // The bit-plane form evaluates sum_{b=k}^{7} c_b (Xq . W_b^T) with W_b bit b of
 // the two's-complement byte (c_b = 2^b, sign plane -2^7): the activation
-// fragment is loaded once per K-tile and reused against each retained plane,
+// fragment is loaded once per K-step and reused against each retained plane,
 // the analogue of the Temporal-Precision Engine keeping activation planes on
 // chip and streaming only the selected weight planes.  A plane is the byte
 // W & (1 << b) read as int8 ({0, 2^b}, or {0, -128} for b = 7), so its MFMA
 // product is exactly c_b (Xq . W_b^T).
 //
-// Both operands are K-contiguous ([M][K] and [N][K]).  A workgroup computes a
-// BM x BN tile with 2 x 2 waves; K advances in 128-byte steps through a
-// double-buffered LDS tile (one barrier per step).  LDS rows are 128 bytes,
-// 16-byte chunks XOR-swizzled by (row & 7) ^ ((row >> 3) & 1), which keeps
-// both the staging writes and the MFMA operand reads (16 rows x one chunk per
-// 16 lanes) free of bank conflicts.  The step's LSB mask is applied to the
-// weight tile as it is staged into LDS.  The epilogue scales in fp32, rounds to
-// bf16 and transposes through LDS so that global stores are 16-byte and
-// row-contiguous.  Workgroup ids are remapped so that consecutive tiles stay on
-// one XCD (dispatch round-robins workgroups over the 8 XCDs, each with its own
-// L2), and tiles are walked in groups of 4 tile-rows for L2 reuse.
+// Both operands are K-contiguous ([M][K] and [N][K]).  A workgroup of WM x WN
+// waves computes a BM x BN tile; K advances in 128-byte stages copied straight
+// from global memory into a double-buffered LDS tile by buffer loads (no
+// register staging; rows and chunks out of range arrive as zeros) into an
+// NST-deep ring of LDS stages: up to NST-1 stages are in flight, so the
+// copy latency (an L2 miss costs about as much as a stage of MFMAs) hides
+// under the compute.  One barrier per stage.  The step's LSB mask is applied to the weight
+// fragments as they come out of LDS (four v_and per 16-byte fragment).  The
+// matrix-core op is v_mfma_i32_32x32x32_i8 (it sustains ~90% of the chip's INT8
+// rate with a few independent accumulators per wave).  The
+// epilogue scales in fp32, rounds to bf16 and transposes through LDS for
+// 16-byte row-contiguous stores.
 #include "tabit_internal.h"
+#include "tile_common.h"
 
 namespace tabit {
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
+using tile::v4i;
+typedef int v16i __attribute__((ext_vector_type(16)));
+using tile::BKB;
 
-constexpr int BK = 128;  // bytes (= int8 elements) of K per LDS stage
-
-__device__ __forceinline__ int lds_off(int r, int c) {
-  return r * BK + ((c ^ ((r & 7) ^ ((r >> 3) & 1))) << 4);
-}
-
-__device__ __forceinline__ uint16_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-// Logical tile of this workgroup: undo the round-robin XCD dispatch so that
-// each XCD receives a contiguous range of logical ids, then walk tiles in
-// groups of GROUP_M tile-rows (column-major within the group).
-template <int GROUP_M>
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int G = tiles_m * tiles_n;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, j = bid >> 3;
-  const int q = G >> 3, rem = G & 7;
-  const int lin = xcd * q + min(xcd, rem) + j;
-  const int per_group = GROUP_M * tiles_n;
-  const int g = lin / per_group;
-  const int first_m = g * GROUP_M;
-  const int gsz = min(tiles_m - first_m, GROUP_M);
-  const int in_g = lin - g * per_group;
-  tm = first_m + in_g % gsz;
-  tn = in_g / gsz;
-}
-
-template <int BM, int BN, bool BITSERIAL>
-__global__ void __launch_bounds__(256)
+template <int BM, int BN, int WM, int WN, int RB, int NST, bool BITSERIAL>
+__global__ void __launch_bounds__(WM* WN * 64)
 gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
                const int8_t* __restrict__ B, const float* __restrict__ SB, int M, int N, int K,
                int kbits, uint16_t* __restrict__ Y, int32_t* __restrict__ ACC, int tiles_m,
                int tiles_n) {
-  constexpr int NT = 256;
-  constexpr int WM = 2, WN = 2;
+  constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int FM = WTM / 16, FN = WTN / 16;
-  constexpr int A_LD = BM * (BK / 16) / NT;
-  constexpr int B_LD = BN * (BK / 16) / NT;
-  constexpr int STAGE = (BM + BN) * BK;
-  static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for 256 threads");
-  static_assert(2 * STAGE >= BM * BN * 2, "epilogue tile must fit in the LDS stages");
-  __shared__ __attribute__((aligned(16))) int8_t smem[2 * STAGE];
+  constexpr int FM = WTM / 32, FN = WTN / 32;   // 32 x 32 MFMA blocks per wave
+  constexpr int KS = RB / 32;                   // MFMA K-steps (32 bytes) per stage
+  constexpr int STAGE = (BM + BN) * RB;
+  constexpr int DPW = STAGE / 1024 / NW;        // DMA instructions per wave per stage
+  static_assert(FM >= 1 && FN >= 1, "wave tile must hold whole 32x32 blocks");
+  static_assert(NST >= 2 && NST <= 4, "2 to 4 LDS stages");
+  static_assert(NST * STAGE >= BM * BN * 2, "epilogue tile must fit in the LDS stages");
+  __shared__ __attribute__((aligned(1024))) int8_t smem[NST * STAGE];
 
   int tm, tn;
-  tile_coords<4>(tiles_m, tiles_n, tm, tn);
+  tile::tile_coords<4>(tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave / WN, wn = wave % WN;
+  const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
+  const auto rsa = tile::make_rsrc(A, (unsigned)M * (unsigned)K);
+  const auto rsb = tile::make_rsrc(B, (unsigned)N * (unsigned)K);
 
   const uint32_t m8 = (0xFFu << kbits) & 0xFFu;
   const int mask32 = (int)(m8 * 0x01010101u);
 
-  v4i ra[A_LD], rb[B_LD];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const int qd = i * NT + tid, r = qd >> 3, c = qd & 7;
-      const int gm = m0 + r, gk = k0 + c * 16;
-      ra[i] = (gm < M && gk < K) ? *reinterpret_cast<const v4i*>(A + (size_t)gm * K + gk)
-                                 : v4i{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      const int qd = i * NT + tid, r = qd >> 3, c = qd & 7;
-      const int gn = n0 + r, gk = k0 + c * 16;
-      rb[i] = (gn < N && gk < K) ? *reinterpret_cast<const v4i*>(B + (size_t)gn * K + gk)
-                                 : v4i{0, 0, 0, 0};
-    }
-  };
-  auto sstore = [&](int buf) {
-    int8_t* sa = smem + buf * STAGE;
-    int8_t* sb = sa + BM * BK;
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const int qd = i * NT + tid;
-      *reinterpret_cast<v4i*>(sa + lds_off(qd >> 3, qd & 7)) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      const int qd = i * NT + tid;
-      v4i w = rb[i];
-      if constexpr (!BITSERIAL) w &= mask32;  // TASQ LSB mask, applied while staging
-      *reinterpret_cast<v4i*>(sb + lds_off(qd >> 3, qd & 7)) = w;
-    }
-  };
-
-  v4i acc[FM][FN];
+  v16i acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    for (int j = 0; j < FN; ++j) acc[i][j] = v16i{};
 
-  const int nk = (K + BK - 1) / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-    const int8_t* sa = smem + cur * STAGE;
-    const int8_t* sb = sa + BM * BK;
+  // operand rows this lane reads: A rows wm*WTM + i*32 + lane%32, B likewise
+  const int ra0 = wm * WTM + (lane & 31), rb0 = wn * WTN + (lane & 31);
+  const int khalf = lane >> 5;   // which 16-byte half of the 32-byte K-step
+
+  const int nk = (K + RB - 1) / RB;
+  auto issue = [&](int kt) {
+    int8_t* dst = smem + (kt % NST) * STAGE;
+    tile::dma_stage<BM, NW, RB>(rsa, dst, m0, rows_a, K, kt * RB, wave, lane);
+    tile::dma_stage<BN, NW, RB>(rsb, dst + BM * RB, n0, rows_b, K, kt * RB, wave, lane);
+  };
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int c = kk * 4 + (lane >> 4);
-      v4i a[FM], b[FN];
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < nk) issue(s);
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt has landed once at most (stages issued after it) x DPW copies are pending
+    const int ahead = min(NST - 2, nk - 1 - kt);
+    if (NST >= 4 && ahead >= 2) tile::wait_vmcnt<(NST >= 4 ? 2 : 0) * DPW>();
+    else if (NST >= 3 && ahead >= 1) tile::wait_vmcnt<(NST >= 3 ? 1 : 0) * DPW>();
+    else tile::wait_vmcnt<0>();
+    __syncthreads();   // stage kt visible to all; stage kt-1's buffer free for reuse
+    if (kt + NST - 1 < nk) issue(kt + NST - 1);
+    const int8_t* sa = smem + (kt % NST) * STAGE;
+    const int8_t* sb = sa + BM * RB;
+    v4i a[2][FM], b[2][FN];
+    auto load = [&](int ks, int buf) {
+      const int c = ks * 2 + khalf;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        a[i] = *reinterpret_cast<const v4i*>(sa + lds_off(wm * WTM + i * 16 + (lane & 15), c));
+        a[buf][i] = *reinterpret_cast<const v4i*>(sa + tile::lds_off<RB>(ra0 + i * 32, c));
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        b[j] = *reinterpret_cast<const v4i*>(sb + lds_off(wn * WTN + j * 16 + (lane & 15), c));
+        b[buf][j] = *reinterpret_cast<const v4i*>(sb + tile::lds_off<RB>(rb0 + j * 32, c));
+    };
+    load(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < KS) load(ks + 1, cur ^ 1);
       if constexpr (!BITSERIAL) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int j = 0; j < FN; ++j) {
+          const v4i bm = b[cur][j] & mask32;   // TASQ LSB mask on the staged weight tile
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+          for (int i = 0; i < FM; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[cur][i], bm, acc[i][j], 0, 0, 0);
+        }
       } else {
         for (int p = 7; p >= kbits; --p) {
           const int pm = (int)(0x01010101u << p);
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
-            const v4i bp = b[j] & pm;
+            const v4i bp = b[cur][j] & pm;
 #pragma unroll
             for (int i = 0; i < FM; ++i)
-              acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], bp, acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[cur][i], bp, acc[i][j], 0, 0, 0);
           }
         }
       }
     }
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
   }
 
   // ------------------------------------------------------------ epilogue
-  // MFMA 16x16 output layout: lane l, register r holds row 4*(l/16)+r, col l%16.
-  const int row_base = m0 + wm * WTM + 4 * (lane >> 4);
-  const int col_base = n0 + wn * WTN + (lane & 15);
+  // 32x32 output layout: lane l, register r holds row (r/4)*8 + (l/32)*4 + r%4, col l%32.
+  const int row_w = m0 + wm * WTM, col_w = n0 + wn * WTN;
   if (ACC != nullptr) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int gm = row_base + i * 16 + r, gn = col_base + j * 16;
+        for (int r = 0; r < 16; ++r) {
+          const int gm = row_w + i * 32 + (r >> 2) * 8 + khalf * 4 + (r & 3);
+          const int gn = col_w + j * 32 + (lane & 31);
           if (gm < M && gn < N) ACC[(size_t)gm * N + gn] = acc[i][j][r];
         }
   }
   if (Y != nullptr) {
-    float sa_r[FM][4], sb_c[FN];
+    // per-row scales: this lane's rows come in runs of 4 (r%4), so load float4s
+    float sa_r[FM][16], sb_c[FN];
+    const bool sa16 = (reinterpret_cast<uintptr_t>(SA) & 15) == 0;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int gm = row_base + i * 16 + r;
-        sa_r[i][r] = gm < M ? SA[gm] : 0.0f;
+      for (int g = 0; g < 4; ++g) {
+        const int gm = row_w + i * 32 + g * 8 + khalf * 4;
+        if (sa16 && gm + 3 < M) {
+          const float4 v = *reinterpret_cast<const float4*>(SA + gm);
+          sa_r[i][g * 4 + 0] = v.x;
+          sa_r[i][g * 4 + 1] = v.y;
+          sa_r[i][g * 4 + 2] = v.z;
+          sa_r[i][g * 4 + 3] = v.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sa_r[i][g * 4 + e] = gm + e < M ? SA[gm + e] : 0.0f;
+        }
       }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int gn = col_base + j * 16;
+      const int gn = col_w + j * 32 + (lane & 31);
       sb_c[j] = gn < N ? SB[gn] : 0.0f;
     }
-    // Each wave stages its WTM x WTN bf16 tile in its own LDS region; 16-byte
-    // column chunks are XOR-swizzled by the row so the scattered 2-byte writes
-    // and the row-contiguous 16-byte reads avoid bank conflicts.
-    constexpr int CH = WTN / 8;  // 16-byte chunks per staged row
+    __syncthreads();  // every wave is done reading the last stage
     uint16_t* st = reinterpret_cast<uint16_t*>(smem) + wave * WTM * WTN;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int lr = i * 16 + 4 * (lane >> 4) + r;
-          const int lc = j * 16 + (lane & 15);
-          const float f = ((float)acc[i][j][r] * sa_r[i][r]) * sb_c[j];
-          const int ch = (lc >> 3) ^ (lr & (CH - 1));
-          st[lr * WTN + ch * 8 + (lc & 7)] = bf16_rne(f);
-        }
-    __syncthreads();
-#pragma unroll
-    for (int it = 0; it < WTM * CH / 64; ++it) {
-      const int idx = it * 64 + lane;
-      const int lr = idx / CH, ch = idx % CH;
-      const int gm = m0 + wm * WTM + lr, gn = n0 + wn * WTN + ch * 8;
-      const uint4 v = *reinterpret_cast<const uint4*>(st + lr * WTN + ((ch ^ (lr & (CH - 1))) * 8));
-      if (gm < M && gn < N) *reinterpret_cast<uint4*>(Y + (size_t)gm * N + gn) = v;
-    }
+    tile::store_tile32_bf16<WTM, WTN>(st, lane, Y, row_w, col_w, M, N, [&](int i, int j, int r) {
+      return tile::bf16_rne(((float)acc[i][j][r] * sa_r[i][r]) * sb_c[j]);
+    });
   }
 }
 
 struct CfgDesc {
-  int bm, bn;
-  float eff;  // relative MFMA efficiency used by the automatic choice
+  int bm, bn, wm, wn, rb, nst;
+  int slots;    // workgroups one CU holds at once (LDS and register limits)
+  float rate;   // relative per-CU throughput when busy (measured on MI355X)
 };
-constexpr CfgDesc kCfgs[] = {
-    {256, 256, 1.00f},
-    {256, 128, 0.92f},
-    {128, 128, 0.85f},
-    {128, 64, 0.70f},
-    {64, 64, 0.50f},
-};
+// index, BM, BN, WM, WN, stage row bytes, LDS stages, slots per CU, rate
+#define TABIT_I8_CONFIGS(X)                \
+  X(0, 256, 256, 2, 4, 128, 2, 1, 1.00f)    \
+  X(1, 192, 192, 2, 3, 128, 3, 1, 0.80f)    \
+  X(2, 128, 128, 2, 2, 128, 2, 2, 0.95f)    \
+  X(3, 256, 128, 2, 2, 128, 3, 1, 0.75f)    \
+  X(4, 128, 64, 2, 2, 128, 2, 3, 0.75f)     \
+  X(5, 64, 64, 2, 2, 128, 2, 4, 0.55f)      \
+  X(6, 192, 128, 2, 2, 128, 2, 1, 0.70f)
+#define TABIT_DESC(I, BM, BN, WM, WN, RB, NST, SLOTS, RATE) {BM, BN, WM, WN, RB, NST, SLOTS, RATE},
+constexpr CfgDesc kCfgs[] = {TABIT_I8_CONFIGS(TABIT_DESC)};
+#undef TABIT_DESC
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
-template <int BM, int BN>
+template <int BM, int BN, int WM, int WN, int RB, int NST>
 hipError_t launch_cfg(bool bitserial, const int8_t* xq, const float* sa, const int8_t* wq,
                       const float* sw, int M, int N, int K, int kbits, uint16_t* y, int32_t* acc,
                       hipStream_t s) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int grid = tiles_m * tiles_n;
   if (bitserial)
-    gemm_i8_kernel<BM, BN, true><<<grid, 256, 0, s>>>(xq, sa, wq, sw, M, N, K, kbits, y, acc,
-                                                      tiles_m, tiles_n);
+    gemm_i8_kernel<BM, BN, WM, WN, RB, NST, true><<<grid, WM * WN * 64, 0, s>>>(
+        xq, sa, wq, sw, M, N, K, kbits, y, acc, tiles_m, tiles_n);
   else
-    gemm_i8_kernel<BM, BN, false><<<grid, 256, 0, s>>>(xq, sa, wq, sw, M, N, K, kbits, y, acc,
-                                                       tiles_m, tiles_n);
+    gemm_i8_kernel<BM, BN, WM, WN, RB, NST, false><<<grid, WM * WN * 64, 0, s>>>(
+        xq, sa, wq, sw, M, N, K, kbits, y, acc, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -264,16 +221,21 @@ int gemm_config_count() { return kNumCfgs; }
 
 GemmConfig gemm_config(int index) { return GemmConfig{kCfgs[index].bm, kCfgs[index].bn, 1}; }
 
+// Estimated time of a configuration: tiles run in rounds of (CUs x slots);
+// each round costs slots x BM x BN x K / rate (the CU's throughput is shared
+// by the workgroups it holds).  The rates come from sweeps on MI355X; callers
+// that want the measured best use tabit_autotune_gemm.
 int gemm_config_choose(int M, int N, int K, int num_cus) {
   (void)K;
   if (num_cus <= 0) num_cus = 256;
   int best = 0;
   double best_cost = 1e300;
   for (int i = 0; i < kNumCfgs; ++i) {
-    const long long tiles = (long long)((M + kCfgs[i].bm - 1) / kCfgs[i].bm) *
-                            ((N + kCfgs[i].bn - 1) / kCfgs[i].bn);
-    const long long per_cu = (tiles + num_cus - 1) / num_cus;
-    const double cost = (double)per_cu * kCfgs[i].bm * kCfgs[i].bn / kCfgs[i].eff;
+    const CfgDesc& c = kCfgs[i];
+    const long long tiles = (long long)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+    const long long per_round = (long long)num_cus * c.slots;
+    const long long rounds = (tiles + per_round - 1) / per_round;
+    const double cost = (double)rounds * c.slots * c.bm * c.bn / c.rate;
     if (cost < best_cost * 0.999) {
       best_cost = cost;
       best = i;
@@ -285,13 +247,14 @@ int gemm_config_choose(int M, int N, int K, int num_cus) {
 hipError_t launch_gemm_i8(int cfg, bool bitserial, const int8_t* xq, const float* sa,
                           const int8_t* wq, const float* sw, int M, int N, int K, int kbits,
                           uint16_t* y, int32_t* acc, hipStream_t stream) {
+#define TABIT_CASE(I, BM, BN, WM, WN, RB, NST, SLOTS, RATE) \
+  case I:                                            \
+    return launch_cfg<BM, BN, WM, WN, RB, NST>(bitserial, xq, sa, wq, sw, M, N, K, kbits, y, acc, stream);
   switch (cfg) {
-    case 0: return launch_cfg<256, 256>(bitserial, xq, sa, wq, sw, M, N, K, kbits, y, acc, stream);
-    case 1: return launch_cfg<256, 128>(bitserial, xq, sa, wq, sw, M, N, K, kbits, y, acc, stream);
-    case 2: return launch_cfg<128, 128>(bitserial, xq, sa, wq, sw, M, N, K, kbits, y, acc, stream);
-    case 3: return launch_cfg<128, 64>(bitserial, xq, sa, wq, sw, M, N, K, kbits, y, acc, stream);
-    default: return launch_cfg<64, 64>(bitserial, xq, sa, wq, sw, M, N, K, kbits, y, acc, stream);
+    TABIT_I8_CONFIGS(TABIT_CASE)
+    default: return hipErrorInvalidValue;
   }
+#undef TABIT_CASE
 }
 
 }  // namespace tabit

@@ -6,7 +6,9 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <map>
 #include <string>
+#include <tuple>
 #include <vector>
 
 namespace tabit {
@@ -56,4 +58,11 @@ struct tabit_ctx {
   std::vector<uint8_t> fmt;
   int force_gemm_cfg = -1;
   int force_mx_cfg = -1;
+  // autotuned tile configuration per (path, M, N, K); path 2 = MXFP4
+  std::map<std::tuple<int, int, int, int>, int> tuned;
+
+  int tuned_cfg(int path, int M, int N, int K) const {
+    auto it = tuned.find(std::make_tuple(path, M, N, K));
+    return it == tuned.end() ? -1 : it->second;
+  }
 };
