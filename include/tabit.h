@@ -259,6 +259,9 @@ int tabit_set_option(tabit_ctx* ctx, int option, int value);
  * index < 0.  Makes no HIP call. */
 int tabit_gemm_config_info(int index, int* bm, int* bn, int* split_k);
 
+/* As tabit_gemm_config_info, for the MXFP4 GEMM's tile configurations. */
+int tabit_mxfp4_config_info(int index, int* bm, int* bn);
+
 /* The configuration the automatic choice would take for (M, N, K) on a device
  * with num_cus compute units (num_cus <= 0: 256).  Makes no HIP call. */
 int tabit_gemm_config_choose(int M, int N, int K, int num_cus);

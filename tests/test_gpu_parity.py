@@ -180,19 +180,21 @@ def _check_mx(y_gpu, acc_gpu, xf, xe, wf, we, scale):
         assert np.all(err <= 1e-2 * np.abs(y_ref) + 1e-3 * np.abs(y_ref).max() + 1e-30)
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2])
-@pytest.mark.parametrize("M,N,K", [(1, 32, 32), (17, 96, 96), (300, 416, 2240), (129, 64, 1920)])
-def test_mxfp4_gemm(ctx, cfg, M, N, K):
+@pytest.mark.parametrize("M,N,K", [(1, 32, 32), (17, 96, 96), (300, 416, 2240), (129, 64, 1920),
+                                   (520, 288, 544)])
+def test_mxfp4_gemm(ctx, M, N, K):
+    """Every MXFP4 tile configuration against the exact fp64 product."""
     rng = np.random.default_rng(M * N + K)
     xf = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
     wf = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
     xe = rng.integers(118, 136, size=(M, K // 32), dtype=np.uint8)
     we = rng.integers(118, 136, size=(N, K // 32), dtype=np.uint8)
     d = [torch.from_numpy(a).to(DEV) for a in (xf, xe, wf, we)]
-    ctx.set_option(T.OPT_MXFP4_CONFIG, cfg)
     try:
-        y, acc = ctx.mxfp4_qgemm(*d, 1 / 32, want_acc=True)
-        _check_mx(_bf16_np(y), _np(acc).astype(np.float64), xf, xe, wf, we, 1 / 32)
+        for cfg in range(T.mxfp4_config_info()):
+            ctx.set_option(T.OPT_MXFP4_CONFIG, cfg)
+            y, acc = ctx.mxfp4_qgemm(*d, 1 / 32, want_acc=True)
+            _check_mx(_bf16_np(y), _np(acc).astype(np.float64), xf, xe, wf, we, 1 / 32)
     finally:
         ctx.set_option(T.OPT_MXFP4_CONFIG, -1)
 

@@ -58,6 +58,7 @@ _SIGNATURES = {
     "tabit_set_option": (_c_int, [_c_void_p, _c_int, _c_int]),
     "tabit_gemm_config_info": (_c_int, [_c_int, _PINT, _PINT, _PINT]),
     "tabit_gemm_config_choose": (_c_int, [_c_int, _c_int, _c_int, _c_int]),
+    "tabit_mxfp4_config_info": (_c_int, [_c_int, _PINT, _PINT]),
 }
 
 
@@ -143,6 +144,18 @@ def gemm_config_info(index: int = -1):
     if st != OK:
         raise TabitError(st, "bad config index")
     return bm.value, bn.value, sk.value
+
+
+def mxfp4_config_info(index: int = -1):
+    """Number of MXFP4 GEMM configs (index < 0) or (bm, bn) of one."""
+    lib = load()
+    if index < 0:
+        return int(lib.tabit_mxfp4_config_info(-1, None, None))
+    bm, bn = ctypes.c_int(), ctypes.c_int()
+    st = lib.tabit_mxfp4_config_info(index, ctypes.byref(bm), ctypes.byref(bn))
+    if st != OK:
+        raise TabitError(st, "bad config index")
+    return bm.value, bn.value
 
 
 def gemm_config_choose(M: int, N: int, K: int, num_cus: int = 0) -> int:

@@ -485,6 +485,15 @@ int tabit_gemm_config_info(int index, int* bm, int* bn, int* split_k) {
   return TABIT_OK;
 }
 
+int tabit_mxfp4_config_info(int index, int* bm, int* bn) {
+  if (index < 0) return tabit::mx_config_count();
+  if (index >= tabit::mx_config_count() || bm == nullptr || bn == nullptr) return TABIT_EINVAL;
+  const tabit::GemmConfig c = tabit::mx_config(index);
+  *bm = c.bm;
+  *bn = c.bn;
+  return TABIT_OK;
+}
+
 int tabit_gemm_config_choose(int M, int N, int K, int num_cus) {
   return tabit::gemm_config_choose(M, N, K, num_cus);
 }

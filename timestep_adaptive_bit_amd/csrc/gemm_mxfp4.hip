@@ -8,169 +8,128 @@
 // replaced by OCP MXFP4, the 4-bit format gfx950's matrix cores consume
 // natively (32-element blocks, E8M0 scales applied inside the MFMA).
 //
-// v_mfma_scale_f32_16x16x128_f8f6f4 with both operands E2M1: lane l supplies
-// 16 bytes = 32 consecutive K elements of row (l % 16) -- exactly one MX block
-// -- and that block's E8M0 byte as its scale operand.  Tiling follows the INT8
-// GEMM: 2 x 2 waves, 128-byte (256-element) K stages, double-buffered LDS with
-// the same XOR swizzle; the stage's 8 scale bytes per row are staged next to
-// the data tile.
+// v_mfma_scale_f32_32x32x64_f8f6f4 with both operands E2M1: lane l supplies
+// 16 bytes = 32 consecutive K elements of row (l % 32) -- exactly one MX block
+// -- and that block's E8M0 byte as its scale operand.  The tile skeleton is
+// the INT8 GEMM's: packed operand stages of 128 bytes (256 elements) copied
+// global->LDS by buffer loads into a double-buffered ring, one barrier per
+// stage.  The 8 scale bytes per row and stage go through registers into a
+// small LDS table next to the data (their loads are issued before the stage's
+// copies so waiting for them never waits for the copies).
 #include "tabit_internal.h"
+#include "tile_common.h"
 
 namespace tabit {
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
+using tile::v4i;
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int BKB = 128;  // bytes of packed K per stage (256 elements)
+constexpr int RB = 128;   // packed bytes per row per stage (256 elements)
 constexpr int SPR = 8;    // scale bytes per row per stage
 
-__device__ __forceinline__ int lds_off(int r, int c) {
-  return r * BKB + ((c ^ ((r & 7) ^ ((r >> 3) & 1))) << 4);
-}
-
-__device__ __forceinline__ uint16_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-template <int GROUP_M>
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int G = tiles_m * tiles_n;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, j = bid >> 3;
-  const int q = G >> 3, rem = G & 7;
-  const int lin = xcd * q + min(xcd, rem) + j;
-  const int per_group = GROUP_M * tiles_n;
-  const int g = lin / per_group;
-  const int first_m = g * GROUP_M;
-  const int gsz = min(tiles_m - first_m, GROUP_M);
-  const int in_g = lin - g * per_group;
-  tm = first_m + in_g % gsz;
-  tn = in_g / gsz;
-}
-
-template <int BM, int BN>
-__global__ void __launch_bounds__(256)
+template <int BM, int BN, int WM, int WN>
+__global__ void __launch_bounds__(WM* WN * 64)
 gemm_mxfp4_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ AE,
                   const uint8_t* __restrict__ B, const uint8_t* __restrict__ BE, int M, int N,
                   int K, float out_scale, uint16_t* __restrict__ Y, float* __restrict__ ACC,
                   int tiles_m, int tiles_n) {
-  constexpr int NT = 256;
-  constexpr int WM = 2, WN = 2;
+  constexpr int NT = WM * WN * 64, NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int FM = WTM / 16, FN = WTN / 16;
-  constexpr int A_LD = BM * (BKB / 16) / NT;
-  constexpr int B_LD = BN * (BKB / 16) / NT;
-  constexpr int DATA = (BM + BN) * BKB;
-  constexpr int STAGE = DATA + (BM + BN) * SPR;
-  static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for 256 threads");
-  static_assert(2 * STAGE >= BM * BN * 2, "epilogue tile must fit in the LDS stages");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int KS = RB / 32;                     // 32-byte (64-element) K-steps per stage
+  constexpr int DATA = (BM + BN) * RB;
+  constexpr int SCL = (BM + BN) * SPR;
+  constexpr int SL = (SCL + NT - 1) / NT;         // scale bytes per thread per stage
+  static_assert(FM >= 1 && FN >= 1, "wave tile must hold whole 32x32 blocks");
+  static_assert(2 * DATA >= BM * BN * 2, "epilogue tile must fit in the LDS stages");
+  __shared__ __attribute__((aligned(1024))) int8_t smem[2 * DATA];
+  __shared__ uint8_t sscale[2][SCL];
 
   int tm, tn;
-  tile_coords<4>(tiles_m, tiles_n, tm, tn);
+  tile::tile_coords<4>(tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave / WN, wn = wave % WN;
-  const int KB = K >> 1;        // packed bytes per row
-  const int KS = K >> 5;        // scale bytes per row
+  const int KB = K >> 1, KSB = K >> 5;            // packed bytes and scale bytes per row
+  const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
+  const auto rsa = tile::make_rsrc(A, (unsigned)M * (unsigned)KB);
+  const auto rsb = tile::make_rsrc(B, (unsigned)N * (unsigned)KB);
 
-  v4i ra[A_LD], rb[B_LD];
-  uint8_t rsa[(BM * SPR + NT - 1) / NT], rsb[(BN * SPR + NT - 1) / NT];
-  constexpr int SA_LD = (BM * SPR + NT - 1) / NT, SB_LD = (BN * SPR + NT - 1) / NT;
-  auto gload = [&](int kt) {
-    const int kb0 = kt * BKB;
+  // scale byte q of the stage table: rows 0..BM-1 from AE, then BN rows from BE
+  uint8_t sreg[SL];
+  auto load_scales = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const int qd = i * NT + tid, r = qd >> 3, c = qd & 7;
-      const int gm = m0 + r, gk = kb0 + c * 16;
-      ra[i] = (gm < M && gk < KB) ? *reinterpret_cast<const v4i*>(A + (size_t)gm * KB + gk)
-                                  : v4i{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      const int qd = i * NT + tid, r = qd >> 3, c = qd & 7;
-      const int gn = n0 + r, gk = kb0 + c * 16;
-      rb[i] = (gn < N && gk < KB) ? *reinterpret_cast<const v4i*>(B + (size_t)gn * KB + gk)
-                                  : v4i{0, 0, 0, 0};
-    }
-    const int ks0 = kt * SPR;
-#pragma unroll
-    for (int i = 0; i < SA_LD; ++i) {
-      const int qd = i * NT + tid, r = qd / SPR, j = qd % SPR;
-      const int gm = m0 + r, gs = ks0 + j;
-      rsa[i] = (r < BM && gm < M && gs < KS) ? AE[(size_t)gm * KS + gs] : (uint8_t)127;
-    }
-#pragma unroll
-    for (int i = 0; i < SB_LD; ++i) {
-      const int qd = i * NT + tid, r = qd / SPR, j = qd % SPR;
-      const int gn = n0 + r, gs = ks0 + j;
-      rsb[i] = (r < BN && gn < N && gs < KS) ? BE[(size_t)gn * KS + gs] : (uint8_t)127;
+    for (int i = 0; i < SL; ++i) {
+      const int q = i * NT + tid;
+      const int r = q / SPR, j = q % SPR;
+      const int gs = kt * SPR + j;
+      uint8_t v = 127;
+      if (q < SCL && gs < KSB) {
+        if (r < BM) {
+          if (r < rows_a) v = AE[(size_t)(m0 + r) * KSB + gs];
+        } else if (r - BM < rows_b) {
+          v = BE[(size_t)(n0 + r - BM) * KSB + gs];
+        }
+      }
+      sreg[i] = v;
     }
   };
-  auto sstore = [&](int buf) {
-    uint8_t* sa = smem + buf * STAGE;
-    uint8_t* sb = sa + BM * BKB;
-    uint8_t* ssa = sa + DATA;
-    uint8_t* ssb = ssa + BM * SPR;
+  auto store_scales = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const int qd = i * NT + tid;
-      *reinterpret_cast<v4i*>(sa + lds_off(qd >> 3, qd & 7)) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      const int qd = i * NT + tid;
-      *reinterpret_cast<v4i*>(sb + lds_off(qd >> 3, qd & 7)) = rb[i];
-    }
-#pragma unroll
-    for (int i = 0; i < SA_LD; ++i) {
-      const int qd = i * NT + tid;
-      if (qd < BM * SPR) ssa[qd] = rsa[i];
-    }
-#pragma unroll
-    for (int i = 0; i < SB_LD; ++i) {
-      const int qd = i * NT + tid;
-      if (qd < BN * SPR) ssb[qd] = rsb[i];
+    for (int i = 0; i < SL; ++i) {
+      const int q = i * NT + tid;
+      if (q < SCL) sscale[buf][q] = sreg[i];
     }
   };
+  auto issue = [&](int kt) {
+    int8_t* dst = smem + (kt & 1) * DATA;
+    tile::dma_stage<BM, NW, RB>(rsa, dst, m0, rows_a, KB, kt * RB, wave, lane);
+    tile::dma_stage<BN, NW, RB>(rsb, dst + BM * RB, n0, rows_b, KB, kt * RB, wave, lane);
+  };
 
-  v4f acc[FM][FN];
+  v16f acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FN; ++j) acc[i][j] = v16f{};
 
-  const int nk = (KB + BKB - 1) / BKB;
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  const int ra0 = wm * WTM + (lane & 31), rb0 = wn * WTN + (lane & 31);
+  const int khalf = lane >> 5;
+  const int nk = (KB + RB - 1) / RB;
+
+  load_scales(0);
+  issue(0);
+  store_scales(0);
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const uint8_t* sa = smem + cur * STAGE;
-    const uint8_t* sb = sa + BM * BKB;
-    const uint8_t* ssa = sa + DATA;
+    tile::wait_vmcnt0();
+    __syncthreads();
+    const bool more = kt + 1 < nk;
+    if (more) {
+      load_scales(kt + 1);     // before the copies: waiting on these never waits on the copies
+      issue(kt + 1);
+    }
+    const int8_t* sa = smem + (kt & 1) * DATA;
+    const int8_t* sb = sa + BM * RB;
+    const uint8_t* ssa = sscale[kt & 1];
     const uint8_t* ssb = ssa + BM * SPR;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int c = kk * 4 + (lane >> 4);
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c = ks * 2 + khalf;     // 16-byte chunk = one 32-element MX block
       v4i a[FM], b[FN];
       int ea[FM], eb[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const int r = wm * WTM + i * 16 + (lane & 15);
-        a[i] = *reinterpret_cast<const v4i*>(sa + lds_off(r, c));
+        const int r = ra0 + i * 32;
+        a[i] = *reinterpret_cast<const v4i*>(sa + tile::lds_off<RB>(r, c));
         ea[i] = ssa[r * SPR + c];
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int r = wn * WTN + j * 16 + (lane & 15);
-        b[j] = *reinterpret_cast<const v4i*>(sb + lds_off(r, c));
+        const int r = rb0 + j * 32;
+        b[j] = *reinterpret_cast<const v4i*>(sb + tile::lds_off<RB>(r, c));
         eb[j] = ssb[r * SPR + c];
       }
 #pragma unroll
@@ -179,72 +138,59 @@ gemm_mxfp4_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ AE,
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const v8i b8 = {b[j][0], b[j][1], b[j][2], b[j][3], 0, 0, 0, 0};
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[i][j], 4, 4, 0,
-                                                                        ea[i], 0, eb[j]);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc[i][j], 4, 4, 0,
+                                                                       ea[i], 0, eb[j]);
         }
       }
     }
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
+    if (more) store_scales((kt + 1) & 1);
   }
 
-  const int row_base = m0 + wm * WTM + 4 * (lane >> 4);
-  const int col_base = n0 + wn * WTN + (lane & 15);
+  const int row_w = m0 + wm * WTM, col_w = n0 + wn * WTN;
   if (ACC != nullptr) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int gm = row_base + i * 16 + r, gn = col_base + j * 16;
+        for (int r = 0; r < 16; ++r) {
+          const int gm = row_w + i * 32 + (r >> 2) * 8 + khalf * 4 + (r & 3);
+          const int gn = col_w + j * 32 + (lane & 31);
           if (gm < M && gn < N) ACC[(size_t)gm * N + gn] = acc[i][j][r];
         }
   }
   if (Y != nullptr) {
-    constexpr int CH = WTN / 8;
+    __syncthreads();  // every wave is done reading the last stage
     uint16_t* st = reinterpret_cast<uint16_t*>(smem) + wave * WTM * WTN;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int lr = i * 16 + 4 * (lane >> 4) + r;
-          const int lc = j * 16 + (lane & 15);
-          const int ch = (lc >> 3) ^ (lr & (CH - 1));
-          st[lr * WTN + ch * 8 + (lc & 7)] = bf16_rne(acc[i][j][r] * out_scale);
-        }
-    __syncthreads();
-#pragma unroll
-    for (int it = 0; it < WTM * CH / 64; ++it) {
-      const int idx = it * 64 + lane;
-      const int lr = idx / CH, ch = idx % CH;
-      const int gm = m0 + wm * WTM + lr, gn = n0 + wn * WTN + ch * 8;
-      const uint4 v = *reinterpret_cast<const uint4*>(st + lr * WTN + ((ch ^ (lr & (CH - 1))) * 8));
-      if (gm < M && gn < N) *reinterpret_cast<uint4*>(Y + (size_t)gm * N + gn) = v;
-    }
+    tile::store_tile32_bf16<WTM, WTN>(st, lane, Y, row_w, col_w, M, N, [&](int i, int j, int r) {
+      return tile::bf16_rne(acc[i][j][r] * out_scale);
+    });
   }
 }
 
 struct CfgDesc {
-  int bm, bn;
-  float eff;
+  int bm, bn, wm, wn;
+  int slots;
+  float rate;
 };
-constexpr CfgDesc kCfgs[] = {
-    {256, 256, 1.00f},
-    {128, 128, 0.85f},
-    {64, 64, 0.50f},
-};
+// index, BM, BN, WM, WN, slots per CU, rate
+#define TABIT_MX_CONFIGS(X)          \
+  X(0, 256, 128, 2, 2, 1, 1.00f)     \
+  X(1, 128, 128, 2, 2, 2, 0.95f)     \
+  X(2, 128, 64, 2, 2, 3, 0.75f)      \
+  X(3, 64, 64, 2, 2, 4, 0.55f)
+#define TABIT_DESC(I, BM, BN, WM, WN, SLOTS, RATE) {BM, BN, WM, WN, SLOTS, RATE},
+constexpr CfgDesc kCfgs[] = {TABIT_MX_CONFIGS(TABIT_DESC)};
+#undef TABIT_DESC
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
-template <int BM, int BN>
+template <int BM, int BN, int WM, int WN>
 hipError_t launch_cfg(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq, const uint8_t* we,
                       int M, int N, int K, float out_scale, uint16_t* y, float* acc,
                       hipStream_t s) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  gemm_mxfp4_kernel<BM, BN><<<tiles_m * tiles_n, 256, 0, s>>>(xq, xe, wq, we, M, N, K, out_scale,
-                                                              y, acc, tiles_m, tiles_n);
+  gemm_mxfp4_kernel<BM, BN, WM, WN><<<tiles_m * tiles_n, WM * WN * 64, 0, s>>>(
+      xq, xe, wq, we, M, N, K, out_scale, y, acc, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -260,10 +206,11 @@ int mx_config_choose(int M, int N, int K, int num_cus) {
   int best = 0;
   double best_cost = 1e300;
   for (int i = 0; i < kNumCfgs; ++i) {
-    const long long tiles = (long long)((M + kCfgs[i].bm - 1) / kCfgs[i].bm) *
-                            ((N + kCfgs[i].bn - 1) / kCfgs[i].bn);
-    const long long per_cu = (tiles + num_cus - 1) / num_cus;
-    const double cost = (double)per_cu * kCfgs[i].bm * kCfgs[i].bn / kCfgs[i].eff;
+    const CfgDesc& c = kCfgs[i];
+    const long long tiles = (long long)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+    const long long per_round = (long long)num_cus * c.slots;
+    const long long rounds = (tiles + per_round - 1) / per_round;
+    const double cost = (double)rounds * c.slots * c.bm * c.bn / c.rate;
     if (cost < best_cost * 0.999) {
       best_cost = cost;
       best = i;
@@ -275,11 +222,14 @@ int mx_config_choose(int M, int N, int K, int num_cus) {
 hipError_t launch_gemm_mxfp4(int cfg, const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
                              const uint8_t* we, int M, int N, int K, float out_scale, uint16_t* y,
                              float* acc, hipStream_t stream) {
+#define TABIT_CASE(I, BM, BN, WM, WN, SLOTS, RATE) \
+  case I:                                           \
+    return launch_cfg<BM, BN, WM, WN>(xq, xe, wq, we, M, N, K, out_scale, y, acc, stream);
   switch (cfg) {
-    case 0: return launch_cfg<256, 256>(xq, xe, wq, we, M, N, K, out_scale, y, acc, stream);
-    case 1: return launch_cfg<128, 128>(xq, xe, wq, we, M, N, K, out_scale, y, acc, stream);
-    default: return launch_cfg<64, 64>(xq, xe, wq, we, M, N, K, out_scale, y, acc, stream);
+    TABIT_MX_CONFIGS(TABIT_CASE)
+    default: return hipErrorInvalidValue;
   }
+#undef TABIT_CASE
 }
 
 }  // namespace tabit

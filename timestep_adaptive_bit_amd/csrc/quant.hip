@@ -14,7 +14,7 @@
 //
 // Data layout: the workgroup's rows are contiguous in memory, so the
 // workgroup sees them as one flat run of 16-element chunks; chunk c of the run
-// lives in thread (c mod 256), register slot (c / 256).  Loads and stores are
+// lives in thread (c mod NT), register slot (c / NT) for NT threads per workgroup.  Loads and stores are
 // 16-byte, fully coalesced.  A Hadamard block of b elements spans b/16
 // consecutive, aligned lanes, so the cross-lane FWHT stages are lane-XOR
 // exchanges (DPP within a quad, ds_swizzle beyond).
@@ -23,7 +23,7 @@
 namespace tabit {
 namespace {
 
-constexpr int QT = 256;  // threads per workgroup
+constexpr int QT = 256;  // threads per workgroup of the MX quantizer
 
 template <int MASK>
 __device__ __forceinline__ float lane_xor(float v) {
@@ -101,12 +101,12 @@ __device__ __forceinline__ int row_of(int c, int cr, float inv_cr) {
   return r;
 }
 
-template <int B, int CPT>
-__global__ void __launch_bounds__(QT)
+template <int B, int NT, int CPT>
+__global__ void __launch_bounds__(NT)
 quant_int8_kernel(const uint16_t* __restrict__ x, int M, int K, int rows_per_wg, float scale_div,
                   int8_t* __restrict__ q, float* __restrict__ scale) {
-  __shared__ unsigned s_amax[QT * CPT / 2];
-  __shared__ float s_r[QT * CPT / 2];
+  __shared__ unsigned s_amax[NT * CPT / 2];
+  __shared__ float s_r[NT * CPT / 2];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int r0 = blockIdx.x * rows_per_wg;
@@ -119,7 +119,7 @@ quant_int8_kernel(const uint16_t* __restrict__ x, int M, int K, int rows_per_wg,
   float v[CPT][16];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int c = i * QT + tid;
+    const int c = i * NT + tid;
     if (c < nchunks) {
       load_chunk(x + base + (size_t)c * 16, v[i]);
     } else {
@@ -127,14 +127,14 @@ quant_int8_kernel(const uint16_t* __restrict__ x, int M, int K, int rows_per_wg,
       for (int e = 0; e < 16; ++e) v[i][e] = 0.0f;
     }
   }
-  for (int t = tid; t < rows; t += QT) s_amax[t] = 0u;
+  for (int t = tid; t < rows; t += NT) s_amax[t] = 0u;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) fwht_chunk<B>(v[i], lane);
   __syncthreads();
 
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int c = i * QT + tid;
+    const int c = i * NT + tid;
     if (c < nchunks) {
       float m = 0.0f;
 #pragma unroll
@@ -144,7 +144,7 @@ quant_int8_kernel(const uint16_t* __restrict__ x, int M, int K, int rows_per_wg,
     }
   }
   __syncthreads();
-  for (int t = tid; t < rows; t += QT) {
+  for (int t = tid; t < rows; t += NT) {
     const float a = __uint_as_float(s_amax[t]);
     s_r[t] = a > 0.0f ? 127.0f / a : 0.0f;
     scale[r0 + t] = (a / 127.0f) / scale_div;
@@ -153,7 +153,7 @@ quant_int8_kernel(const uint16_t* __restrict__ x, int M, int K, int rows_per_wg,
 
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int c = i * QT + tid;
+    const int c = i * NT + tid;
     if (c < nchunks) {
       const float r = s_r[row_of(c, cr, inv_cr)];
       uint4 o;
@@ -223,15 +223,17 @@ quant_mx_kernel(const uint16_t* __restrict__ x, long long nchunks, uint8_t* __re
 }
 
 template <int B>
-hipError_t dispatch_int8_cpt(int cpt, int grid, int rows, const uint16_t* x, int M, int K,
-                             float scale_div, int8_t* q, float* scale, hipStream_t s) {
-  switch (cpt) {
-    case 1: quant_int8_kernel<B, 1><<<grid, QT, 0, s>>>(x, M, K, rows, scale_div, q, scale); break;
-    case 2: quant_int8_kernel<B, 2><<<grid, QT, 0, s>>>(x, M, K, rows, scale_div, q, scale); break;
-    case 4: quant_int8_kernel<B, 4><<<grid, QT, 0, s>>>(x, M, K, rows, scale_div, q, scale); break;
-    default: quant_int8_kernel<B, 8><<<grid, QT, 0, s>>>(x, M, K, rows, scale_div, q, scale); break;
+hipError_t dispatch_int8(int nt, int cpt, int grid, int rows, const uint16_t* x, int M, int K,
+                         float scale_div, int8_t* q, float* scale, hipStream_t s) {
+#define TABIT_Q(NT_, CPT_)                                                                   \
+  if (nt == NT_ && cpt == CPT_) {                                                            \
+    quant_int8_kernel<B, NT_, CPT_><<<grid, NT_, 0, s>>>(x, M, K, rows, scale_div, q, scale); \
+    return hipGetLastError();                                                                \
   }
-  return hipGetLastError();
+  TABIT_Q(256, 1) TABIT_Q(256, 2) TABIT_Q(256, 4) TABIT_Q(512, 2) TABIT_Q(512, 4)
+  TABIT_Q(1024, 2)
+#undef TABIT_Q
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -240,31 +242,34 @@ hipError_t launch_quant_int8(const uint16_t* x, int M, int K, int had_block, flo
                              int8_t* q, float* scale, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
   const int cr = K / 16;
-  // Chunks per thread: the smallest of 1, 2, 4, 8 that keeps >= 90% of the
-  // workgroup's slots busy with whole rows; otherwise the best utilization.
-  int best_cpt = 8;
+  // Workgroup shape (threads x chunks per thread): the smallest that keeps >= 90%
+  // of its 16-element slots busy with whole rows, otherwise the best utilization.
+  // At most 4 chunks (64 fp32 values) per thread keeps occupancy for latency hiding.
+  static const int kShapes[][2] = {{256, 1}, {256, 2}, {256, 4}, {512, 2}, {512, 4}, {1024, 2}};
+  int nt = 1024, cpt = 2;
   double best_util = -1.0;
-  for (int cpt : {1, 2, 4, 8}) {
-    const int slots = QT * cpt;
+  for (const auto& sh : kShapes) {
+    const int slots = sh[0] * sh[1];
     if (slots < cr) continue;
-    const int rows = slots / cr;
-    const double util = (double)(rows * cr) / slots;
+    const double util = (double)((slots / cr) * cr) / slots;
     if (util >= 0.9) {
-      best_cpt = cpt;
+      nt = sh[0];
+      cpt = sh[1];
       break;
     }
     if (util > best_util) {
       best_util = util;
-      best_cpt = cpt;
+      nt = sh[0];
+      cpt = sh[1];
     }
   }
-  const int rows = (QT * best_cpt) / cr;
+  const int rows = (nt * cpt) / cr;
   const int grid = (M + rows - 1) / rows;
   switch (had_block) {
-    case 0: return dispatch_int8_cpt<0>(best_cpt, grid, rows, x, M, K, scale_div, q, scale, stream);
-    case 32: return dispatch_int8_cpt<32>(best_cpt, grid, rows, x, M, K, scale_div, q, scale, stream);
-    case 64: return dispatch_int8_cpt<64>(best_cpt, grid, rows, x, M, K, scale_div, q, scale, stream);
-    default: return dispatch_int8_cpt<128>(best_cpt, grid, rows, x, M, K, scale_div, q, scale, stream);
+    case 0: return dispatch_int8<0>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream);
+    case 32: return dispatch_int8<32>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream);
+    case 64: return dispatch_int8<64>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream);
+    default: return dispatch_int8<128>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream);
   }
 }
 
