@@ -20,6 +20,8 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -34,6 +36,113 @@ if ROOT not in sys.path:
 INT8_PEAK_TOPS = 5000.0     # MI355X dense INT8 MFMA (5.0 POPS)
 MXFP4_PEAK_TOPS = 10100.0   # MI355X dense MXFP4 (10.1 PFLOP/s)
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_i8_traffic.json")
+GEMM_SOURCES = [os.path.join(ROOT, "timestep_adaptive_bit_amd", "csrc", f)
+                for f in ("gemm_i8.hip", "tile_common.h")]
+
+
+def gemm_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, path: str):
+    """HBM bytes per GEMM launch from committed rocprofv3 counters, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != gemm_source_hash():
+        return None       # the kernel changed since the counters were taken
+    if rec.get("workload") != workload or rec.get("path") != path:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def summarize_rocpd(root: str) -> None:
+    """Print kernel durations and counter means from rocprofv3 SQLite output under root."""
+    import collections
+    import re
+    import sqlite3
+    dbs = sorted(glob.glob(os.path.join(root, "**", "*.db"), recursive=True))
+    dur = collections.defaultdict(list)
+    pmc = collections.defaultdict(list)
+
+    def short(name):
+        name = name.replace("void ", "").replace("tabit::(anonymous namespace)::", "")
+        return re.sub(r"\(.*$", "", name)[:80]
+    for db in dbs:
+        c = sqlite3.connect(db)
+        tabs = {r[0] for r in c.execute("select name from sqlite_master")}
+        if "kernels" in tabs:
+            for name, d in c.execute("select name, duration from kernels"):
+                dur[short(name)].append(d / 1e3)
+        if "counters_collection" in tabs:
+            for name, cn, v in c.execute("select kernel_name, counter_name, value from counters_collection"):
+                pmc[(short(name), cn)].append(v)
+    if dur:
+        tot = sum(sum(v) for v in dur.values())
+        print(f"{'kernel':82s} {'calls':>7s} {'avg_us':>9s} {'total_ms':>9s} {'pct':>6s}")
+        for k, v in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
+            print(f"{k:82s} {len(v):7d} {sum(v)/len(v):9.2f} {sum(v)/1e3:9.2f} {100*sum(v)/tot:6.1f}")
+    if pmc:
+        print(f"{'kernel':82s} {'counter':28s} {'dispatches':>10s} {'mean_per_dispatch':>18s}")
+        for (k, cn), v in sorted(pmc.items()):
+            print(f"{k:82s} {cn:28s} {len(v):10d} {sum(v)/len(v):18.6g}")
+
+
+def _pmc_values(root: str, counter: str, name_part: str):
+    """Per-dispatch values of `counter` for kernels whose name contains name_part, in dispatch order."""
+    import sqlite3
+    vals = []
+    for db in sorted(glob.glob(os.path.join(root, "**", "*.db"), recursive=True)):
+        c = sqlite3.connect(db)
+        q = ("select dispatch_id, value from counters_collection where counter_name = ? "
+             "and kernel_name like ? order by dispatch_id")
+        vals += [v for _, v in c.execute(q, (counter, f"%{name_part}%"))]
+    return vals
+
+
+def record_traffic(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_bytes, n_last,
+                   workload, path):
+    """HBM bytes per GEMM launch: FETCH_SIZE + WRITE_SIZE (KiB per dispatch) of the last
+    n_last gemm_i8 dispatches, each scaled by the same counter's reading for a plain copy
+    of cal_bytes bytes."""
+    cf = _pmc_values(cal_fetch_dir, "FETCH_SIZE", "")
+    cw = _pmc_values(cal_write_dir, "WRITE_SIZE", "")
+    # the copy dispatches are the largest readings in the calibration run
+    cf_kib, cw_kib = max(cf), max(cw)
+    f_factor = cf_kib * 1024.0 / cal_bytes
+    w_factor = cw_kib * 1024.0 / cal_bytes
+    gf = _pmc_values(fetch_dir, "FETCH_SIZE", "gemm_i8")[-n_last:]
+    gw = _pmc_values(write_dir, "WRITE_SIZE", "gemm_i8")[-n_last:]
+    fetch = sum(gf) / len(gf) * 1024.0 / f_factor
+    write = sum(gw) / len(gw) * 1024.0 / w_factor
+    rec = {"source_hash": gemm_source_hash(), "workload": workload, "path": path,
+           "dispatches": len(gf), "copy_calibration_bytes": cal_bytes,
+           "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
+           "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
+           "traffic_bytes_per_launch": round(fetch + write)}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+def copy_calibration(mib: int) -> None:
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
 
 
 class Hip:
@@ -45,6 +154,11 @@ class Hip:
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def record(self, ev, stream) -> None:
+        if self.lib.hipEventRecord(ev, ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def events(self, n: int):
         arr = (ctypes.c_void_p * n)()
@@ -108,6 +222,54 @@ def cpu_baseline(wl, rows: int):
     }
 
 
+def k_sweep(ctx, T, torch, wl, weights, xs, ys, b):
+    """Per distinct INT8 shape: GEMM time at every k, masked and bit-plane (HIP events)."""
+    res = {}
+    seen = set()
+    for li, layer in enumerate(wl.layers):
+        key = (layer.M, layer.N, layer.K)
+        if key in seen or not (wl.fmt[:, li] == 0).any():
+            continue
+        seen.add(key)
+        xq, sa = ctx.hadamard_quant_act(xs[(0, layer.M, layer.K)], b, T.FMT_INT8)
+        wq, sw = weights[li]["w_q"], weights[li]["w_scale"]
+        ctx.autotune_gemm(T.PATH_BITSERIAL, xq, sa, wq, sw, *key, 0, ys[li], reps=2)
+        row = {}
+        for name, fn in (("masked", ctx.masked_qgemm), ("bitserial", ctx.qgemm_bitserial)):
+            times = []
+            for k in range(8):
+                for _ in range(2):
+                    fn(xq, sa, wq, sw, k, y=ys[li])
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(5):
+                    fn(xq, sa, wq, sw, k, y=ys[li])
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(round(e0.elapsed_time(e1) * 1e3 / 5, 2))
+            row[name] = times
+        res["x".join(map(str, key))] = row
+    return res
+
+
+def gemm_tiles(T, wl, tuned):
+    """Tile shape (BM, BN) each distinct GEMM shape runs with."""
+    out = {}
+    for li, layer in enumerate(wl.layers):
+        for fmt in sorted(set(int(f) for f in wl.fmt[:, li])):
+            key = (fmt, layer.M, layer.N, layer.K)
+            name = f"{'mxfp4' if fmt else 'int8'} {layer.M}x{layer.N}x{layer.K}"
+            if name in out:
+                continue
+            if fmt == 0:
+                cfg = tuned.get(key, T.gemm_config_choose(layer.M, layer.N, layer.K))
+                out[name] = list(T.gemm_config_info(cfg)[:2])
+            else:
+                out[name] = "tuned" if key in tuned else "auto"
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,10 +279,36 @@ def main() -> int:
     ap.add_argument("--path", default="masked", choices=["masked", "bitserial"])
     ap.add_argument("--had-block", type=int, default=None, help="override the workload's block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--cpu-rows", type=int, default=2048, help="token rows per shape in the oracle sample")
     ap.add_argument("--no-events", action="store_true", help="skip per-GEMM event timing")
-    ap.add_argument("--no-tune", action="store_true", help="skip the warm-up tile autotuning")
+    ap.add_argument("--tune", action="store_true",
+                    help="autotune the GEMM tiles per shape during warm-up (default: the library's "
+                         "calibrated choice, which keeps counter runs on the same kernels)")
+    ap.add_argument("--shared-x", action="store_true",
+                    help="reuse step 0's activations at every step (same work, faster set-up)")
+    ap.add_argument("--k-sweep", action="store_true",
+                    help="also time each distinct INT8 shape at every k (masked and bit-plane)")
+    ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--summarize", metavar="DIR", default=None,
+                    help="only print a summary of rocprofv3 output under DIR")
+    ap.add_argument("--record-traffic", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR",
+                                                          "CAL_WRITE_DIR", "N_LAST"), default=None,
+                    help="only turn counter runs into the per-launch GEMM traffic record")
+    ap.add_argument("--copy-mib", type=int, default=256, help="size of the calibration copy")
     args = ap.parse_args()
+    if args.record_traffic:
+        fd, wd, cfd, cwd, n = args.record_traffic
+        import tabit_synth as S
+        record_traffic(fd, wd, cfd, cwd, args.copy_mib << 20, int(n),
+                       S.WORKLOADS[args.workload]().name, args.path)
+        return 0
+    if args.summarize:
+        summarize_rocpd(args.summarize)
+        return 0
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return 0
 
     if args.gpus != 1:
         print("bench.py measures one GPU: the linear shards by tokens with no communication, "
@@ -156,7 +344,11 @@ def main() -> int:
         for layer in wl.layers:
             key = (t, layer.M, layer.K)
             if key not in xs:
-                xs[key] = S.gen_activation(layer.M, layer.K, seed=S.activation_seed(t, layer.K)).to(dev)
+                if args.shared_x and t > 0:
+                    xs[key] = xs[(0, layer.M, layer.K)]
+                else:
+                    xs[key] = S.gen_activation(layer.M, layer.K,
+                                               seed=S.activation_seed(t, layer.K)).to(dev)
     ys = [torch.empty((l.M, l.N), dtype=torch.bfloat16, device=dev) for l in wl.layers]
     ws_bytes = max(T.act_workspace_bytes(l.M, l.K) for l in wl.layers)
     act_ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -176,7 +368,7 @@ def main() -> int:
 
     # ---- warm-up tuning: time every tile configuration once per distinct GEMM shape
     tuned = {}
-    if not args.no_tune:
+    if args.tune:
         for li, layer in enumerate(wl.layers):
             for fmt in sorted(set(int(f) for f in wl.fmt[:, li])):
                 key = (fmt, layer.M, layer.N, layer.K)
@@ -207,18 +399,37 @@ def main() -> int:
         one_pass()
     torch.cuda.synchronize()
 
-    ev_sets = [] if args.no_events else [hip.events(2 * Tn * L) for _ in range(args.steps)]
+    # ---- timed region: K schedule passes, nothing else on the stream
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        one_pass(None if args.no_events else ev_sets[s])
+    for _ in range(args.steps):
+        one_pass()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
+    # ---- instrumented region: the same K passes with HIP events recorded on the
+    # launch stream around every GEMM (events cost a few us each, so they are
+    # kept out of the region that gives `value`)
+    ev_sets = [] if args.no_events else [hip.events(2 * Tn * L) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s_ in range(len(ev_sets)):
+        one_pass(ev_sets[s_])
+    torch.cuda.synchronize()
+    # the cost of an event pair with nothing between them, on the same stream
+    ev_overhead_ms = 0.0
+    if not args.no_events:
+        pairs = hip.events(400)
+        for i in range(200):
+            hip.record(pairs[2 * i], stream)
+            hip.record(pairs[2 * i + 1], stream)
+        torch.cuda.synchronize()
+        empty = sorted(hip.elapsed_ms(pairs[2 * i], pairs[2 * i + 1]) for i in range(200))
+        ev_overhead_ms = empty[len(empty) // 2]
+        hip.destroy(pairs)
+
     # ---- work accounting
     int8_ops = mx_ops = 0
-    gemm_bytes = 0
     for t in range(Tn):
         for li, layer in enumerate(wl.layers):
             ops = 2 * layer.M * layer.N * layer.K
@@ -239,7 +450,7 @@ def main() -> int:
             for t in range(Tn):
                 for li in range(L):
                     i = t * L + li
-                    ms = hip.elapsed_ms(ev[2 * i], ev[2 * i + 1])
+                    ms = max(hip.elapsed_ms(ev[2 * i], ev[2 * i + 1]) - ev_overhead_ms, 0.0)
                     if wl.fmt[t, li] == 0:
                         gemm_ms_i8 += ms
                         n_i8 += 1
@@ -251,10 +462,12 @@ def main() -> int:
         if n_i8:
             achieved = (int8_ops * args.steps) / (gemm_ms_i8 / 1e3) / 1e12
             roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS,
-                        "unit": "TOPS", "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": None,
+                        "unit": "TOPS", "frac": round(achieved / INT8_PEAK_TOPS, 4),
+                        "traffic": recorded_traffic(wl.name, args.path),
                         "kernel": "gemm_i8_kernel (masked)" if path == T.PATH_MASKED
                         else "gemm_i8_kernel (bitserial)",
-                        "avg_launch_us": round(gemm_ms_i8 * 1e3 / n_i8, 3)}
+                        "avg_launch_us": round(gemm_ms_i8 * 1e3 / n_i8, 3),
+                        "event_pair_overhead_us": round(ev_overhead_ms * 1e3, 3)}
             detail["gemm_int8_ms_per_step"] = round(gemm_ms_i8 / args.steps, 3)
         if n_mx:
             mx_tops = (mx_ops * args.steps) / (gemm_ms_mx / 1e3) / 1e12
@@ -266,6 +479,12 @@ def main() -> int:
                             "unit": "TFLOP/s", "frac": round(mx_tops / MXFP4_PEAK_TOPS, 4),
                             "traffic": None, "kernel": "gemm_mxfp4_kernel",
                             "avg_launch_us": round(gemm_ms_mx * 1e3 / n_mx, 3)}
+
+    if int8_ops > 0 and not args.no_events:
+        detail["quantizer_and_gaps_ms_per_step"] = round(ms_per_step - detail["gemm_int8_ms_per_step"]
+                                                         - detail.get("gemm_mxfp4_ms_per_step", 0.0), 3)
+    if args.k_sweep:
+        detail["k_sweep_us"] = k_sweep(ctx, T, torch, wl, weights, xs, ys, b)
 
     out = {
         "metric": "masked W8A8 GEMM TOPS and % of INT8 MFMA peak per denoising schedule",
@@ -287,8 +506,7 @@ def main() -> int:
         "frac_of_int8_peak": round(value / INT8_PEAK_TOPS, 4),
         "roofline": roofline,
         "detail": detail,
-        "tuned_tiles": {f"{'mxfp4' if k[0] else 'int8'} {k[1]}x{k[2]}x{k[3]}": T.gemm_config_info(v)[:2]
-                        if k[0] == 0 else v for k, v in tuned.items()},
+        "gemm_tiles": gemm_tiles(T, wl, tuned),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows)

@@ -1,0 +1,110 @@
+"""Full-size parity on every workload's distinct linear shapes.
+
+Shapes, block sizes, formats and k values are the workloads' own (the
+configurations bench.py times), and the kernels run in the launch
+configuration bench.py uses (the library's automatic tile choice).
+Activation and weight codes and scales are compared with the oracle in full,
+bit-exact; GEMM outputs on a seeded sample of rows (first and last row
+included): int32 accumulators bit-exact, bf16 within 1e-2 relative, MXFP4
+outputs within the MXFP4 bound of test_gpu_parity.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import tabit_oracle as O
+import tabit_synth as S
+import timestep_adaptive_bit_amd as T
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+ROWS = 64
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    c = T.Context()
+    yield c
+    c.close()
+
+
+def _np(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _distinct(wl):
+    seen = {}
+    for li, layer in enumerate(wl.layers):
+        key = (layer.M, layer.N, layer.K)
+        if key not in seen:
+            fmts = sorted(set(int(f) for f in wl.fmt[:, li]))
+            kmax = int(wl.k_bits[:, li].max())
+            seen[key] = (li, fmts, kmax)
+    return seen
+
+
+def _sample_rows(M, seed):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(M, size=min(ROWS, M), replace=False).tolist()) | {0, M - 1}
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_workload_shapes(ctx, name):
+    wl = S.WORKLOADS[name]()
+    b = wl.had_block
+    for (M, N, K), (li, fmts, kmax) in _distinct(wl).items():
+        print(f"[{name}] {M}x{N}x{K} layer {li} fmts {fmts} k {kmax}", flush=True)
+        x = S.gen_activation(M, K, seed=S.activation_seed(0, K))
+        w = S.gen_weight(N, K, seed=li)
+        xb, wb = S.bf16_bits(x), S.bf16_bits(w)
+        dx = x.to(DEV)
+        wts = ctx.quantize_weights(w.to(DEV), b, int8=0 in fmts, mx=1 in fmts)
+        rows = _sample_rows(M, seed=M + N + K)
+        if 0 in fmts:
+            wq_ref, sw_ref = O.quantize_weights_int8(wb, b)
+            np.testing.assert_array_equal(_np(wts["w_q"]), wq_ref)
+            np.testing.assert_array_equal(_np(wts["w_scale"]).view(np.uint32), sw_ref.view(np.uint32))
+            xq, sa = ctx.hadamard_quant_act(dx, b)
+            xq_ref, sa_ref = O.quantize_act_int8(xb, b)
+            np.testing.assert_array_equal(_np(xq), xq_ref)
+            np.testing.assert_array_equal(_np(sa).view(np.uint32), sa_ref.view(np.uint32))
+            y, acc = ctx.masked_qgemm(xq, sa, wts["w_q"], wts["w_scale"], kmax, want_acc=True)
+            acc_ref = O.masked_gemm_i32(xq_ref[rows], wq_ref, kmax)
+            np.testing.assert_array_equal(_np(acc)[rows], acc_ref)
+            y_ref = O.dequant(acc_ref, sa_ref[rows], sw_ref)
+            yy = y.float().cpu().numpy().astype(np.float64)[rows]
+            assert np.all(np.abs(yy - y_ref) <= 1e-2 * np.abs(y_ref) + 1e-30)
+        if 1 in fmts:
+            wf_ref, we_ref = O.mx_quantize_rows(O.bf16_to_f32(wb), b)
+            np.testing.assert_array_equal(_np(wts["w_fp4"]), wf_ref)
+            np.testing.assert_array_equal(_np(wts["w_e8m0"]), we_ref)
+            xf, xe = ctx.hadamard_quant_act(dx, b, T.FMT_MXFP4)
+            xf_np, xe_np = _np(xf), _np(xe)
+            xf_ref, xe_ref = O.mx_quantize_rows(O.bf16_to_f32(xb[rows]), b)
+            np.testing.assert_array_equal(xf_np[rows], xf_ref)
+            np.testing.assert_array_equal(xe_np[rows], xe_ref)
+            y, _ = ctx.mxfp4_qgemm(xf, xe, wts["w_fp4"], wts["w_e8m0"], 1.0 / max(b, 1))
+            y_ref = O.mxfp4_gemm(xf_ref, xe_ref, wf_ref, we_ref, 1.0 / max(b, 1))
+            yy = y.float().cpu().numpy().astype(np.float64)[rows]
+            err = np.abs(yy - y_ref)
+            assert np.all(err <= 1e-2 * np.abs(y_ref) + 1e-3 * np.abs(y_ref).max() + 1e-30)
+        del dx, wts
+
+
+def test_c3_bitplane_every_k_sampled(ctx):
+    """The bit-plane path at the SANA-shaped sizes for every k, sampled rows bit-exact."""
+    wl = S.c3_sana()
+    for (M, N, K), (li, _, _) in _distinct(wl).items():
+        x = S.gen_activation(M, K, seed=S.activation_seed(0, K))
+        w = S.gen_weight(N, K, seed=li)
+        wts = ctx.quantize_weights(w.to(DEV), 0)
+        xq, sa = ctx.hadamard_quant_act(x.to(DEV), 0)
+        xq_np = _np(xq)
+        rows = _sample_rows(M, seed=li)
+        wq_np = _np(wts["w_q"])
+        for k in range(8):
+            _, acc = ctx.qgemm_bitserial(xq, sa, wts["w_q"], wts["w_scale"], k, want_y=False,
+                                         want_acc=True)
+            np.testing.assert_array_equal(_np(acc)[rows], O.bitplane_gemm_i32(xq_np[rows], wq_np, k))
