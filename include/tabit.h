@@ -219,9 +219,10 @@ typedef struct tabit_layer {
  *   x_bf16      host array [num_steps][num_layers] of device pointers to the
  *               layer inputs ([M][K] bf16 each).
  *   gemm_events NULL, or a host array of 2 * num_steps * num_layers hipEvent_t
- *               (passed as void*): events[2i] is recorded on `stream` right
- *               before the GEMM of layer-step i and events[2i+1] right after,
- *               so a caller can time the GEMM kernels alone.
+ *               (passed as void*): events[2i] and events[2i+1] become the start
+ *               and stop events of the GEMM dispatch of layer-step i
+ *               (hipExtLaunchKernel), stamped with that kernel's own start and
+ *               end, so a caller can time the GEMM kernels alone.
  *   num_layers must equal the schedule's layer count.  Validation covers every
  *   layer before the first launch.
  */

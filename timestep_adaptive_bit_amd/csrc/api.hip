@@ -374,28 +374,25 @@ int tabit_run_schedule(tabit_ctx* ctx, int first_step, int num_steps, const tabi
         float* sa = reinterpret_cast<float*>(ws + align256(mk));
         e = tabit::launch_quant_int8(x, L.M, L.K, had_block, 1.0f, xq, sa, s);
         if (e != hipSuccess) return hip_status(ctx, e, "run_schedule quantizer launch");
-        if (e0 && (e = hipEventRecord(e0, s)) != hipSuccess) return hip_status(ctx, e, "event record");
         int cfg = ctx->force_gemm_cfg;
         if (cfg < 0) cfg = ctx->tuned_cfg(path == TABIT_PATH_BITSERIAL ? 1 : 0, L.M, L.N, L.K);
         if (cfg < 0) cfg = tabit::gemm_config_choose(L.M, L.N, L.K, num_cus);
         e = tabit::launch_gemm_i8(cfg, path == TABIT_PATH_BITSERIAL, xq, sa, L.w_q, L.w_scale, L.M,
-                                  L.N, L.K, ctx->k_bits[i], L.y_bf16, nullptr, s);
+                                  L.N, L.K, ctx->k_bits[i], L.y_bf16, nullptr, s, e0, e1);
         if (e != hipSuccess) return hip_status(ctx, e, "run_schedule GEMM launch");
       } else {
         uint8_t* xf = ws;
         uint8_t* xe = ws + align256(mk / 2);
         e = tabit::launch_quant_mx(x, L.M, L.K, had_block, xf, xe, s);
         if (e != hipSuccess) return hip_status(ctx, e, "run_schedule MX quantizer launch");
-        if (e0 && (e = hipEventRecord(e0, s)) != hipSuccess) return hip_status(ctx, e, "event record");
         int cfg = ctx->force_mx_cfg;
         if (cfg < 0) cfg = ctx->tuned_cfg(2, L.M, L.N, L.K);
         if (cfg < 0) cfg = tabit::mx_config_choose(L.M, L.N, L.K, num_cus);
         e = tabit::launch_gemm_mxfp4(cfg, xf, xe, L.w_fp4, L.w_e8m0, L.M, L.N, L.K,
                                      1.0f / (float)(had_block > 0 ? had_block : 1), L.y_bf16,
-                                     nullptr, s);
+                                     nullptr, s, e0, e1);
         if (e != hipSuccess) return hip_status(ctx, e, "run_schedule MXFP4 GEMM launch");
       }
-      if (e1 && (e = hipEventRecord(e1, s)) != hipSuccess) return hip_status(ctx, e, "event record");
     }
   }
   return TABIT_OK;

@@ -203,15 +203,16 @@ constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 template <int BM, int BN, int WM, int WN, int RB, int NST>
 hipError_t launch_cfg(bool bitserial, const int8_t* xq, const float* sa, const int8_t* wq,
                       const float* sw, int M, int N, int K, int kbits, uint16_t* y, int32_t* acc,
-                      hipStream_t s) {
+                      hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const int grid = tiles_m * tiles_n;
-  if (bitserial)
-    gemm_i8_kernel<BM, BN, WM, WN, RB, NST, true><<<grid, WM * WN * 64, 0, s>>>(
-        xq, sa, wq, sw, M, N, K, kbits, y, acc, tiles_m, tiles_n);
+  const dim3 grid(tiles_m * tiles_n), block(WM * WN * 64);
+  auto kern = bitserial ? gemm_i8_kernel<BM, BN, WM, WN, RB, NST, true>
+                        : gemm_i8_kernel<BM, BN, WM, WN, RB, NST, false>;
+  if (ev0 != nullptr || ev1 != nullptr)   // timestamps of this dispatch itself
+    hipExtLaunchKernelGGL(kern, grid, block, 0, s, ev0, ev1, 0, xq, sa, wq, sw, M, N, K, kbits, y,
+                          acc, tiles_m, tiles_n);
   else
-    gemm_i8_kernel<BM, BN, WM, WN, RB, NST, false><<<grid, WM * WN * 64, 0, s>>>(
-        xq, sa, wq, sw, M, N, K, kbits, y, acc, tiles_m, tiles_n);
+    kern<<<grid, block, 0, s>>>(xq, sa, wq, sw, M, N, K, kbits, y, acc, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -246,10 +247,12 @@ int gemm_config_choose(int M, int N, int K, int num_cus) {
 
 hipError_t launch_gemm_i8(int cfg, bool bitserial, const int8_t* xq, const float* sa,
                           const int8_t* wq, const float* sw, int M, int N, int K, int kbits,
-                          uint16_t* y, int32_t* acc, hipStream_t stream) {
+                          uint16_t* y, int32_t* acc, hipStream_t stream, hipEvent_t ev0,
+                          hipEvent_t ev1) {
 #define TABIT_CASE(I, BM, BN, WM, WN, RB, NST, SLOTS, RATE) \
   case I:                                            \
-    return launch_cfg<BM, BN, WM, WN, RB, NST>(bitserial, xq, sa, wq, sw, M, N, K, kbits, y, acc, stream);
+    return launch_cfg<BM, BN, WM, WN, RB, NST>(bitserial, xq, sa, wq, sw, M, N, K, kbits, y, acc, \
+                                               stream, ev0, ev1);
   switch (cfg) {
     TABIT_I8_CONFIGS(TABIT_CASE)
     default: return hipErrorInvalidValue;

@@ -187,10 +187,15 @@ constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_cfg(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq, const uint8_t* we,
                       int M, int N, int K, float out_scale, uint16_t* y, float* acc,
-                      hipStream_t s) {
+                      hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  gemm_mxfp4_kernel<BM, BN, WM, WN><<<tiles_m * tiles_n, WM * WN * 64, 0, s>>>(
-      xq, xe, wq, we, M, N, K, out_scale, y, acc, tiles_m, tiles_n);
+  const dim3 grid(tiles_m * tiles_n), block(WM * WN * 64);
+  if (ev0 != nullptr || ev1 != nullptr)   // timestamps of this dispatch itself
+    hipExtLaunchKernelGGL(gemm_mxfp4_kernel<BM, BN, WM, WN>, grid, block, 0, s, ev0, ev1, 0, xq, xe,
+                          wq, we, M, N, K, out_scale, y, acc, tiles_m, tiles_n);
+  else
+    gemm_mxfp4_kernel<BM, BN, WM, WN><<<grid, block, 0, s>>>(xq, xe, wq, we, M, N, K, out_scale, y,
+                                                             acc, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -221,10 +226,11 @@ int mx_config_choose(int M, int N, int K, int num_cus) {
 
 hipError_t launch_gemm_mxfp4(int cfg, const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
                              const uint8_t* we, int M, int N, int K, float out_scale, uint16_t* y,
-                             float* acc, hipStream_t stream) {
+                             float* acc, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
 #define TABIT_CASE(I, BM, BN, WM, WN, SLOTS, RATE) \
   case I:                                           \
-    return launch_cfg<BM, BN, WM, WN>(xq, xe, wq, we, M, N, K, out_scale, y, acc, stream);
+    return launch_cfg<BM, BN, WM, WN>(xq, xe, wq, we, M, N, K, out_scale, y, acc, stream, \
+                                      ev0, ev1);
   switch (cfg) {
     TABIT_MX_CONFIGS(TABIT_CASE)
     default: return hipErrorInvalidValue;

@@ -2,6 +2,7 @@
 // Not part of the public ABI (see include/tabit.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -32,9 +33,11 @@ int gemm_config_count();
 GemmConfig gemm_config(int index);
 int gemm_config_choose(int M, int N, int K, int num_cus);
 
+// ev0 / ev1 (optional): events stamped with this GEMM kernel's start and stop.
 hipError_t launch_gemm_i8(int cfg, bool bitserial, const int8_t* xq, const float* sa,
                           const int8_t* wq, const float* sw, int M, int N, int K, int kbits,
-                          uint16_t* y, int32_t* acc, hipStream_t stream);
+                          uint16_t* y, int32_t* acc, hipStream_t stream,
+                          hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 // ---------------------------------------------------------------- MXFP4 GEMM
 int mx_config_count();
@@ -43,7 +46,8 @@ int mx_config_choose(int M, int N, int K, int num_cus);
 
 hipError_t launch_gemm_mxfp4(int cfg, const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
                              const uint8_t* we, int M, int N, int K, float out_scale,
-                             uint16_t* y, float* acc, hipStream_t stream);
+                             uint16_t* y, float* acc, hipStream_t stream,
+                             hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 // Compute units of the current device (cached per device id).
 int device_num_cus();
