@@ -36,7 +36,8 @@
  *               Faults inside kernels surface at the caller's synchronize.
  *   Threads     A ctx is not thread-safe; separate ctxs are independent.
  *   Shapes      M >= 0 (M == 0 is a no-op), K % 32 == 0 and 32 <= K <= 32768,
- *               N % 32 == 0 (N == 0 is a no-op), K % had_block == 0.
+ *               N % 32 == 0 (N == 0 is a no-op), K % had_block == 0;
+ *               M * K and N * K below 2^31 (each operand under 2 GiB).
  *               had_block in {0, 32, 64, 128} (0 = no rotation); the MXFP4
  *               format takes had_block in {0, 32}.
  *   Alignment   bf16/int8/fp4 matrices 16-byte aligned; fp32 vectors 4-byte.
@@ -68,7 +69,7 @@ enum tabit_status {
 };
 
 enum tabit_fmt { TABIT_FMT_INT8 = 0, TABIT_FMT_MXFP4 = 1 };
-enum tabit_path { TABIT_PATH_MASKED = 0, TABIT_PATH_BITSERIAL = 1 };
+enum tabit_path { TABIT_PATH_MASKED = 0, TABIT_PATH_BITSERIAL = 1, TABIT_PATH_PLANES = 3 };
 
 /* Create / destroy a context (host memory only; makes no HIP call).
  * tabit_create returns TABIT_EINVAL if out is NULL, TABIT_ENOMEM on failure. */
@@ -167,6 +168,33 @@ int tabit_qgemm_bitserial(tabit_ctx* ctx, const int8_t* x_q, const float* x_scal
                           uint16_t* y_bf16, int32_t* acc, void* stream);
 
 /*
+ * Plane-major copy of the shared INT8 buffer.  TASQ section 2 (Temporal-
+ * Precision Engine): only the weight bit-planes a layer-step keeps are
+ * streamed (plane fetches 2LR -> L + R).  Stored plane by plane, a step with
+ * mask k reads (8 - k)/8 of the buffer; the copy has the same size as w_q
+ * (N * K bytes) and replaces it for tabit_plane_qgemm.
+ *   w_q       device int8 [N][K] (from tabit_quantize_weights).
+ *   w_planes  device uint32 [8][K/32][N] output: word [b][g][n] holds bit b
+ *             of the 32 codes w_q[n][32g + i], code i = 4u + q (u = 0..7,
+ *             q = 0..3) at bit 8q + u.  16-byte aligned.
+ * Errors: EINVAL (null), ESHAPE (N % 32, K % 32, K range, size), EALIGN.
+ */
+int tabit_pack_weight_planes(tabit_ctx* ctx, const int8_t* w_q, int N, int K, uint32_t* w_planes,
+                             void* stream);
+
+/*
+ * Masked W8A8 GEMM reading the plane-major weights: only planes b = k_bits..7
+ * are fetched; each 16-byte weight fragment is rebuilt on chip as
+ * sum_{b >= k} c_b * bit_b = (w >> k) << k (TASQ section 2), so the results
+ * equal tabit_masked_qgemm bit for bit (acc exact, y by the same epilogue).
+ * Same arguments, layouts and errors as tabit_masked_qgemm, with w_planes
+ * from tabit_pack_weight_planes in place of w_q.
+ */
+int tabit_plane_qgemm(tabit_ctx* ctx, const int8_t* x_q, const float* x_scale,
+                      const uint32_t* w_planes, const float* w_scale, int M, int N, int K,
+                      int k_bits, uint16_t* y_bf16, int32_t* acc, void* stream);
+
+/*
  * MXFP4 (W4A4) GEMM for layer-steps scheduled to 4 bits (6Bit-Diffusion
  * section 2A).  acc[m][n] = sum over 32-blocks j of 2^(xe[m][j] + we[n][j] - 254)
  * * sum_i e2m1(x)*e2m1(w), accumulated in fp32 by the scaled matrix cores
@@ -188,8 +216,9 @@ size_t tabit_act_workspace_bytes(int M, int K);
  * TASQ section 2 / abstract: the learned schedule maps to execution with no
  * switching overhead -- here a switch is one table lookup and a scalar kernel
  * argument.  Looks up (k, fmt); INT8: quantizes x into act_ws and runs the
- * masked GEMM (path = TABIT_PATH_MASKED) or the bit-plane GEMM
- * (TABIT_PATH_BITSERIAL) with k; MXFP4: MX-quantizes x and runs the MXFP4 GEMM
+ * masked GEMM (path = TABIT_PATH_MASKED), the bit-plane GEMM
+ * (TABIT_PATH_BITSERIAL) or the plane-major GEMM (TABIT_PATH_PLANES: w_q then
+ * points at the words of tabit_pack_weight_planes) with k; MXFP4: MX-quantizes x and runs the MXFP4 GEMM
  * with out_scale 1/max(had_block, 1).
  *   w_q/w_scale required for INT8 steps, w_fp4/w_e8m0 for MXFP4 steps.
  *   act_ws device workspace of at least tabit_act_workspace_bytes(M, K),
@@ -204,7 +233,8 @@ int tabit_scheduled_linear(tabit_ctx* ctx, int step, int layer, int path,
 /* One linear layer of a stack, for tabit_run_schedule. */
 typedef struct tabit_layer {
   int M, N, K;               /* tokens, output and input features                     */
-  const int8_t* w_q;         /* device [N][K] INT8 codes (NULL if never INT8)         */
+  const int8_t* w_q;         /* device [N][K] INT8 codes (NULL if never INT8); with   */
+                             /* TABIT_PATH_PLANES the plane-major words instead       */
   const float* w_scale;      /* device [N]                                            */
   const uint8_t* w_fp4;      /* device [N][K/2] MXFP4 copy (NULL if never MXFP4)      */
   const uint8_t* w_e8m0;     /* device [N][K/32]                                      */
@@ -232,13 +262,14 @@ int tabit_run_schedule(tabit_ctx* ctx, int first_step, int num_steps, const tabi
 
 /*
  * Autotune the tile configuration for one GEMM problem: time every
- * configuration of the GEMM `path` (TABIT_PATH_MASKED, TABIT_PATH_BITSERIAL, or
- * 2 for the MXFP4 GEMM) on the caller's buffers, `reps` launches each, and
+ * configuration of the GEMM `path` (TABIT_PATH_MASKED, TABIT_PATH_BITSERIAL,
+ * 2 for the MXFP4 GEMM, TABIT_PATH_PLANES) on the caller's buffers, `reps` launches each, and
  * remember the fastest for (path, M, N, K) in ctx; later calls with that shape
  * on that path use it (an explicit TABIT_OPT_*_CONFIG still wins).  The
  * buffers follow the layouts of tabit_masked_qgemm (path 0/1: x_q int8,
- * x_scale fp32, w_q int8, w_scale fp32) or tabit_mxfp4_qgemm (path 2: x_fp4,
- * x_e8m0, w_fp4, w_e8m0); y_bf16 [M][N] receives scratch results.
+ * x_scale fp32, w_q int8, w_scale fp32), tabit_mxfp4_qgemm (path 2: x_fp4,
+ * x_e8m0, w_fp4, w_e8m0) or tabit_plane_qgemm (path 3: w_q = the plane-major
+ * words); y_bf16 [M][N] receives scratch results.
  * Synchronizes `stream` to read the timings: call it outside graph capture,
  * e.g. during warm-up.  *best_cfg (may be NULL) receives the winner.
  */
@@ -249,10 +280,10 @@ int tabit_autotune_gemm(tabit_ctx* ctx, int path, const void* x_q, const void* x
 /*
  * Options (tests and tuning).  TABIT_OPT_GEMM_CONFIG forces the INT8 GEMM tile
  * configuration (value = index from tabit_gemm_config_info, -1 = automatic);
- * TABIT_OPT_MXFP4_CONFIG likewise for the MXFP4 GEMM.  EINVAL for an unknown
- * option or value.  Makes no HIP call.
+ * TABIT_OPT_MXFP4_CONFIG and TABIT_OPT_PLANE_CONFIG likewise for the MXFP4 and
+ * plane-major GEMMs.  EINVAL for an unknown option or value.  Makes no HIP call.
  */
-enum tabit_option { TABIT_OPT_GEMM_CONFIG = 0, TABIT_OPT_MXFP4_CONFIG = 1 };
+enum tabit_option { TABIT_OPT_GEMM_CONFIG = 0, TABIT_OPT_MXFP4_CONFIG = 1, TABIT_OPT_PLANE_CONFIG = 2 };
 int tabit_set_option(tabit_ctx* ctx, int option, int value);
 
 /* Describe INT8 GEMM tile configuration `index` (0 <= index < count): block
@@ -262,6 +293,9 @@ int tabit_gemm_config_info(int index, int* bm, int* bn, int* split_k);
 
 /* As tabit_gemm_config_info, for the MXFP4 GEMM's tile configurations. */
 int tabit_mxfp4_config_info(int index, int* bm, int* bn);
+
+/* As tabit_mxfp4_config_info, for the plane-major GEMM's tile configurations. */
+int tabit_plane_config_info(int index, int* bm, int* bn);
 
 /* The configuration the automatic choice would take for (M, N, K) on a device
  * with num_cus compute units (num_cus <= 0: 256).  Makes no HIP call. */

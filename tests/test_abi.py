@@ -78,7 +78,7 @@ def _gemm(lib, ctx, fn, **kw):
                             a["k"], a["y"], a["acc"], None)
 
 
-@pytest.mark.parametrize("fn", ["tabit_masked_qgemm", "tabit_qgemm_bitserial"])
+@pytest.mark.parametrize("fn", ["tabit_masked_qgemm", "tabit_qgemm_bitserial", "tabit_plane_qgemm"])
 def test_gemm_validation(lib, ctx, fn):
     cases = [
         (dict(k=8), T.ERANGE), (dict(k=-1), T.ERANGE),
@@ -88,10 +88,26 @@ def test_gemm_validation(lib, ctx, fn):
         (dict(xq=MISALIGNED), T.EALIGN), (dict(y=FAKE + 8), T.EALIGN),
         (dict(xs=FAKE + 2), T.EALIGN),
         (dict(M=0), T.OK), (dict(N=0), T.OK),        # empty problems are no-ops
+        (dict(M=1 << 16, K=32768), T.ESHAPE),         # an operand of 2 GiB
+        (dict(N=65536, K=32768), T.ESHAPE),
     ]
     for kw, want in cases:
         assert _gemm(lib, ctx, fn, **kw) == want, (kw, ctx.last_error())
     assert lib.tabit_masked_qgemm(None, FAKE, FAKE, FAKE, FAKE, 1, 32, 32, 0, FAKE, None, None) == T.EINVAL
+
+
+def test_pack_planes_validation(lib, ctx):
+    def p(N=64, K=64, w=FAKE, out=FAKE):
+        return lib.tabit_pack_weight_planes(ctx.handle, w, N, K, out, None)
+    assert p(w=None) == T.EINVAL
+    assert p(out=None) == T.EINVAL
+    assert p(N=48) == T.ESHAPE
+    assert p(K=48) == T.ESHAPE
+    assert p(K=65536) == T.ESHAPE
+    assert p(N=65536, K=32768) == T.ESHAPE
+    assert p(out=FAKE + 4) == T.EALIGN
+    assert p(N=0) == T.OK
+    assert lib.tabit_pack_weight_planes(None, FAKE, 32, 32, FAKE, None) == T.EINVAL
 
 
 def test_quant_act_validation(lib, ctx):
@@ -138,6 +154,7 @@ def test_scheduled_linear_validation(lib, ctx):
     assert s() == T.ENOSCHED
     ctx.set_step_schedule(np.array([[0, 3]]), np.array([[0, 1]]))
     assert s(path=5) == T.EINVAL
+    assert s(path=2) == T.EINVAL                         # 2 names the MXFP4 GEMM only in autotune
     assert s(step=1) == T.ENOSCHED
     assert s(nbytes=10) == T.ESHAPE
     assert s(wq=None) == T.EINVAL                        # INT8 step without INT8 weights
@@ -168,6 +185,15 @@ def test_options_and_configs(ctx):
         ctx.set_option(99, 0)
     for M, N, K in ((64, 1152, 1152), (4096, 3456, 1152), (17776, 7680, 1920)):
         assert 0 <= T.gemm_config_choose(M, N, K) < n
+    npl = T.plane_config_info()
+    assert npl >= 1
+    for i in range(npl):
+        bm, bn = T.plane_config_info(i)
+        assert bm % 32 == 0 and bn % 32 == 0
+        ctx.set_option(T.OPT_PLANE_CONFIG, i)
+    ctx.set_option(T.OPT_PLANE_CONFIG, -1)
+    with pytest.raises(T.TabitError):
+        ctx.set_option(T.OPT_PLANE_CONFIG, npl)
 
 
 def test_product_path_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -246,6 +246,57 @@ def test_accumulator_bound_extreme():
     assert int(O.masked_gemm_i32(X, W, 0)[0, 0]) == 127 * 128 * K
 
 
+# ---------------------------------------------------------------- plane-major storage
+# Layout (this library's encoding): word P[b][g][n] holds bit b of the weights
+# W[n][32g + i]; weight i = 4u + q sits at bit 8q + u.
+
+
+def test_plane_layout_hand_examples():
+    w = np.zeros((2, 64), np.int8)
+    w[0, 0] = 1            # i = 0 (u 0, q 0): plane 0, bit 0
+    w[0, 5] = -128         # 0x80, i = 5 (u 1, q 1): plane 7, bit 9
+    w[0, 31] = 3           # i = 31 (u 7, q 3): planes 0 and 1, bit 31
+    w[1, 32 + 6] = 64      # group 1, i = 6 (u 1, q 2): plane 6, bit 17
+    w[1, 32 + 12] = -1     # 0xFF, group 1, i = 12 (u 3, q 0): every plane, bit 3
+    P = O.pack_weight_planes(w)
+    assert P.shape == (8, 2, 2) and P.dtype == np.uint32
+    expect = np.zeros((8, 2, 2), np.uint64)
+    expect[0, 0, 0] = 0x00000001 | 0x80000000
+    expect[1, 0, 0] = 0x80000000
+    expect[7, 0, 0] = 0x00000200
+    expect[6, 1, 1] = 0x00020000
+    for b in range(8):
+        expect[b, 1, 1] |= 0x00000008
+    assert np.array_equal(P.astype(np.uint64), expect)
+
+
+def test_plane_round_trip_every_byte_value():
+    w = np.arange(-128, 128, dtype=np.int64).astype(np.int8).reshape(1, 256)
+    w = np.concatenate([w, w[:, ::-1]], axis=0)
+    P = O.pack_weight_planes(w)
+    for k in range(8):
+        rebuilt = O.unpack_weight_planes(P, k)
+        assert rebuilt.tolist() == [[(int(v) >> k) << k for v in row] for row in w]
+
+
+def test_plane_unpack_reads_only_retained_planes():
+    w = S.gen_int8((7, 96), seed=5, lo=-128, hi=127)
+    P = O.pack_weight_planes(w)
+    rng = np.random.default_rng(9)
+    for k in range(1, 8):
+        junk = P.copy()
+        junk[:k] = rng.integers(0, 2**32, size=junk[:k].shape, dtype=np.uint64).astype(np.uint32)
+        assert np.array_equal(O.unpack_weight_planes(junk, k), O.lsb_truncate(w, k))
+
+
+@pytest.mark.parametrize("k", range(8))
+def test_plane_gemm_brute_force(k):
+    X = S.gen_int8((3, 64), seed=31, lo=-127, hi=127)
+    Wq = S.gen_int8((4, 64), seed=32, lo=-128, hi=127)
+    Wt = [[(int(w) >> k) << k for w in row] for row in Wq]
+    assert O.plane_gemm_i32(X, O.pack_weight_planes(Wq), k).tolist() == _brute_gemm(X, Wt)
+
+
 # ---------------------------------------------------------------- epilogue
 def test_bf16_rne_matches_torch_cast():
     rng = np.random.default_rng(5)

@@ -20,8 +20,8 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "tabit.h")
 
 OK, EINVAL, ESHAPE, EALIGN, ERANGE, ENOSCHED, EHIP, ENOMEM = 0, -1, -2, -3, -4, -5, -6, -7
 FMT_INT8, FMT_MXFP4 = 0, 1
-PATH_MASKED, PATH_BITSERIAL = 0, 1
-OPT_GEMM_CONFIG, OPT_MXFP4_CONFIG = 0, 1
+PATH_MASKED, PATH_BITSERIAL, PATH_PLANES = 0, 1, 3
+OPT_GEMM_CONFIG, OPT_MXFP4_CONFIG, OPT_PLANE_CONFIG = 0, 1, 2
 PATH_MXFP4_GEMM = 2
 
 _c_int, _c_void_p, _c_size_t, _c_float = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
@@ -59,6 +59,11 @@ _SIGNATURES = {
     "tabit_gemm_config_info": (_c_int, [_c_int, _PINT, _PINT, _PINT]),
     "tabit_gemm_config_choose": (_c_int, [_c_int, _c_int, _c_int, _c_int]),
     "tabit_mxfp4_config_info": (_c_int, [_c_int, _PINT, _PINT]),
+    "tabit_pack_weight_planes": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_void_p,
+                                          _c_void_p]),
+    "tabit_plane_qgemm": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
+                                   _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
+    "tabit_plane_config_info": (_c_int, [_c_int, _PINT, _PINT]),
 }
 
 
@@ -153,6 +158,18 @@ def mxfp4_config_info(index: int = -1):
         return int(lib.tabit_mxfp4_config_info(-1, None, None))
     bm, bn = ctypes.c_int(), ctypes.c_int()
     st = lib.tabit_mxfp4_config_info(index, ctypes.byref(bm), ctypes.byref(bn))
+    if st != OK:
+        raise TabitError(st, "bad config index")
+    return bm.value, bn.value
+
+
+def plane_config_info(index: int = -1):
+    """Number of plane-major GEMM configs (index < 0) or (bm, bn) of one."""
+    lib = load()
+    if index < 0:
+        return int(lib.tabit_plane_config_info(-1, None, None))
+    bm, bn = ctypes.c_int(), ctypes.c_int()
+    st = lib.tabit_plane_config_info(index, ctypes.byref(bm), ctypes.byref(bn))
     if st != OK:
         raise TabitError(st, "bad config index")
     return bm.value, bn.value
@@ -265,13 +282,19 @@ class Context:
         return x_q, x_scale
 
     def _gemm_i8(self, fn, x_q, x_scale, w_q, w_scale, k_bits, y=None, acc=None, want_y=True,
-                 want_acc=False):
+                 want_acc=False, planes=False):
         _dev(x_q, torch.int8, "x_q")
-        _dev(w_q, torch.int8, "w_q")
         M, K = x_q.shape
-        N = w_q.shape[0]
-        if w_q.shape[1] != K:
-            raise ValueError("x_q and w_q disagree on K")
+        if planes:
+            _dev(w_q, torch.int32, "w_planes")
+            if w_q.dim() != 3 or w_q.shape[0] != 8 or w_q.shape[1] * 32 != K:
+                raise ValueError("w_planes must be [8][K/32][N] words")
+            N = w_q.shape[2]
+        else:
+            _dev(w_q, torch.int8, "w_q")
+            N = w_q.shape[0]
+            if w_q.shape[1] != K:
+                raise ValueError("x_q and w_q disagree on K")
         _dev(x_scale, torch.float32, "x_scale", (M,))
         _dev(w_scale, torch.float32, "w_scale", (N,))
         dev = x_q.device
@@ -297,6 +320,23 @@ class Context:
                         want_acc=False):
         return self._gemm_i8(self._lib.tabit_qgemm_bitserial, x_q, x_scale, w_q, w_scale, k_bits, y,
                              acc, want_y, want_acc)
+
+    def pack_weight_planes(self, w_q: torch.Tensor, out: Optional[torch.Tensor] = None):
+        """Plane-major copy of int8 codes [N][K]: int32 tensor [8][K/32][N] (uint32 words)."""
+        _dev(w_q, torch.int8, "w_q")
+        N, K = w_q.shape
+        if out is None:
+            out = torch.empty((8, K // 32, N), dtype=torch.int32, device=w_q.device)
+        _dev(out, torch.int32, "w_planes", (8, K // 32, N))
+        st = self._lib.tabit_pack_weight_planes(self._h, w_q.data_ptr(), N, K, out.data_ptr(),
+                                                _stream(w_q.device))
+        self._check(st)
+        return out
+
+    def plane_qgemm(self, x_q, x_scale, w_planes, w_scale, k_bits, y=None, acc=None, want_y=True,
+                    want_acc=False):
+        return self._gemm_i8(self._lib.tabit_plane_qgemm, x_q, x_scale, w_planes, w_scale, k_bits,
+                             y, acc, want_y, want_acc, planes=True)
 
     def mxfp4_qgemm(self, x_fp4, x_e8m0, w_fp4, w_e8m0, out_scale: float, y=None, acc=None,
                     want_y=True, want_acc=False):
@@ -328,9 +368,12 @@ class Context:
         """One linear at (step, layer): schedule lookup, quantize, GEMM -- all in the library."""
         _dev(x, torch.bfloat16, "x")
         M, K = x.shape
-        wq = weights.get("w_q")
+        wq = weights.get("w_planes") if path == PATH_PLANES else weights.get("w_q")
         wf = weights.get("w_fp4")
-        N = (wq if wq is not None else wf).shape[0]
+        if wq is not None:
+            N = wq.shape[2] if path == PATH_PLANES else wq.shape[0]
+        else:
+            N = wf.shape[0]
         if y is None:
             y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
         _dev(y, torch.bfloat16, "y", (M, N))

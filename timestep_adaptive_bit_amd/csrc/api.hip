@@ -14,6 +14,9 @@
 namespace {
 
 constexpr int kMaxK = 32768;
+// Buffer descriptors address operands with 32-bit byte offsets; the top bit marks
+// out-of-range reads, so every operand stays below 2^31 bytes.
+constexpr size_t kMaxOperandBytes = 0x7FFFFFFFu;
 
 int fail(tabit_ctx* ctx, int status, const char* fmt, ...) {
   if (ctx != nullptr) {
@@ -57,28 +60,57 @@ int check_gemm(tabit_ctx* ctx, const void* xq, const void* xs, const void* wq, c
     return fail(ctx, TABIT_ESHAPE, "N must be a non-negative multiple of 32 (got %d)", N);
   if (K < 32 || K > kMaxK || K % 32 != 0)
     return fail(ctx, TABIT_ESHAPE, "K must be a multiple of 32 in [32, %d] (got %d)", kMaxK, K);
+  if ((size_t)M * (size_t)K > kMaxOperandBytes || (size_t)N * (size_t)K > kMaxOperandBytes)
+    return fail(ctx, TABIT_ESHAPE, "operands must stay below 2 GiB (M*K = %zu, N*K = %zu)",
+                (size_t)M * (size_t)K, (size_t)N * (size_t)K);
   if (!aligned(xq, 16) || !aligned(wq, 16) || (y && !aligned(y, 16)) || (acc && !aligned(acc, 16)))
     return fail(ctx, TABIT_EALIGN, "matrices must be 16-byte aligned");
   return TABIT_OK;
 }
 
-int gemm_i8_common(tabit_ctx* ctx, bool bitserial, const int8_t* x_q, const float* x_scale,
-                   const int8_t* w_q, const float* w_scale, int M, int N, int K, int k_bits,
+// The GEMM of one INT8 layer-step on `path`: masked (w = int8 codes), bit-plane
+// (same codes) or plane-major (w = the words of tabit_pack_weight_planes).  The
+// tile configuration is the forced one, else the autotuned one, else the
+// cost model's choice.
+hipError_t launch_int8_family(const tabit_ctx* ctx, int path, const int8_t* xq, const float* sa,
+                              const void* w, const float* sw, int M, int N, int K, int k,
+                              uint16_t* y, int32_t* acc, hipStream_t s, int num_cus,
+                              hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
+  if (path == TABIT_PATH_PLANES) {
+    int cfg = ctx->force_plane_cfg;
+    if (cfg < 0) cfg = ctx->tuned_cfg(TABIT_PATH_PLANES, M, N, K);
+    if (cfg < 0) cfg = tabit::plane_config_choose(M, N, K, num_cus);
+    return tabit::launch_gemm_planes(cfg, xq, sa, static_cast<const uint32_t*>(w), sw, M, N, K, k,
+                                     y, acc, s, e0, e1);
+  }
+  const bool bitserial = path == TABIT_PATH_BITSERIAL;
+  int cfg = ctx->force_gemm_cfg;
+  if (cfg < 0) cfg = ctx->tuned_cfg(bitserial ? 1 : 0, M, N, K);
+  if (cfg < 0) cfg = tabit::gemm_config_choose(M, N, K, num_cus);
+  return tabit::launch_gemm_i8(cfg, bitserial, xq, sa, static_cast<const int8_t*>(w), sw, M, N, K,
+                               k, y, acc, s, e0, e1);
+}
+
+bool valid_int8_path(int path) {
+  return path == TABIT_PATH_MASKED || path == TABIT_PATH_BITSERIAL || path == TABIT_PATH_PLANES;
+}
+
+int gemm_i8_common(tabit_ctx* ctx, int path, const int8_t* x_q, const float* x_scale,
+                   const void* w, const float* w_scale, int M, int N, int K, int k_bits,
                    uint16_t* y, int32_t* acc, void* stream) {
   if (ctx == nullptr) return TABIT_EINVAL;
-  int st = check_gemm(ctx, x_q, x_scale, w_q, w_scale, M, N, K, y, acc);
+  int st = check_gemm(ctx, x_q, x_scale, w, w_scale, M, N, K, y, acc);
   if (st != TABIT_OK) return st;
   if (!aligned(x_scale, 4) || !aligned(w_scale, 4))
     return fail(ctx, TABIT_EALIGN, "scales must be 4-byte aligned");
   if (k_bits < 0 || k_bits > 7) return fail(ctx, TABIT_ERANGE, "k_bits must be in [0, 7] (got %d)", k_bits);
   if (M == 0 || N == 0) return TABIT_OK;
-  int cfg = ctx->force_gemm_cfg;
-  if (cfg < 0) cfg = ctx->tuned_cfg(bitserial ? 1 : 0, M, N, K);
-  if (cfg < 0) cfg = tabit::gemm_config_choose(M, N, K, tabit::device_num_cus());
+  static const char* const what[] = {"masked_qgemm launch", "qgemm_bitserial launch", "",
+                                     "plane_qgemm launch"};
   return hip_status(ctx,
-                    tabit::launch_gemm_i8(cfg, bitserial, x_q, x_scale, w_q, w_scale, M, N, K,
-                                          k_bits, y, acc, static_cast<hipStream_t>(stream)),
-                    bitserial ? "qgemm_bitserial launch" : "masked_qgemm launch");
+                    launch_int8_family(ctx, path, x_q, x_scale, w, w_scale, M, N, K, k_bits, y, acc,
+                                       static_cast<hipStream_t>(stream), tabit::device_num_cus()),
+                    what[path]);
 }
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -226,15 +258,39 @@ int tabit_hadamard_quant_act(tabit_ctx* ctx, const uint16_t* x_bf16, int M, int 
 int tabit_masked_qgemm(tabit_ctx* ctx, const int8_t* x_q, const float* x_scale, const int8_t* w_q,
                        const float* w_scale, int M, int N, int K, int k_bits, uint16_t* y_bf16,
                        int32_t* acc, void* stream) {
-  return gemm_i8_common(ctx, false, x_q, x_scale, w_q, w_scale, M, N, K, k_bits, y_bf16, acc,
-                        stream);
+  return gemm_i8_common(ctx, TABIT_PATH_MASKED, x_q, x_scale, w_q, w_scale, M, N, K, k_bits, y_bf16,
+                        acc, stream);
 }
 
 int tabit_qgemm_bitserial(tabit_ctx* ctx, const int8_t* x_q, const float* x_scale,
                           const int8_t* w_q, const float* w_scale, int M, int N, int K, int k_bits,
                           uint16_t* y_bf16, int32_t* acc, void* stream) {
-  return gemm_i8_common(ctx, true, x_q, x_scale, w_q, w_scale, M, N, K, k_bits, y_bf16, acc,
-                        stream);
+  return gemm_i8_common(ctx, TABIT_PATH_BITSERIAL, x_q, x_scale, w_q, w_scale, M, N, K, k_bits,
+                        y_bf16, acc, stream);
+}
+
+int tabit_pack_weight_planes(tabit_ctx* ctx, const int8_t* w_q, int N, int K, uint32_t* w_planes,
+                             void* stream) {
+  if (ctx == nullptr) return TABIT_EINVAL;
+  if (w_q == nullptr || w_planes == nullptr) return fail(ctx, TABIT_EINVAL, "null pointer");
+  if (N < 0 || N % 32 != 0)
+    return fail(ctx, TABIT_ESHAPE, "N must be a non-negative multiple of 32 (got %d)", N);
+  if (K < 32 || K > kMaxK || K % 32 != 0)
+    return fail(ctx, TABIT_ESHAPE, "K must be a multiple of 32 in [32, %d] (got %d)", kMaxK, K);
+  if ((size_t)N * (size_t)K > kMaxOperandBytes)
+    return fail(ctx, TABIT_ESHAPE, "N*K = %zu bytes exceeds 2 GiB", (size_t)N * (size_t)K);
+  if (!aligned(w_q, 16) || !aligned(w_planes, 16))
+    return fail(ctx, TABIT_EALIGN, "w_q and w_planes must be 16-byte aligned");
+  if (N == 0) return TABIT_OK;
+  return hip_status(ctx, tabit::launch_pack_planes(w_q, N, K, w_planes, static_cast<hipStream_t>(stream)),
+                    "pack_weight_planes launch");
+}
+
+int tabit_plane_qgemm(tabit_ctx* ctx, const int8_t* x_q, const float* x_scale,
+                      const uint32_t* w_planes, const float* w_scale, int M, int N, int K,
+                      int k_bits, uint16_t* y_bf16, int32_t* acc, void* stream) {
+  return gemm_i8_common(ctx, TABIT_PATH_PLANES, x_q, x_scale, w_planes, w_scale, M, N, K, k_bits,
+                        y_bf16, acc, stream);
 }
 
 int tabit_mxfp4_qgemm(tabit_ctx* ctx, const uint8_t* x_fp4, const uint8_t* x_e8m0,
@@ -267,8 +323,7 @@ int tabit_scheduled_linear(tabit_ctx* ctx, int step, int layer, int path, const 
                            const float* w_scale, const uint8_t* w_fp4, const uint8_t* w_e8m0,
                            void* act_ws, size_t act_ws_bytes, uint16_t* y_bf16, void* stream) {
   if (ctx == nullptr) return TABIT_EINVAL;
-  if (path != TABIT_PATH_MASKED && path != TABIT_PATH_BITSERIAL)
-    return fail(ctx, TABIT_EINVAL, "unknown path %d", path);
+  if (!valid_int8_path(path)) return fail(ctx, TABIT_EINVAL, "unknown path %d", path);
   int k = 0, fmt = 0;
   int st = tabit_schedule_lookup(ctx, step, layer, &k, &fmt);
   if (st != TABIT_OK) return st;
@@ -299,8 +354,7 @@ int tabit_scheduled_linear(tabit_ctx* ctx, int step, int layer, int path, const 
     float* sa = reinterpret_cast<float*>(ws + align256(mk));
     st = tabit_hadamard_quant_act(ctx, x_bf16, M, K, had_block, TABIT_FMT_INT8, xq, sa, stream);
     if (st != TABIT_OK) return st;
-    return gemm_i8_common(ctx, path == TABIT_PATH_BITSERIAL, xq, sa, w_q, w_scale, M, N, K, k,
-                          y_bf16, nullptr, stream);
+    return gemm_i8_common(ctx, path, xq, sa, w_q, w_scale, M, N, K, k, y_bf16, nullptr, stream);
   }
   uint8_t* xf = ws;
   uint8_t* xe = ws + align256(mk / 2);
@@ -316,8 +370,7 @@ int tabit_run_schedule(tabit_ctx* ctx, int first_step, int num_steps, const tabi
   if (ctx == nullptr) return TABIT_EINVAL;
   if (layers == nullptr || x_bf16 == nullptr || act_ws == nullptr)
     return fail(ctx, TABIT_EINVAL, "null pointer");
-  if (path != TABIT_PATH_MASKED && path != TABIT_PATH_BITSERIAL)
-    return fail(ctx, TABIT_EINVAL, "unknown path %d", path);
+  if (!valid_int8_path(path)) return fail(ctx, TABIT_EINVAL, "unknown path %d", path);
   if (ctx->steps == 0) return fail(ctx, TABIT_ENOSCHED, "no schedule installed");
   if (num_layers != ctx->layers)
     return fail(ctx, TABIT_ESHAPE, "%d layers given, schedule has %d", num_layers, ctx->layers);
@@ -336,6 +389,8 @@ int tabit_run_schedule(tabit_ctx* ctx, int first_step, int num_steps, const tabi
       return fail(ctx, TABIT_ESHAPE, "layer %d: N must be a non-negative multiple of 32", l);
     if (L.y_bf16 == nullptr || !aligned(L.y_bf16, 16))
       return fail(ctx, TABIT_EINVAL, "layer %d: missing or misaligned output", l);
+    if ((size_t)L.M * (size_t)L.K > kMaxOperandBytes || (size_t)L.N * (size_t)L.K > kMaxOperandBytes)
+      return fail(ctx, TABIT_ESHAPE, "layer %d: operands must stay below 2 GiB", l);
     if (act_ws_bytes < tabit_act_workspace_bytes(L.M, L.K))
       return fail(ctx, TABIT_ESHAPE, "layer %d: act_ws holds %zu bytes, %zu needed", l,
                   act_ws_bytes, tabit_act_workspace_bytes(L.M, L.K));
@@ -374,11 +429,8 @@ int tabit_run_schedule(tabit_ctx* ctx, int first_step, int num_steps, const tabi
         float* sa = reinterpret_cast<float*>(ws + align256(mk));
         e = tabit::launch_quant_int8(x, L.M, L.K, had_block, 1.0f, xq, sa, s);
         if (e != hipSuccess) return hip_status(ctx, e, "run_schedule quantizer launch");
-        int cfg = ctx->force_gemm_cfg;
-        if (cfg < 0) cfg = ctx->tuned_cfg(path == TABIT_PATH_BITSERIAL ? 1 : 0, L.M, L.N, L.K);
-        if (cfg < 0) cfg = tabit::gemm_config_choose(L.M, L.N, L.K, num_cus);
-        e = tabit::launch_gemm_i8(cfg, path == TABIT_PATH_BITSERIAL, xq, sa, L.w_q, L.w_scale, L.M,
-                                  L.N, L.K, ctx->k_bits[i], L.y_bf16, nullptr, s, e0, e1);
+        e = launch_int8_family(ctx, path, xq, sa, L.w_q, L.w_scale, L.M, L.N, L.K, ctx->k_bits[i],
+                               L.y_bf16, nullptr, s, num_cus, e0, e1);
         if (e != hipSuccess) return hip_status(ctx, e, "run_schedule GEMM launch");
       } else {
         uint8_t* xf = ws;
@@ -402,7 +454,7 @@ int tabit_autotune_gemm(tabit_ctx* ctx, int path, const void* x_q, const void* x
                         const void* w_q, const void* w_scale, int M, int N, int K, int k_bits,
                         uint16_t* y_bf16, int reps, int* best_cfg, void* stream) {
   if (ctx == nullptr) return TABIT_EINVAL;
-  if (path < 0 || path > 2) return fail(ctx, TABIT_EINVAL, "unknown GEMM path %d", path);
+  if (path < 0 || path > 3) return fail(ctx, TABIT_EINVAL, "unknown GEMM path %d", path);
   if (y_bf16 == nullptr) return fail(ctx, TABIT_EINVAL, "autotune needs y_bf16");
   if (reps < 1) return fail(ctx, TABIT_EINVAL, "reps must be >= 1");
   int st = check_gemm(ctx, x_q, x_scale, w_q, w_scale, M, N, K, y_bf16, nullptr);
@@ -410,7 +462,9 @@ int tabit_autotune_gemm(tabit_ctx* ctx, int path, const void* x_q, const void* x
   if (k_bits < 0 || k_bits > 7) return fail(ctx, TABIT_ERANGE, "k_bits must be in [0, 7] (got %d)", k_bits);
   if (M == 0 || N == 0) return TABIT_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int n = path == 2 ? tabit::mx_config_count() : tabit::gemm_config_count();
+  const int n = path == 2   ? tabit::mx_config_count()
+                : path == 3 ? tabit::plane_config_count()
+                            : tabit::gemm_config_count();
   hipEvent_t e0 = nullptr, e1 = nullptr;
   hipError_t e = hipEventCreate(&e0);
   if (e == hipSuccess) e = hipEventCreate(&e1);
@@ -425,6 +479,12 @@ int tabit_autotune_gemm(tabit_ctx* ctx, int path, const void* x_q, const void* x
                                       static_cast<const uint8_t*>(w_q),
                                       static_cast<const uint8_t*>(w_scale), M, N, K, 1.0f, y_bf16,
                                       nullptr, s);
+    if (path == 3)
+      return tabit::launch_gemm_planes(cfg, static_cast<const int8_t*>(x_q),
+                                       static_cast<const float*>(x_scale),
+                                       static_cast<const uint32_t*>(w_q),
+                                       static_cast<const float*>(w_scale), M, N, K, k_bits, y_bf16,
+                                       nullptr, s);
     return tabit::launch_gemm_i8(cfg, path == 1, static_cast<const int8_t*>(x_q),
                                  static_cast<const float*>(x_scale), static_cast<const int8_t*>(w_q),
                                  static_cast<const float*>(w_scale), M, N, K, k_bits, y_bf16,
@@ -466,6 +526,11 @@ int tabit_set_option(tabit_ctx* ctx, int option, int value) {
         return fail(ctx, TABIT_EINVAL, "MXFP4 config %d out of range", value);
       ctx->force_mx_cfg = value;
       return TABIT_OK;
+    case TABIT_OPT_PLANE_CONFIG:
+      if (value < -1 || value >= tabit::plane_config_count())
+        return fail(ctx, TABIT_EINVAL, "plane GEMM config %d out of range", value);
+      ctx->force_plane_cfg = value;
+      return TABIT_OK;
     default:
       return fail(ctx, TABIT_EINVAL, "unknown option %d", option);
   }
@@ -486,6 +551,15 @@ int tabit_mxfp4_config_info(int index, int* bm, int* bn) {
   if (index < 0) return tabit::mx_config_count();
   if (index >= tabit::mx_config_count() || bm == nullptr || bn == nullptr) return TABIT_EINVAL;
   const tabit::GemmConfig c = tabit::mx_config(index);
+  *bm = c.bm;
+  *bn = c.bn;
+  return TABIT_OK;
+}
+
+int tabit_plane_config_info(int index, int* bm, int* bn) {
+  if (index < 0) return tabit::plane_config_count();
+  if (index >= tabit::plane_config_count() || bm == nullptr || bn == nullptr) return TABIT_EINVAL;
+  const tabit::GemmConfig c = tabit::plane_config(index);
   *bm = c.bm;
   *bn = c.bn;
   return TABIT_OK;

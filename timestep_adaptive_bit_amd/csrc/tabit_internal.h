@@ -49,6 +49,18 @@ hipError_t launch_gemm_mxfp4(int cfg, const uint8_t* xq, const uint8_t* xe, cons
                              uint16_t* y, float* acc, hipStream_t stream,
                              hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
+// ---------------------------------------------------------------- plane-major storage
+// uint32 P[8][K/32][N]: word P[b][g][n] holds bit b of W[n][32g + i] at bit
+// 8*(i % 4) + i / 4.
+hipError_t launch_pack_planes(const int8_t* wq, int N, int K, uint32_t* planes, hipStream_t s);
+int plane_config_count();
+GemmConfig plane_config(int index);
+int plane_config_choose(int M, int N, int K, int num_cus);
+hipError_t launch_gemm_planes(int cfg, const int8_t* xq, const float* sa, const uint32_t* wp,
+                              const float* sw, int M, int N, int K, int kbits, uint16_t* y,
+                              int32_t* acc, hipStream_t stream, hipEvent_t ev0 = nullptr,
+                              hipEvent_t ev1 = nullptr);
+
 // Compute units of the current device (cached per device id).
 int device_num_cus();
 
@@ -62,7 +74,8 @@ struct tabit_ctx {
   std::vector<uint8_t> fmt;
   int force_gemm_cfg = -1;
   int force_mx_cfg = -1;
-  // autotuned tile configuration per (path, M, N, K); path 2 = MXFP4
+  int force_plane_cfg = -1;
+  // autotuned tile configuration per (path, M, N, K); path 2 = MXFP4, 3 = plane-major
   std::map<std::tuple<int, int, int, int>, int> tuned;
 
   int tuned_cfg(int path, int M, int N, int K) const {
