@@ -234,8 +234,11 @@ def cpu_baseline(wl, rows: int):
     }
 
 
-def k_sweep(ctx, T, torch, wl, weights, xs, ys, b):
-    """Per distinct INT8 shape: GEMM time at every k, masked and bit-plane (HIP events)."""
+def k_sweep(ctx, T, torch, wl, weights, xs, ys, b, cold=False):
+    """Per distinct INT8 shape: GEMM time at every k on the masked, bit-plane and
+    plane-major paths (HIP events around 5 launches).  cold: each launch reads its
+    own copy of the weights, cycling over more than 320 MB of copies, so the
+    weights stream from HBM (past the 256 MB last-level cache) on every launch."""
     res = {}
     seen = set()
     for li, layer in enumerate(wl.layers):
@@ -244,28 +247,44 @@ def k_sweep(ctx, T, torch, wl, weights, xs, ys, b):
             continue
         seen.add(key)
         xq, sa = ctx.hadamard_quant_act(xs[(0, layer.M, layer.K)], b, T.FMT_INT8)
-        wq, sw = weights[li]["w_q"], weights[li]["w_scale"]
-        ctx.autotune_gemm(T.PATH_BITSERIAL, xq, sa, wq, sw, *key, 0, ys[li], reps=2)
+        sw = weights[li]["w_scale"]
+        if "w_q" in weights[li]:
+            wq = weights[li]["w_q"]
+            wp = ctx.pack_weight_planes(wq)
+        else:
+            wp = weights[li]["w_planes"]
+            wq = None
+        ctx.autotune_gemm(T.PATH_PLANES, xq, sa, wp, sw, *key, 0, ys[li], reps=2)
+        fns = [("planes", ctx.plane_qgemm, wp)]
+        if wq is not None:
+            ctx.autotune_gemm(T.PATH_BITSERIAL, xq, sa, wq, sw, *key, 0, ys[li], reps=2)
+            fns = [("masked", ctx.masked_qgemm, wq), ("bitserial", ctx.qgemm_bitserial, wq)] + fns
         row = {}
-        for name, fn in (("masked", ctx.masked_qgemm), ("bitserial", ctx.qgemm_bitserial)):
+        for name, fn, w in fns:
+            copies = [w]
+            if cold:
+                n_copies = max(1, int(320e6 // (w.numel() * w.element_size())))
+                copies = [w] + [w.clone() for _ in range(n_copies - 1)]
+            reps = max(5, len(copies))
             times = []
             for k in range(8):
-                for _ in range(2):
-                    fn(xq, sa, wq, sw, k, y=ys[li])
+                for i in range(2):
+                    fn(xq, sa, copies[i % len(copies)], sw, k, y=ys[li])
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record()
-                for _ in range(5):
-                    fn(xq, sa, wq, sw, k, y=ys[li])
+                for i in range(reps):
+                    fn(xq, sa, copies[(i + 2) % len(copies)], sw, k, y=ys[li])
                 e1.record()
                 torch.cuda.synchronize()
-                times.append(round(e0.elapsed_time(e1) * 1e3 / 5, 2))
+                times.append(round(e0.elapsed_time(e1) * 1e3 / reps, 2))
             row[name] = times
+            del copies
         res["x".join(map(str, key))] = row
     return res
 
 
-def gemm_tiles(T, wl, tuned):
+def gemm_tiles(T, wl, tuned, path=0):
     """Tile shape (BM, BN) each distinct GEMM shape runs with."""
     out = {}
     for li, layer in enumerate(wl.layers):
@@ -274,7 +293,9 @@ def gemm_tiles(T, wl, tuned):
             name = f"{'mxfp4' if fmt else 'int8'} {layer.M}x{layer.N}x{layer.K}"
             if name in out:
                 continue
-            if fmt == 0:
+            if fmt == 0 and path == T.PATH_PLANES:
+                out[name] = "tuned" if key in tuned else "auto"
+            elif fmt == 0:
                 cfg = tuned.get(key, T.gemm_config_choose(layer.M, layer.N, layer.K))
                 out[name] = list(T.gemm_config_info(cfg)[:2])
             else:
@@ -288,7 +309,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=5, help="timed schedule passes")
     ap.add_argument("--warmup", type=int, default=2, help="untimed schedule passes")
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
-    ap.add_argument("--path", default="masked", choices=["masked", "bitserial"])
+    ap.add_argument("--path", default="masked", choices=["masked", "bitserial", "planes"])
     ap.add_argument("--had-block", type=int, default=None, help="override the workload's block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="token rows per shape in the oracle sample")
@@ -298,6 +319,8 @@ def main() -> int:
                          "calibrated choice, which keeps counter runs on the same kernels)")
     ap.add_argument("--shared-x", action="store_true",
                     help="reuse step 0's activations at every step (same work, faster set-up)")
+    ap.add_argument("--cold", action="store_true",
+                    help="with --k-sweep: every launch reads weights cold from HBM")
     ap.add_argument("--k-sweep", action="store_true",
                     help="also time each distinct INT8 shape at every k (masked and bit-plane)")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
@@ -340,7 +363,7 @@ def main() -> int:
     L, Tn = wl.num_layers, wl.steps
     ctx = T.Context()
     ctx.set_step_schedule(wl.k_bits, wl.fmt)
-    path = T.PATH_BITSERIAL if args.path == "bitserial" else T.PATH_MASKED
+    path = {"masked": T.PATH_MASKED, "bitserial": T.PATH_BITSERIAL, "planes": T.PATH_PLANES}[args.path]
 
     # ---- weights: one shared INT8 buffer per layer (+ MX copy where scheduled)
     weights = []
@@ -349,6 +372,8 @@ def main() -> int:
         needs_mx = bool(wl.fmt[:, li].any())
         needs_i8 = bool((wl.fmt[:, li] == 0).any())
         weights.append(ctx.quantize_weights(w, b, int8=needs_i8, mx=needs_mx))
+        if needs_i8 and path == T.PATH_PLANES:   # the same buffer stored plane by plane
+            weights[-1]["w_planes"] = ctx.pack_weight_planes(weights[-1].pop("w_q"))
         del w
     # ---- activations: one per distinct (M, K) per step; outputs: one per layer
     xs = {}
@@ -368,7 +393,8 @@ def main() -> int:
     layers = (T.Layer * L)()
     for li, (layer, wt) in enumerate(zip(wl.layers, weights)):
         layers[li].M, layers[li].N, layers[li].K = layer.M, layer.N, layer.K
-        layers[li].w_q = wt["w_q"].data_ptr() if "w_q" in wt else None
+        wq = wt.get("w_planes", wt.get("w_q"))
+        layers[li].w_q = wq.data_ptr() if wq is not None else None
         layers[li].w_scale = wt["w_scale"].data_ptr() if "w_scale" in wt else None
         layers[li].w_fp4 = wt["w_fp4"].data_ptr() if "w_fp4" in wt else None
         layers[li].w_e8m0 = wt["w_e8m0"].data_ptr() if "w_e8m0" in wt else None
@@ -389,7 +415,8 @@ def main() -> int:
                 x = xs[(0, layer.M, layer.K)]
                 if fmt == 0:
                     xq, xs_ = ctx.hadamard_quant_act(x, b, T.FMT_INT8)
-                    tuned[key] = ctx.autotune_gemm(path, xq, xs_, weights[li]["w_q"],
+                    tuned[key] = ctx.autotune_gemm(path, xq, xs_,
+                                                   weights[li].get("w_planes", weights[li].get("w_q")),
                                                    weights[li]["w_scale"], layer.M, layer.N,
                                                    layer.K, 2, ys[li], reps=3)
                 else:
@@ -465,8 +492,9 @@ def main() -> int:
             roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS,
                         "unit": "TOPS", "frac": round(achieved / INT8_PEAK_TOPS, 4),
                         "traffic": recorded_traffic(wl.name, args.path),
-                        "kernel": "gemm_i8_kernel (masked)" if path == T.PATH_MASKED
-                        else "gemm_i8_kernel (bitserial)",
+                        "kernel": {T.PATH_MASKED: "gemm_i8_kernel (masked)",
+                                   T.PATH_BITSERIAL: "gemm_i8_kernel (bitserial)",
+                                   T.PATH_PLANES: "gemm_planes_kernel"}[path],
                         "avg_launch_us": round(gemm_ms_i8 * 1e3 / n_i8, 3),
                         "timing": "start/stop events of each GEMM dispatch (hipExtLaunchKernel)"}
             detail["gemm_int8_ms_per_step"] = round(gemm_ms_i8 / args.steps, 3)
@@ -485,7 +513,8 @@ def main() -> int:
         detail["quantizer_and_gaps_ms_per_step"] = round(ms_per_step - detail["gemm_int8_ms_per_step"]
                                                          - detail.get("gemm_mxfp4_ms_per_step", 0.0), 3)
     if args.k_sweep:
-        detail["k_sweep_us"] = k_sweep(ctx, T, torch, wl, weights, xs, ys, b)
+        detail["k_sweep_us" + ("_cold" if args.cold else "")] = k_sweep(ctx, T, torch, wl, weights, xs,
+                                                                        ys, b, cold=args.cold)
 
     out = {
         "metric": "masked W8A8 GEMM TOPS and % of INT8 MFMA peak per denoising schedule",
@@ -507,7 +536,7 @@ def main() -> int:
         "frac_of_int8_peak": round(value / INT8_PEAK_TOPS, 4),
         "roofline": roofline,
         "detail": detail,
-        "gemm_tiles": gemm_tiles(T, wl, tuned),
+        "gemm_tiles": gemm_tiles(T, wl, tuned, path),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows)

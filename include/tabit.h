@@ -174,13 +174,19 @@ int tabit_qgemm_bitserial(tabit_ctx* ctx, const int8_t* x_q, const float* x_scal
  * mask k reads (8 - k)/8 of the buffer; the copy has the same size as w_q
  * (N * K bytes) and replaces it for tabit_plane_qgemm.
  *   w_q       device int8 [N][K] (from tabit_quantize_weights).
- *   w_planes  device uint32 [8][K/32][N] output: word [b][g][n] holds bit b
- *             of the 32 codes w_q[n][32g + i], code i = 4u + q (u = 0..7,
- *             q = 0..3) at bit 8q + u.  16-byte aligned.
+ *   w_planes  device uint32 [8][S][N][4], S = ceil(K/128), output
+ *             (tabit_weight_planes_bytes(N, K) bytes, 16-byte aligned): word
+ *             [b][s][n][j] holds bit b of the 32 codes w_q[n][128s + 32j + i],
+ *             code i = 4u + q (u = 0..7, q = 0..3) at bit 8q + u; words past K
+ *             are zero.  A plane's 128-code K-stage is 16 bytes per row.
  * Errors: EINVAL (null), ESHAPE (N % 32, K % 32, K range, size), EALIGN.
  */
 int tabit_pack_weight_planes(tabit_ctx* ctx, const int8_t* w_q, int N, int K, uint32_t* w_planes,
                              void* stream);
+
+/* Bytes of the plane-major copy of an N x K buffer: 128 * ceil(K/128) * N
+ * (N * K when K % 128 == 0).  0 for N or K <= 0.  Makes no HIP call. */
+size_t tabit_weight_planes_bytes(int N, int K);
 
 /*
  * Masked W8A8 GEMM reading the plane-major weights: only planes b = k_bits..7

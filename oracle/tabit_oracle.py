@@ -260,31 +260,38 @@ def bitplane_gemm_i32(x_q: np.ndarray, w_q: np.ndarray, k: int) -> np.ndarray:
 # plane fetches from 2LR to L + R.  The same 8 bits per weight can be stored
 # plane by plane so that a step with mask k reads 8 - k planes and never
 # touches the k dropped ones.  The layout is this library's own encoding (the
-# pages fix none): a uint32 array P[8][K/32][N]; word P[b][g][n] holds bit b
-# of the 32 weights W[n][32g + i], i = 0..31, with weight i = 4u + q at bit
-# position 8q + u (u = 0..7, q = 0..3).
+# pages fix none): a uint32 array P[8][S][N][4] with S = ceil(K/128); word
+# P[b][s][n][j] holds bit b of the 32 weights W[n][128s + 32j + i], i = 0..31,
+# with weight i = 4u + q at bit position 8q + u (u = 0..7, q = 0..3).  Words
+# whose 32 weights lie past K are zero.
+
+
+def planes_shape(n_rows: int, k_cols: int) -> Tuple[int, int, int, int]:
+    return (8, (k_cols + 127) // 128, n_rows, 4)
 
 
 def pack_weight_planes(w_q: np.ndarray) -> np.ndarray:
-    """Plane-major copy of the INT8 codes: uint32 [8][K/32][N] (layout above)."""
+    """Plane-major copy of the INT8 codes: uint32 [8][ceil(K/128)][N][4] (layout above)."""
     w = np.asarray(w_q, dtype=np.int8)
     n_rows, k_cols = w.shape
     if k_cols % 32:
         raise ValueError("K must be a multiple of 32")
-    u8 = w.view(np.uint8).astype(np.uint64)
-    groups = u8.reshape(n_rows, k_cols // 32, 32)            # [N][G][32]
-    out = np.zeros((8, k_cols // 32, n_rows), dtype=np.uint64)
+    shape = planes_shape(n_rows, k_cols)
+    padded = np.zeros((n_rows, shape[1] * 128), dtype=np.uint64)
+    padded[:, :k_cols] = w.view(np.uint8)
+    groups = padded.reshape(n_rows, shape[1], 4, 32)          # [N][S][j][i]
+    out = np.zeros(shape, dtype=np.uint64)
     for b in range(8):
         bits = (groups >> np.uint64(b)) & np.uint64(1)        # bit b of every weight
-        word = np.zeros((n_rows, k_cols // 32), dtype=np.uint64)
+        word = np.zeros((n_rows, shape[1], 4), dtype=np.uint64)
         for i in range(32):
             u, q = i // 4, i % 4
-            word |= bits[:, :, i] << np.uint64(8 * q + u)
-        out[b] = word.T
+            word |= bits[:, :, :, i] << np.uint64(8 * q + u)
+        out[b] = word.transpose(1, 0, 2)                      # [S][N][j]
     return out.astype(np.uint32)
 
 
-def unpack_weight_planes(planes: np.ndarray, k: int) -> np.ndarray:
+def unpack_weight_planes(planes: np.ndarray, k: int, k_cols: int) -> np.ndarray:
     """Operational weights rebuilt from the planes b = k..7 only: int8 [N][K].
 
     Each retained plane contributes c_b * bit, c_b = 2^b for b < 7 and -2^7
@@ -295,21 +302,21 @@ def unpack_weight_planes(planes: np.ndarray, k: int) -> np.ndarray:
     if not 0 <= k <= 7:
         raise ValueError("k must be in [0, 7]")
     p = np.asarray(planes, dtype=np.uint32).astype(np.int64)
-    _, n_groups, n_rows = p.shape
-    w = np.zeros((n_rows, n_groups, 32), dtype=np.int64)
+    _, n_stages, n_rows, _ = p.shape
+    w = np.zeros((n_rows, n_stages, 4, 32), dtype=np.int64)
     for b in range(k, 8):
         weight = -(1 << 7) if b == 7 else (1 << b)
-        word = p[b].T                                          # [N][G]
+        word = p[b].transpose(1, 0, 2)                         # [N][S][j]
         for i in range(32):
             u, q = i // 4, i % 4
-            w[:, :, i] += weight * ((word >> (8 * q + u)) & 1)
-    return w.reshape(n_rows, n_groups * 32).astype(np.int8)
+            w[:, :, :, i] += weight * ((word >> (8 * q + u)) & 1)
+    return w.reshape(n_rows, n_stages * 128)[:, :k_cols].astype(np.int8)
 
 
 def plane_gemm_i32(x_q: np.ndarray, planes: np.ndarray, k: int) -> np.ndarray:
     """acc = Xq . W_k^T with W_k rebuilt from the retained planes (exact int64 -> int32)."""
     a = np.asarray(x_q, dtype=np.int64)
-    w = unpack_weight_planes(planes, k).astype(np.int64)
+    w = unpack_weight_planes(planes, k, a.shape[1]).astype(np.int64)
     acc = a @ w.T
     if acc.size and np.max(np.abs(acc)) > INT32_MAX:
         raise OverflowError("accumulator exceeds int32")

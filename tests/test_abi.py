@@ -108,6 +108,9 @@ def test_pack_planes_validation(lib, ctx):
     assert p(out=FAKE + 4) == T.EALIGN
     assert p(N=0) == T.OK
     assert lib.tabit_pack_weight_planes(None, FAKE, 32, 32, FAKE, None) == T.EINVAL
+    assert T.weight_planes_bytes(1152, 1152) == 1152 * 1152
+    assert T.weight_planes_bytes(64, 160) == 64 * 256          # K padded to whole 128-code stages
+    assert T.weight_planes_bytes(0, 64) == 0
 
 
 def test_quant_act_validation(lib, ctx):

@@ -247,35 +247,36 @@ def test_accumulator_bound_extreme():
 
 
 # ---------------------------------------------------------------- plane-major storage
-# Layout (this library's encoding): word P[b][g][n] holds bit b of the weights
-# W[n][32g + i]; weight i = 4u + q sits at bit 8q + u.
+# Layout (this library's encoding): word P[b][s][n][j] holds bit b of the
+# weights W[n][128s + 32j + i]; weight i = 4u + q sits at bit 8q + u; words
+# past K are zero.
 
 
 def test_plane_layout_hand_examples():
-    w = np.zeros((2, 64), np.int8)
-    w[0, 0] = 1            # i = 0 (u 0, q 0): plane 0, bit 0
+    w = np.zeros((2, 160), np.int8)   # two K-stages, the second holds one group
+    w[0, 0] = 1            # s 0, j 0, i 0 (u 0, q 0): plane 0, bit 0
     w[0, 5] = -128         # 0x80, i = 5 (u 1, q 1): plane 7, bit 9
     w[0, 31] = 3           # i = 31 (u 7, q 3): planes 0 and 1, bit 31
-    w[1, 32 + 6] = 64      # group 1, i = 6 (u 1, q 2): plane 6, bit 17
-    w[1, 32 + 12] = -1     # 0xFF, group 1, i = 12 (u 3, q 0): every plane, bit 3
+    w[1, 32 + 6] = 64      # j 1, i = 6 (u 1, q 2): plane 6, bit 17
+    w[1, 128 + 12] = -1    # 0xFF, s 1, j 0, i = 12 (u 3, q 0): every plane, bit 3
     P = O.pack_weight_planes(w)
-    assert P.shape == (8, 2, 2) and P.dtype == np.uint32
-    expect = np.zeros((8, 2, 2), np.uint64)
-    expect[0, 0, 0] = 0x00000001 | 0x80000000
-    expect[1, 0, 0] = 0x80000000
-    expect[7, 0, 0] = 0x00000200
-    expect[6, 1, 1] = 0x00020000
+    assert P.shape == (8, 2, 2, 4) and P.dtype == np.uint32
+    expect = np.zeros((8, 2, 2, 4), np.uint64)
+    expect[0, 0, 0, 0] = 0x00000001 | 0x80000000
+    expect[1, 0, 0, 0] = 0x80000000
+    expect[7, 0, 0, 0] = 0x00000200
+    expect[6, 0, 1, 1] = 0x00020000
     for b in range(8):
-        expect[b, 1, 1] |= 0x00000008
-    assert np.array_equal(P.astype(np.uint64), expect)
+        expect[b, 1, 1, 0] |= 0x00000008
+    assert np.array_equal(P.astype(np.uint64), expect)   # words past K (s 1, j 1..3) stay 0
 
 
 def test_plane_round_trip_every_byte_value():
     w = np.arange(-128, 128, dtype=np.int64).astype(np.int8).reshape(1, 256)
-    w = np.concatenate([w, w[:, ::-1]], axis=0)
+    w = np.concatenate([w, w[:, ::-1]], axis=0)[:, :224]           # K = 224: a ragged last stage
     P = O.pack_weight_planes(w)
     for k in range(8):
-        rebuilt = O.unpack_weight_planes(P, k)
+        rebuilt = O.unpack_weight_planes(P, k, 224)
         assert rebuilt.tolist() == [[(int(v) >> k) << k for v in row] for row in w]
 
 
@@ -286,7 +287,7 @@ def test_plane_unpack_reads_only_retained_planes():
     for k in range(1, 8):
         junk = P.copy()
         junk[:k] = rng.integers(0, 2**32, size=junk[:k].shape, dtype=np.uint64).astype(np.uint32)
-        assert np.array_equal(O.unpack_weight_planes(junk, k), O.lsb_truncate(w, k))
+        assert np.array_equal(O.unpack_weight_planes(junk, k, 96), O.lsb_truncate(w, k))
 
 
 @pytest.mark.parametrize("k", range(8))

@@ -64,6 +64,7 @@ _SIGNATURES = {
     "tabit_plane_qgemm": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
                                    _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
     "tabit_plane_config_info": (_c_int, [_c_int, _PINT, _PINT]),
+    "tabit_weight_planes_bytes": (_c_size_t, [_c_int, _c_int]),
 }
 
 
@@ -161,6 +162,10 @@ def mxfp4_config_info(index: int = -1):
     if st != OK:
         raise TabitError(st, "bad config index")
     return bm.value, bn.value
+
+
+def weight_planes_bytes(N: int, K: int) -> int:
+    return int(load().tabit_weight_planes_bytes(N, K))
 
 
 def plane_config_info(index: int = -1):
@@ -287,8 +292,8 @@ class Context:
         M, K = x_q.shape
         if planes:
             _dev(w_q, torch.int32, "w_planes")
-            if w_q.dim() != 3 or w_q.shape[0] != 8 or w_q.shape[1] * 32 != K:
-                raise ValueError("w_planes must be [8][K/32][N] words")
+            if w_q.dim() != 4 or w_q.shape[0] != 8 or w_q.shape[1] != (K + 127) // 128 or w_q.shape[3] != 4:
+                raise ValueError("w_planes must be [8][ceil(K/128)][N][4] words")
             N = w_q.shape[2]
         else:
             _dev(w_q, torch.int8, "w_q")
@@ -322,12 +327,13 @@ class Context:
                              acc, want_y, want_acc)
 
     def pack_weight_planes(self, w_q: torch.Tensor, out: Optional[torch.Tensor] = None):
-        """Plane-major copy of int8 codes [N][K]: int32 tensor [8][K/32][N] (uint32 words)."""
+        """Plane-major copy of int8 codes [N][K]: int32 tensor [8][ceil(K/128)][N][4] (uint32 words)."""
         _dev(w_q, torch.int8, "w_q")
         N, K = w_q.shape
+        shape = (8, (K + 127) // 128, N, 4)
         if out is None:
-            out = torch.empty((8, K // 32, N), dtype=torch.int32, device=w_q.device)
-        _dev(out, torch.int32, "w_planes", (8, K // 32, N))
+            out = torch.empty(shape, dtype=torch.int32, device=w_q.device)
+        _dev(out, torch.int32, "w_planes", shape)
         st = self._lib.tabit_pack_weight_planes(self._h, w_q.data_ptr(), N, K, out.data_ptr(),
                                                 _stream(w_q.device))
         self._check(st)
@@ -371,7 +377,7 @@ class Context:
         wq = weights.get("w_planes") if path == PATH_PLANES else weights.get("w_q")
         wf = weights.get("w_fp4")
         if wq is not None:
-            N = wq.shape[2] if path == PATH_PLANES else wq.shape[0]
+            N = wq.shape[2] if path == PATH_PLANES else wq.shape[0]   # planes: [8][S][N][4]
         else:
             N = wf.shape[0]
         if y is None:

@@ -277,8 +277,9 @@ int tabit_pack_weight_planes(tabit_ctx* ctx, const int8_t* w_q, int N, int K, ui
     return fail(ctx, TABIT_ESHAPE, "N must be a non-negative multiple of 32 (got %d)", N);
   if (K < 32 || K > kMaxK || K % 32 != 0)
     return fail(ctx, TABIT_ESHAPE, "K must be a multiple of 32 in [32, %d] (got %d)", kMaxK, K);
-  if ((size_t)N * (size_t)K > kMaxOperandBytes)
-    return fail(ctx, TABIT_ESHAPE, "N*K = %zu bytes exceeds 2 GiB", (size_t)N * (size_t)K);
+  if (tabit::planes_bytes(N, K) > kMaxOperandBytes)
+    return fail(ctx, TABIT_ESHAPE, "the plane-major copy (%zu bytes) exceeds 2 GiB",
+                tabit::planes_bytes(N, K));
   if (!aligned(w_q, 16) || !aligned(w_planes, 16))
     return fail(ctx, TABIT_EALIGN, "w_q and w_planes must be 16-byte aligned");
   if (N == 0) return TABIT_OK;
@@ -286,9 +287,17 @@ int tabit_pack_weight_planes(tabit_ctx* ctx, const int8_t* w_q, int N, int K, ui
                     "pack_weight_planes launch");
 }
 
+size_t tabit_weight_planes_bytes(int N, int K) {
+  if (N <= 0 || K <= 0) return 0;
+  return tabit::planes_bytes(N, K);
+}
+
 int tabit_plane_qgemm(tabit_ctx* ctx, const int8_t* x_q, const float* x_scale,
                       const uint32_t* w_planes, const float* w_scale, int M, int N, int K,
                       int k_bits, uint16_t* y_bf16, int32_t* acc, void* stream) {
+  if (ctx != nullptr && N > 0 && K > 0 && tabit::planes_bytes(N, K) > kMaxOperandBytes)
+    return fail(ctx, TABIT_ESHAPE, "the plane-major copy (%zu bytes) exceeds 2 GiB",
+                tabit::planes_bytes(N, K));
   return gemm_i8_common(ctx, TABIT_PATH_PLANES, x_q, x_scale, w_planes, w_scale, M, N, K, k_bits,
                         y_bf16, acc, stream);
 }
@@ -389,7 +398,8 @@ int tabit_run_schedule(tabit_ctx* ctx, int first_step, int num_steps, const tabi
       return fail(ctx, TABIT_ESHAPE, "layer %d: N must be a non-negative multiple of 32", l);
     if (L.y_bf16 == nullptr || !aligned(L.y_bf16, 16))
       return fail(ctx, TABIT_EINVAL, "layer %d: missing or misaligned output", l);
-    if ((size_t)L.M * (size_t)L.K > kMaxOperandBytes || (size_t)L.N * (size_t)L.K > kMaxOperandBytes)
+    if ((size_t)L.M * (size_t)L.K > kMaxOperandBytes || (size_t)L.N * (size_t)L.K > kMaxOperandBytes ||
+        (path == TABIT_PATH_PLANES && L.N > 0 && tabit::planes_bytes(L.N, L.K) > kMaxOperandBytes))
       return fail(ctx, TABIT_ESHAPE, "layer %d: operands must stay below 2 GiB", l);
     if (act_ws_bytes < tabit_act_workspace_bytes(L.M, L.K))
       return fail(ctx, TABIT_ESHAPE, "layer %d: act_ws holds %zu bytes, %zu needed", l,

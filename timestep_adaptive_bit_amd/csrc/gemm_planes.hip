@@ -11,17 +11,20 @@
 // The storage is the same size as the INT8 buffer (one copy, no per-step
 // copies).
 //
-// Layout: uint32 P[8][K/32][N].  Word P[b][g][n] holds bit b of the 32 weights
-// W[n][32g + i]; weight i = 4u + q (u = 0..7, q = 0..3) sits at bit 8q + u.
-// Rows n are contiguous for a fixed (plane, group), so a tile's words for one
-// plane and K-stage form a few contiguous runs.
+// Layout: uint32 P[8][S][N][4], S = ceil(K/128).  Word P[b][s][n][j] holds bit
+// b of the 32 weights W[n][128s + 32j + i]; weight i = 4u + q (u = 0..7,
+// q = 0..3) sits at bit 8q + u; words past K are zero.  For one plane and one
+// 128-weight K-stage a row's four words are 16 contiguous bytes and a tile's
+// rows are one contiguous run, so a plane's stage is copied with full 16-byte
+// lanes and read back from LDS with one 16-byte read per lane.
 //
 // GEMM: as the masked INT8 GEMM (K-contiguous int8 activations, LDS stages
 // filled by direct global->LDS buffer loads, v_mfma_i32_32x32x32_i8, fused
 // dequantization to bf16), except that the weight stage holds the retained
 // planes' words and each wave rebuilds its 16-byte weight fragment in
 // registers: for every retained plane b one rotate moves the lane's four
-// weight bits of each output dword to byte bit b, and one and-or merges them.
+// weight bits of each output dword to byte bit b, and one and-or merges them
+// (planes unrolled, dropped planes skipped by a uniform branch).
 // The rebuilt byte is sum_{b >= k} c_b * bit_b = (w >> k) << k exactly
 // (c_7 = -128 is the two's-complement sign bit), so the product equals the
 // masked GEMM bit for bit with one MFMA per K-step.
@@ -37,55 +40,58 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 constexpr int RB = 128;        // K bytes per stage = 4 groups of 32 weights
 constexpr int GPS = RB / 32;   // groups per stage
 
-// Pack: one thread per (group g, row n), rows fastest so the plane words are
-// written coalesced.  Reads the 32 codes W[n][32g .. 32g + 31].
+// Pack: one thread per (stage s, row n, word j), j fastest, so both the 32
+// codes a thread reads and the words the threads write are contiguous.
 __global__ void __launch_bounds__(256)
 pack_planes_kernel(const int8_t* __restrict__ W, int N, int K, uint32_t* __restrict__ P) {
-  const int G = K / 32;
+  const int S = (K + RB - 1) / RB;
   const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (t >= (long long)G * N) return;
-  const int n = (int)(t % N), g = (int)(t / N);
-  const uint4* src = reinterpret_cast<const uint4*>(W + (size_t)n * K + (size_t)g * 32);
-  const uint4 lo = src[0], hi = src[1];
-  const uint32_t d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};   // d[u]: weights 4u..4u+3
-  uint32_t word[8];
+  if (t >= (long long)S * N * GPS) return;
+  const int j = (int)(t % GPS);
+  const int n = (int)((t / GPS) % N);
+  const int st = (int)(t / ((long long)GPS * N));
+  const int k0 = st * RB + 32 * j;
+  uint32_t word[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (k0 < K) {
+    const uint4* src = reinterpret_cast<const uint4*>(W + (size_t)n * K + k0);
+    const uint4 lo = src[0], hi = src[1];
+    const uint32_t d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};   // d[u]: weights 4u..4u+3
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    uint32_t w = 0;
+    for (int b = 0; b < 8; ++b) {
+      uint32_t w = 0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) w |= ((d[u] >> b) & 0x01010101u) << u;   // byte q bit b -> bit 8q + u
-    word[b] = w;
+      for (int u = 0; u < 8; ++u) w |= ((d[u] >> b) & 0x01010101u) << u;   // byte q bit b -> bit 8q + u
+      word[b] = w;
+    }
   }
 #pragma unroll
-  for (int b = 0; b < 8; ++b) P[((size_t)b * G + g) * N + n] = word[b];
+  for (int b = 0; b < 8; ++b) P[(((size_t)b * S + st) * N + n) * GPS + j] = word[b];
 }
 
-// Copy the retained planes of one K-stage into LDS: slot b (8 slots of
-// 16*BN bytes, layout [group][row] words) for b = kbits..7.  Each wave
-// instruction fills 1 KB; lane l copies 4 consecutive rows' words of one
-// group.  Slots below kbits are never fetched (their lanes read out of range
-// and nothing is requested from memory); instructions entirely below kbits
-// are skipped.
+// Copy the retained planes of K-stage `st` into LDS: slot b (8 slots of
+// 16*BN bytes, one 16-byte row of 4 words per tile row) for b = kbits..7.
+// Each wave instruction fills 1 KB (64 rows of one plane, or two planes'
+// slots when BN = 32).  Lanes of dropped planes read out of range, so nothing
+// is requested from memory for them; the instructions are still issued so
+// every wave has the same, compile-time number of copies in flight.
 template <int BN, int NW>
 __device__ __forceinline__ void dma_planes(__amdgpu_buffer_rsrc_t rs, int8_t* lds, int n0, int N,
-                                           int G, int g0, int kbits, int wave, int lane) {
+                                           int S, int st, int kbits, int wave, int lane) {
   constexpr int SLOT = 16 * BN;            // bytes per plane slot
   constexpr int NI = 8 * SLOT / 1024;      // 1 KB instructions per stage
 #pragma unroll
   for (int i = 0; i < (NI + NW - 1) / NW; ++i) {
     const int j = i * NW + wave;
     if (j >= NI) break;
-    if ((1024 * j + 1023) / SLOT < kbits) continue;   // wave-uniform: every slot dropped
     const int byte = 1024 * j + 16 * lane;
-    const int b = byte / SLOT, o = byte % SLOT;
-    const int gi = o / (4 * BN), row = (o % (4 * BN)) / 4;
-    const bool ok = b >= kbits && g0 + gi < G && n0 + row < N;
-    const unsigned off = ok ? (unsigned)((((size_t)b * G + g0 + gi) * N + n0 + row) * 4) : tile::kOOB;
+    const int b = byte / SLOT, row = (byte % SLOT) / 16;
+    const bool ok = b >= kbits && n0 + row < N;
+    const unsigned off = ok ? (unsigned)((((size_t)b * S + st) * N + n0 + row) * 16) : tile::kOOB;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (tile::lds_ptr_t)(lds + 1024 * j), 16, off, 0, 0, 0);
   }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int NST>
 __global__ void __launch_bounds__(WM* WN * 64)
 gemm_planes_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
                    const uint32_t* __restrict__ P, const float* __restrict__ SB, int M, int N,
@@ -98,10 +104,13 @@ gemm_planes_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
   constexpr int SLOT = 16 * BN;
   constexpr int SP_BYTES = 8 * SLOT;
   constexpr int STAGE = SA_BYTES + SP_BYTES;
+  constexpr int NI = SP_BYTES / 1024;                         // plane copies per stage
+  constexpr int DPW = SA_BYTES / 1024 / NW + (NI + NW - 1) / NW;   // copies per wave per stage
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold whole 32x32 blocks");
-  static_assert((8 * SLOT) % 1024 == 0, "plane slots fill whole 1 KB copies");
-  static_assert(2 * STAGE >= BM * BN * 2, "epilogue tile must fit in the LDS stages");
-  __shared__ __attribute__((aligned(1024))) int8_t smem[2 * STAGE];
+  static_assert(SP_BYTES % 1024 == 0 && NI % NW == 0, "plane copies split evenly over the waves");
+  static_assert(NST >= 2 && NST <= 4, "2 to 4 LDS stages");
+  static_assert(NST * STAGE >= BM * BN * 2, "epilogue tile must fit in the LDS stages");
+  __shared__ __attribute__((aligned(1024))) int8_t smem[NST * STAGE];
 
   int tm, tn;
   tile::tile_coords<4>(tiles_m, tiles_n, tm, tn);
@@ -110,9 +119,9 @@ gemm_planes_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave / WN, wn = wave % WN;
   const int rows_a = min(BM, M - m0);
-  const int G = K / 32;
+  const int S = (K + RB - 1) / RB;
   const auto rsa = tile::make_rsrc(A, (unsigned)M * (unsigned)K);
-  const auto rsp = tile::make_rsrc(P, (unsigned)N * (unsigned)K);   // 8 planes x N x K/8 bytes
+  const auto rsp = tile::make_rsrc(P, (unsigned)S * 128u * (unsigned)N);   // 8 planes x S x N x 16 bytes
 
   v16i acc[FM][FN];
 #pragma unroll
@@ -122,19 +131,37 @@ gemm_planes_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
 
   const int ra0 = wm * WTM + (lane & 31), rb0 = wn * WTN + (lane & 31);
   const int khalf = lane >> 5;
-  const int nk = (K + RB - 1) / RB;
+  const int nk = S;
+  // rotate amounts (t - b + 4*khalf) mod 32 for t - b = -7..3: bit 8q + 4*khalf + t
+  // of a word (this lane's weight 4t + q) moves to bit 8q + b
+  int rot[11];
+#pragma unroll
+  for (int d = 0; d < 11; ++d) rot[d] = (d - 7 + 4 * khalf) & 31;
   auto issue = [&](int kt) {
-    int8_t* dst = smem + (kt & 1) * STAGE;
+    int8_t* dst = smem + (kt % NST) * STAGE;
     tile::dma_stage<BM, NW, RB>(rsa, dst, m0, rows_a, K, kt * RB, wave, lane);
-    dma_planes<BN, NW>(rsp, dst + SA_BYTES, n0, N, G, kt * GPS, kbits, wave, lane);
+    dma_planes<BN, NW>(rsp, dst + SA_BYTES, n0, N, S, kt, kbits, wave, lane);
   };
-  issue(0);
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st)
+    if (st < nk) issue(st);
   for (int kt = 0; kt < nk; ++kt) {
-    tile::wait_vmcnt<0>();
+    // stage kt has landed once at most (stages issued after it) x DPW copies are pending
+    const int ahead = min(NST - 2, nk - 1 - kt);
+    if (NST >= 4 && ahead >= 2) tile::wait_vmcnt<(NST >= 4 ? 2 : 0) * DPW>();
+    else if (NST >= 3 && ahead >= 1) tile::wait_vmcnt<(NST >= 3 ? 1 : 0) * DPW>();
+    else tile::wait_vmcnt<0>();
     __syncthreads();   // stage kt visible to all; stage kt-1's buffer is free
-    if (kt + 1 < nk) issue(kt + 1);
-    const int8_t* sa = smem + (kt & 1) * STAGE;
-    const uint32_t* sp = reinterpret_cast<const uint32_t*>(sa + SA_BYTES);
+    if (kt + NST - 1 < nk) issue(kt + NST - 1);
+    const int8_t* sa = smem + (kt % NST) * STAGE;
+    const int8_t* sp = sa + SA_BYTES;
+    // this lane's row of every retained plane: 4 words = the stage's 4 K-steps
+    uint4 pw[FN][8];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int b = 0; b < 8; ++b)
+        if (b >= kbits) pw[j][b] = *reinterpret_cast<const uint4*>(sp + (b * BN + rb0 + j * 32) * 16);
 #pragma unroll
     for (int ks = 0; ks < GPS; ++ks) {
       v4i a[FM], bw[FN];
@@ -145,15 +172,16 @@ gemm_planes_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         uint32_t d0 = 0, d1 = 0, d2 = 0, d3 = 0;
-        for (int b = kbits; b < 8; ++b) {   // kbits is uniform: a scalar loop
-          // word of plane b, group ks, this lane's row; the lane's 16 weights
-          // (4t + q for t, q = 0..3) now sit at bit 8q + t
-          const uint32_t x = sp[(b * GPS + ks) * BN + rb0 + j * 32] >> (4 * khalf);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          if (b < kbits) continue;   // uniform: dropped planes are neither read nor merged
+          const uint4 q = pw[j][b];
+          const uint32_t x = ks == 0 ? q.x : ks == 1 ? q.y : ks == 2 ? q.z : q.w;
           const uint32_t mb = 0x01010101u << b;
-          d0 |= __builtin_amdgcn_alignbit(x, x, (0 - b) & 31) & mb;
-          d1 |= __builtin_amdgcn_alignbit(x, x, (1 - b) & 31) & mb;
-          d2 |= __builtin_amdgcn_alignbit(x, x, (2 - b) & 31) & mb;
-          d3 |= __builtin_amdgcn_alignbit(x, x, (3 - b) & 31) & mb;
+          d0 |= __builtin_amdgcn_alignbit(x, x, rot[0 - b + 7]) & mb;
+          d1 |= __builtin_amdgcn_alignbit(x, x, rot[1 - b + 7]) & mb;
+          d2 |= __builtin_amdgcn_alignbit(x, x, rot[2 - b + 7]) & mb;
+          d3 |= __builtin_amdgcn_alignbit(x, x, rot[3 - b + 7]) & mb;
         }
         bw[j] = v4i{(int)d0, (int)d1, (int)d2, (int)d3};
       }
@@ -202,26 +230,27 @@ gemm_planes_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
 }
 
 struct PlaneCfg {
-  int bm, bn, wm, wn;
+  int bm, bn, wm, wn, nst;
   float rate;   // relative per-CU throughput when busy
 };
-// index, BM, BN, WM, WN, rate
-#define TABIT_PLANE_CONFIGS(X) \
-  X(0, 64, 32, 2, 1, 0.30f)    \
-  X(1, 64, 64, 2, 2, 0.45f)    \
-  X(2, 128, 128, 2, 2, 1.00f)
-#define TABIT_PDESC(I, BM, BN, WM, WN, RATE) {BM, BN, WM, WN, RATE},
+// index, BM, BN, WM, WN, LDS stages, rate
+#define TABIT_PLANE_CONFIGS(X)   \
+  X(0, 64, 32, 1, 1, 4, 0.30f)   \
+  X(1, 64, 64, 1, 2, 2, 0.45f)   \
+  X(2, 128, 64, 1, 2, 2, 0.70f)  \
+  X(3, 128, 128, 2, 2, 2, 1.00f)
+#define TABIT_PDESC(I, BM, BN, WM, WN, NST, RATE) {BM, BN, WM, WN, NST, RATE},
 constexpr PlaneCfg kPlaneCfgs[] = {TABIT_PLANE_CONFIGS(TABIT_PDESC)};
 #undef TABIT_PDESC
 constexpr int kNumPlaneCfgs = sizeof(kPlaneCfgs) / sizeof(kPlaneCfgs[0]);
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int NST>
 hipError_t launch_planes_cfg(const int8_t* xq, const float* sa, const uint32_t* wp,
                              const float* sw, int M, int N, int K, int kbits, uint16_t* y,
                              int32_t* acc, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const dim3 grid(tiles_m * tiles_n), block(WM * WN * 64);
-  auto kern = gemm_planes_kernel<BM, BN, WM, WN>;
+  auto kern = gemm_planes_kernel<BM, BN, WM, WN, NST>;
   if (ev0 != nullptr || ev1 != nullptr)
     hipExtLaunchKernelGGL(kern, grid, block, 0, s, ev0, ev1, 0, xq, sa, wp, sw, M, N, K, kbits, y,
                           acc, tiles_m, tiles_n);
@@ -232,8 +261,10 @@ hipError_t launch_planes_cfg(const int8_t* xq, const float* sa, const uint32_t* 
 
 }  // namespace
 
+size_t planes_bytes(int N, int K) { return (size_t)((K + RB - 1) / RB) * 128u * (size_t)N; }
+
 hipError_t launch_pack_planes(const int8_t* wq, int N, int K, uint32_t* planes, hipStream_t s) {
-  const long long threads = (long long)(K / 32) * N;
+  const long long threads = (long long)((K + RB - 1) / RB) * N * GPS;
   const int grid = (int)((threads + 255) / 256);
   pack_planes_kernel<<<grid, 256, 0, s>>>(wq, N, K, planes);
   return hipGetLastError();
@@ -268,9 +299,10 @@ int plane_config_choose(int M, int N, int K, int num_cus) {
 hipError_t launch_gemm_planes(int cfg, const int8_t* xq, const float* sa, const uint32_t* wp,
                               const float* sw, int M, int N, int K, int kbits, uint16_t* y,
                               int32_t* acc, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-#define TABIT_PCASE(I, BM, BN, WM, WN, RATE) \
-  case I:                                   \
-    return launch_planes_cfg<BM, BN, WM, WN>(xq, sa, wp, sw, M, N, K, kbits, y, acc, stream, ev0, ev1);
+#define TABIT_PCASE(I, BM, BN, WM, WN, NST, RATE) \
+  case I:                                        \
+    return launch_planes_cfg<BM, BN, WM, WN, NST>(xq, sa, wp, sw, M, N, K, kbits, y, acc, stream, \
+                                                  ev0, ev1);
   switch (cfg) {
     TABIT_PLANE_CONFIGS(TABIT_PCASE)
     default: return hipErrorInvalidValue;

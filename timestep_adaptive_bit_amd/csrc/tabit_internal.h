@@ -50,8 +50,9 @@ hipError_t launch_gemm_mxfp4(int cfg, const uint8_t* xq, const uint8_t* xe, cons
                              hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 // ---------------------------------------------------------------- plane-major storage
-// uint32 P[8][K/32][N]: word P[b][g][n] holds bit b of W[n][32g + i] at bit
-// 8*(i % 4) + i / 4.
+// uint32 P[8][ceil(K/128)][N][4]: word P[b][s][n][j] holds bit b of
+// W[n][128s + 32j + i] at bit 8*(i % 4) + i / 4; words past K are zero.
+size_t planes_bytes(int N, int K);
 hipError_t launch_pack_planes(const int8_t* wq, int N, int K, uint32_t* planes, hipStream_t s);
 int plane_config_count();
 GemmConfig plane_config(int index);
