@@ -230,8 +230,7 @@ hipError_t dispatch_int8(int nt, int cpt, int grid, int rows, const uint16_t* x,
     quant_int8_kernel<B, NT_, CPT_><<<grid, NT_, 0, s>>>(x, M, K, rows, scale_div, q, scale); \
     return hipGetLastError();                                                                \
   }
-  TABIT_Q(256, 1) TABIT_Q(256, 2) TABIT_Q(256, 4) TABIT_Q(512, 2) TABIT_Q(512, 4)
-  TABIT_Q(1024, 2)
+  TABIT_Q(256, 1) TABIT_Q(512, 1) TABIT_Q(1024, 1) TABIT_Q(1024, 2)
 #undef TABIT_Q
   return hipErrorInvalidValue;
 }
@@ -242,27 +241,16 @@ hipError_t launch_quant_int8(const uint16_t* x, int M, int K, int had_block, flo
                              int8_t* q, float* scale, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
   const int cr = K / 16;
-  // Workgroup shape (threads x chunks per thread): the smallest that keeps >= 90%
-  // of its 16-element slots busy with whole rows, otherwise the best utilization.
-  // At most 4 chunks (64 fp32 values) per thread keeps occupancy for latency hiding.
-  static const int kShapes[][2] = {{256, 1}, {256, 2}, {256, 4}, {512, 2}, {512, 4}, {1024, 2}};
-  int nt = 1024, cpt = 2;
-  double best_util = -1.0;
-  for (const auto& sh : kShapes) {
-    const int slots = sh[0] * sh[1];
-    if (slots < cr) continue;
-    const double util = (double)((slots / cr) * cr) / slots;
-    if (util >= 0.9) {
-      nt = sh[0];
-      cpt = sh[1];
-      break;
-    }
-    if (util > best_util) {
-      best_util = util;
-      nt = sh[0];
-      cpt = sh[1];
-    }
-  }
+  // Workgroup shape: one 16-element chunk per thread and as few rows per
+  // workgroup as fill it (256 threads for rows of up to 256 chunks, else the
+  // next power of two; two chunks per thread past 1024 chunks).  Small
+  // workgroups with few registers outnumber the resident slots, so reads of
+  // late workgroups overlap the stores of early ones; on MI355X this beat
+  // fuller multi-row, multi-chunk shapes by 7-32% at the workloads' sizes.
+  int nt = 1024, cpt = 1;
+  if (cr <= 256) nt = 256;
+  else if (cr <= 512) nt = 512;
+  else if (cr > 1024) cpt = 2;
   const int rows = (nt * cpt) / cr;
   const int grid = (M + rows - 1) / rows;
   switch (had_block) {
@@ -276,7 +264,7 @@ hipError_t launch_quant_int8(const uint16_t* x, int M, int K, int had_block, flo
 hipError_t launch_quant_mx(const uint16_t* x, int M, int K, int had_block, uint8_t* q_fp4,
                            uint8_t* e8m0, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
-  constexpr int CPT = 4;
+  constexpr int CPT = 1;   // one chunk per thread: 7-36% faster than 2-8 on MI355X
   const long long nchunks = (long long)M * K / 16;
   const long long per_wg = (long long)QT * CPT;
   const int grid = (int)((nchunks + per_wg - 1) / per_wg);
