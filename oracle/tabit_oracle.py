@@ -434,6 +434,69 @@ def mxfp4_gemm(x_fp4, x_e8m0, w_fp4, w_e8m0, out_scale: float) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# DMPQ: the online INT8 / 4-bit selector (6Bit-Diffusion section 2A)
+# --------------------------------------------------------------------------
+#
+# The page: the input-output relative L1 difference of a block at step t-1
+# predicts, linearly, how sensitive that block's inner linear layers are to
+# quantization at step t; unstable (high-variation) blocks keep INT8, stable
+# ones go to 4 bits.  It prints neither the predictor's coefficients nor the
+# threshold, so a linear predictor compared with a threshold is a threshold
+# theta_l on Gamma per layer: INT8 when Gamma > theta_l, else 4-bit.
+#
+# Gamma = sum |out - in| / sum |in| over the block's hidden states.  Its
+# summation order is part of this library's contract so that the device
+# decision can be reproduced exactly: terms in fp64 (|in| exact, out - in one
+# fp64 subtraction), each 16-element chunk summed left to right, the chunk
+# sums of a row by a pairwise tree, the row sums by a pairwise tree (trees
+# padded with zeros to a power of two; x + 0 = x, so padding changes nothing).
+
+
+def _pairwise_tree(v: np.ndarray) -> np.ndarray:
+    """Pairwise sums along the last axis: ((v0 + v1) + (v2 + v3)) + ..., zero-padded."""
+    v = np.asarray(v, dtype=np.float64)
+    n = v.shape[-1]
+    p = 1
+    while p < n:
+        p *= 2
+    if p != n:
+        pad = np.zeros(v.shape[:-1] + (p - n,), dtype=np.float64)
+        v = np.concatenate([v, pad], axis=-1)
+    while v.shape[-1] > 1:
+        v = v[..., 0::2] + v[..., 1::2]
+    return v[..., 0]
+
+
+def dmpq_gamma(x_in_bits: np.ndarray, x_out_bits: np.ndarray) -> Tuple[float, float, float]:
+    """(Gamma, sum |out - in|, sum |in|) of one block, in the order stated above.
+
+    Gamma = 0 when both sums are 0, +inf when only sum |in| is 0.
+    """
+    a = bf16_to_f32(np.asarray(x_in_bits)).astype(np.float64)
+    b = bf16_to_f32(np.asarray(x_out_bits)).astype(np.float64)
+    if a.shape != b.shape or a.ndim != 2 or a.shape[1] % 16:
+        raise ValueError("in and out must be [M][H] with H % 16 == 0")
+    m_rows, h = a.shape
+    d = np.abs(b - a).reshape(m_rows, h // 16, 16)
+    s = np.abs(a).reshape(m_rows, h // 16, 16)
+    dc, sc = d[:, :, 0].copy(), s[:, :, 0].copy()
+    for e in range(1, 16):                  # left to right inside a chunk
+        dc = dc + d[:, :, e]
+        sc = sc + s[:, :, e]
+    num = float(_pairwise_tree(_pairwise_tree(dc)))
+    den = float(_pairwise_tree(_pairwise_tree(sc)))
+    if den == 0.0:
+        return (0.0 if num == 0.0 else float("inf")), num, den
+    return num / den, num, den
+
+
+def dmpq_select(gamma: float, thetas) -> np.ndarray:
+    """fmt per layer of the block for the next step: INT8 (0) if Gamma > theta_l, else MXFP4 (1)."""
+    th = np.asarray(thetas, dtype=np.float32).astype(np.float64)
+    return np.where(gamma > th, 0, 1).astype(np.uint8)
+
+
+# --------------------------------------------------------------------------
 # O12: the per-(step, layer) schedule and the full linear at one step
 # --------------------------------------------------------------------------
 

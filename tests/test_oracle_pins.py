@@ -298,6 +298,60 @@ def test_plane_gemm_brute_force(k):
     assert O.plane_gemm_i32(X, O.pack_weight_planes(Wq), k).tolist() == _brute_gemm(X, Wt)
 
 
+# ---------------------------------------------------------------- DMPQ selector
+def _bf(vals):
+    return S.bf16_bits(torch.tensor(vals, dtype=torch.float32).to(torch.bfloat16))
+
+
+def test_dmpq_gamma_closed_forms():
+    x = S.gen_activation(5, 96, seed=3)
+    xb = S.bf16_bits(x)
+    two = S.bf16_bits((x.float() * 2).to(torch.bfloat16))            # exact doubling
+    zero = np.zeros_like(xb)
+    assert O.dmpq_gamma(xb, xb)[0] == 0.0
+    assert O.dmpq_gamma(xb, two)[0] == 1.0
+    assert O.dmpq_gamma(xb, zero)[0] == 1.0
+    assert O.dmpq_gamma(zero, xb)[0] == float("inf")
+    assert O.dmpq_gamma(zero, zero)[0] == 0.0
+
+
+def test_dmpq_gamma_exact_on_small_integers():
+    rng = np.random.default_rng(4)
+    a = rng.integers(-50, 51, size=(7, 48)).astype(np.float32)
+    b = rng.integers(-50, 51, size=(7, 48)).astype(np.float32)
+    g, num, den = O.dmpq_gamma(_bf(a), _bf(b))
+    exact_num = sum(abs(int(p) - int(q)) for p, q in zip(b.ravel(), a.ravel()))
+    exact_den = sum(abs(int(q)) for q in a.ravel())
+    assert num == exact_num and den == exact_den                     # every partial is an exact integer
+    assert g == float(Fraction(exact_num, exact_den))                # one correctly rounded division
+
+
+def test_dmpq_summation_order_golden():
+    """Chunk sums 2^53, 1, 1, 2 (zero-padded chunks): the pairwise tree gives
+    (2^53 + 1) + (1 + 2) = 2^53 + 4 (2^53 + 1 rounds to 2^53; 2^53 + 3 ties to
+    the even 2^53 + 4), a left-to-right sum over the row would give 2^53 + 2."""
+    row = np.zeros((1, 64), np.float32)
+    row[0, 0], row[0, 16], row[0, 32], row[0, 48] = 2.0 ** 53, 1.0, 1.0, 2.0
+    _, num, den = O.dmpq_gamma(_bf(np.zeros_like(row)), _bf(row))
+    assert num == 2.0 ** 53 + 4 and den == 0.0
+    seq = 0.0
+    for v in row.ravel().astype(np.float64):
+        seq += v
+    assert seq == 2.0 ** 53 + 2                                      # the order matters here
+    # rows combine by the same tree: rows 2^53, 1, 1, 2
+    rows = np.zeros((4, 16), np.float32)
+    rows[:, 0] = [2.0 ** 53, 1.0, 1.0, 2.0]
+    assert O.dmpq_gamma(_bf(np.zeros_like(rows)), _bf(rows))[1] == 2.0 ** 53 + 4
+
+
+def test_dmpq_select_threshold_rule():
+    th = np.array([0.25, 0.5, 0.75], np.float32)
+    assert O.dmpq_select(0.5, th).tolist() == [0, 1, 1]              # equal to theta -> 4-bit
+    assert O.dmpq_select(0.0, th).tolist() == [1, 1, 1]
+    assert O.dmpq_select(float("inf"), th).tolist() == [0, 0, 0]
+    assert O.dmpq_select(np.nextafter(0.5, 1.0), th).tolist() == [0, 0, 1]
+
+
 # ---------------------------------------------------------------- epilogue
 def test_bf16_rne_matches_torch_cast():
     rng = np.random.default_rng(5)
