@@ -236,6 +236,49 @@ int tabit_scheduled_linear(tabit_ctx* ctx, int step, int layer, int path,
                            const uint8_t* w_fp4, const uint8_t* w_e8m0,
                            void* act_ws, size_t act_ws_bytes, uint16_t* y_bf16, void* stream);
 
+/*
+ * DMPQ online format selection (6Bit-Diffusion section 2A): the relative L1
+ * input-output change of a transformer block at step t-1 predicts, linearly,
+ * the quantization sensitivity of its linear layers at step t; unstable
+ * blocks keep INT8, stable ones go to 4 bits.  The page gives no predictor
+ * coefficients or threshold, so the rule is a per-layer threshold:
+ *   Gamma  = sum |x_out - x_in| / sum |x_in|   (0 if both sums are 0, +inf if
+ *            only sum |x_in| is)
+ *   fmt[l] = Gamma > theta[l] ? TABIT_FMT_INT8 : TABIT_FMT_MXFP4
+ * The sums run in a fixed fp64 order (terms |x_in| and |x_out - x_in| in fp64;
+ * each 16-element chunk left to right; chunk sums of a row, then row sums, by
+ * pairwise trees zero-padded to a power of two), so the decision is
+ * reproducible bit for bit.  Written on the device: a captured step needs no
+ * host round trip; the next step's tabit_gated_linear calls read fmt.
+ *   x_in, x_out  device bf16 [M][H] (block input and output at step t-1),
+ *                H % 16 == 0, 16 <= H <= 32768, 16-byte aligned.
+ *   theta        device fp32 [n_layers]; fmt device uint8 [n_layers] output
+ *                (both may be NULL when n_layers == 0).
+ *   gamma        device fp64 [1] output (may be NULL if n_layers > 0).
+ *   ws           device workspace of tabit_dmpq_workspace_bytes(M) bytes.
+ */
+size_t tabit_dmpq_workspace_bytes(int M);
+int tabit_dmpq_select(tabit_ctx* ctx, const uint16_t* x_in, const uint16_t* x_out, int M, int H,
+                      const float* theta, int n_layers, uint8_t* fmt, double* gamma, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/*
+ * One linear whose format is read on the device (6Bit-Diffusion section 2A
+ * with the table from tabit_dmpq_select): enqueues the INT8 branch (quantizer
+ * + masked GEMM with k_bits, or the plane-major GEMM when path =
+ * TABIT_PATH_PLANES and w_q holds the plane words) and the MXFP4 branch
+ * (MX quantizer + MXFP4 GEMM with out_scale 1/max(had_block, 1)); every kernel
+ * first reads *fmt_dev and returns at once unless it is its own format, so
+ * exactly one branch does work and no host synchronization is needed.
+ *   fmt_dev  device uint8 (TABIT_FMT_*).  Both weight formats are required;
+ *   had_block in {0, 32}.  Other arguments as tabit_scheduled_linear.
+ */
+int tabit_gated_linear(tabit_ctx* ctx, const uint8_t* fmt_dev, int k_bits, int path,
+                       const uint16_t* x_bf16, int M, int N, int K, int had_block,
+                       const void* w_q, const float* w_scale, const uint8_t* w_fp4,
+                       const uint8_t* w_e8m0, void* act_ws, size_t act_ws_bytes, uint16_t* y_bf16,
+                       void* stream);
+
 /* One linear layer of a stack, for tabit_run_schedule. */
 typedef struct tabit_layer {
   int M, N, K;               /* tokens, output and input features                     */

@@ -113,6 +113,36 @@ def test_pack_planes_validation(lib, ctx):
     assert T.weight_planes_bytes(0, 64) == 0
 
 
+def test_dmpq_validation(lib, ctx):
+    def d(M=4, H=64, th=FAKE, n=2, fmt=FAKE, g=FAKE, ws=FAKE, nb=1 << 20, xi=FAKE):
+        return lib.tabit_dmpq_select(ctx.handle, xi, FAKE, M, H, th, n, fmt, g, ws, nb, None)
+    assert d(xi=None) == T.EINVAL
+    assert d(th=None) == T.EINVAL                      # n_layers > 0 needs theta and fmt
+    assert d(n=0, g=None) == T.EINVAL                  # nothing to write
+    assert d(n=-1) == T.EINVAL
+    assert d(M=0) == T.ESHAPE
+    assert d(H=40) == T.ESHAPE
+    assert d(H=65536) == T.ESHAPE
+    assert d(nb=16) == T.ESHAPE                        # workspace below 16 bytes per row
+    assert d(g=FAKE + 4) == T.EALIGN
+    assert T.dmpq_workspace_bytes(100) == 1600
+
+
+def test_gated_linear_validation(lib, ctx):
+    def g(fmt=FAKE, k=0, path=0, M=8, N=32, K=64, b=0, wq=FAKE, wf=FAKE, ws=FAKE, nb=1 << 20):
+        return lib.tabit_gated_linear(ctx.handle, fmt, k, path, FAKE, M, N, K, b, wq, FAKE, wf, FAKE,
+                                      ws, nb, FAKE, None)
+    assert g(fmt=None) == T.EINVAL
+    assert g(wf=None) == T.EINVAL                      # both weight formats are required
+    assert g(path=1) == T.EINVAL
+    assert g(k=8) == T.ERANGE
+    assert g(b=64) == T.ERANGE                         # the MXFP4 branch needs b in {0, 32}
+    assert g(N=48) == T.ESHAPE
+    assert g(nb=8) == T.ESHAPE
+    assert g(ws=MISALIGNED) == T.EALIGN
+    assert g(M=0) == T.OK
+
+
 def test_quant_act_validation(lib, ctx):
     def q(M=4, K=64, b=0, fmt=0, x=FAKE, xq=FAKE, xs=FAKE):
         return lib.tabit_hadamard_quant_act(ctx.handle, x, M, K, b, fmt, xq, xs, None)

@@ -65,6 +65,12 @@ _SIGNATURES = {
                                    _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
     "tabit_plane_config_info": (_c_int, [_c_int, _PINT, _PINT]),
     "tabit_weight_planes_bytes": (_c_size_t, [_c_int, _c_int]),
+    "tabit_dmpq_workspace_bytes": (_c_size_t, [_c_int]),
+    "tabit_dmpq_select": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_void_p,
+                                   _c_int, _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
+    "tabit_gated_linear": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_void_p, _c_int, _c_int,
+                                    _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                    _c_void_p, _c_size_t, _c_void_p, _c_void_p]),
 }
 
 
@@ -162,6 +168,10 @@ def mxfp4_config_info(index: int = -1):
     if st != OK:
         raise TabitError(st, "bad config index")
     return bm.value, bn.value
+
+
+def dmpq_workspace_bytes(M: int) -> int:
+    return int(load().tabit_dmpq_workspace_bytes(M))
 
 
 def weight_planes_bytes(N: int, K: int) -> int:
@@ -388,6 +398,46 @@ class Context:
             _ptr(wq), _ptr(weights.get("w_scale")), _ptr(wf), _ptr(weights.get("w_e8m0")),
             act_ws.data_ptr(), act_ws.numel() * act_ws.element_size(), y.data_ptr(),
             _stream(x.device))
+        self._check(st)
+        return y
+
+    def dmpq_select(self, x_in: torch.Tensor, x_out: torch.Tensor, theta: Optional[torch.Tensor],
+                    fmt: Optional[torch.Tensor], gamma: Optional[torch.Tensor],
+                    ws: Optional[torch.Tensor] = None):
+        """Gamma of a block (device fp64) and fmt[l] = Gamma > theta[l] ? INT8 : MXFP4 (device)."""
+        _dev(x_in, torch.bfloat16, "x_in")
+        M, H = x_in.shape
+        _dev(x_out, torch.bfloat16, "x_out", (M, H))
+        n = 0
+        if theta is not None:
+            n = theta.numel()
+            _dev(theta, torch.float32, "theta", (n,))
+            _dev(fmt, torch.uint8, "fmt", (n,))
+        if gamma is not None:
+            _dev(gamma, torch.float64, "gamma", (1,))
+        if ws is None:
+            ws = torch.empty(dmpq_workspace_bytes(M), dtype=torch.uint8, device=x_in.device)
+        st = self._lib.tabit_dmpq_select(self._h, x_in.data_ptr(), x_out.data_ptr(), M, H,
+                                         _ptr(theta), n, _ptr(fmt), _ptr(gamma), ws.data_ptr(),
+                                         ws.numel() * ws.element_size(), _stream(x_in.device))
+        self._check(st)
+
+    def gated_linear(self, fmt_dev: torch.Tensor, k_bits: int, x: torch.Tensor, weights: dict,
+                     had_block: int, act_ws: torch.Tensor, y: Optional[torch.Tensor] = None,
+                     path: int = PATH_MASKED):
+        """One linear whose format is the device byte fmt_dev (both weight formats needed)."""
+        _dev(x, torch.bfloat16, "x")
+        M, K = x.shape
+        wq = weights["w_planes"] if path == PATH_PLANES else weights["w_q"]
+        N = wq.shape[2] if path == PATH_PLANES else wq.shape[0]
+        if y is None:
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+        _dev(y, torch.bfloat16, "y", (M, N))
+        st = self._lib.tabit_gated_linear(
+            self._h, fmt_dev.data_ptr(), k_bits, path, x.data_ptr(), M, N, K, had_block,
+            wq.data_ptr(), weights["w_scale"].data_ptr(), weights["w_fp4"].data_ptr(),
+            weights["w_e8m0"].data_ptr(), act_ws.data_ptr(), act_ws.numel() * act_ws.element_size(),
+            y.data_ptr(), _stream(x.device))
         self._check(st)
         return y
 

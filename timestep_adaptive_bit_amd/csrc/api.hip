@@ -75,20 +75,21 @@ int check_gemm(tabit_ctx* ctx, const void* xq, const void* xs, const void* wq, c
 hipError_t launch_int8_family(const tabit_ctx* ctx, int path, const int8_t* xq, const float* sa,
                               const void* w, const float* sw, int M, int N, int K, int k,
                               uint16_t* y, int32_t* acc, hipStream_t s, int num_cus,
-                              hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
+                              hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr,
+                              const uint8_t* gate = nullptr) {
   if (path == TABIT_PATH_PLANES) {
     int cfg = ctx->force_plane_cfg;
     if (cfg < 0) cfg = ctx->tuned_cfg(TABIT_PATH_PLANES, M, N, K);
     if (cfg < 0) cfg = tabit::plane_config_choose(M, N, K, num_cus);
     return tabit::launch_gemm_planes(cfg, xq, sa, static_cast<const uint32_t*>(w), sw, M, N, K, k,
-                                     y, acc, s, e0, e1);
+                                     y, acc, s, e0, e1, gate);
   }
   const bool bitserial = path == TABIT_PATH_BITSERIAL;
   int cfg = ctx->force_gemm_cfg;
   if (cfg < 0) cfg = ctx->tuned_cfg(bitserial ? 1 : 0, M, N, K);
   if (cfg < 0) cfg = tabit::gemm_config_choose(M, N, K, num_cus);
   return tabit::launch_gemm_i8(cfg, bitserial, xq, sa, static_cast<const int8_t*>(w), sw, M, N, K,
-                               k, y, acc, s, e0, e1);
+                               k, y, acc, s, e0, e1, gate);
 }
 
 bool valid_int8_path(int path) {
@@ -371,6 +372,88 @@ int tabit_scheduled_linear(tabit_ctx* ctx, int step, int layer, int path, const 
   if (st != TABIT_OK) return st;
   return tabit_mxfp4_qgemm(ctx, xf, xe, w_fp4, w_e8m0, M, N, K,
                            1.0f / (float)(had_block > 0 ? had_block : 1), y_bf16, nullptr, stream);
+}
+
+size_t tabit_dmpq_workspace_bytes(int M) { return tabit::dmpq_workspace_bytes(M); }
+
+int tabit_dmpq_select(tabit_ctx* ctx, const uint16_t* x_in, const uint16_t* x_out, int M, int H,
+                      const float* theta, int n_layers, uint8_t* fmt, double* gamma, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (ctx == nullptr) return TABIT_EINVAL;
+  if (x_in == nullptr || x_out == nullptr || ws == nullptr) return fail(ctx, TABIT_EINVAL, "null pointer");
+  if (n_layers < 0) return fail(ctx, TABIT_EINVAL, "n_layers must be >= 0 (got %d)", n_layers);
+  if (n_layers > 0 && (theta == nullptr || fmt == nullptr))
+    return fail(ctx, TABIT_EINVAL, "theta and fmt are required when n_layers > 0");
+  if (n_layers == 0 && gamma == nullptr) return fail(ctx, TABIT_EINVAL, "no output requested");
+  if (M < 1) return fail(ctx, TABIT_ESHAPE, "M must be >= 1 (got %d)", M);
+  if (H < 16 || H > kMaxK || H % 16 != 0)
+    return fail(ctx, TABIT_ESHAPE, "H must be a multiple of 16 in [16, %d] (got %d)", kMaxK, H);
+  if ((size_t)M * (size_t)H * 2 > kMaxOperandBytes)
+    return fail(ctx, TABIT_ESHAPE, "hidden states must stay below 2 GiB");
+  if (!aligned(x_in, 16) || !aligned(x_out, 16) || !aligned(ws, 16) ||
+      (theta && !aligned(theta, 4)) || (gamma && !aligned(gamma, 8)))
+    return fail(ctx, TABIT_EALIGN, "misaligned pointer");
+  if (ws_bytes < tabit::dmpq_workspace_bytes(M))
+    return fail(ctx, TABIT_ESHAPE, "ws holds %zu bytes, %zu needed", ws_bytes,
+                tabit::dmpq_workspace_bytes(M));
+  return hip_status(ctx,
+                    tabit::launch_dmpq_select(x_in, x_out, M, H, static_cast<double*>(ws), theta,
+                                              n_layers, fmt, gamma, static_cast<hipStream_t>(stream)),
+                    "dmpq_select launch");
+}
+
+int tabit_gated_linear(tabit_ctx* ctx, const uint8_t* fmt_dev, int k_bits, int path,
+                       const uint16_t* x_bf16, int M, int N, int K, int had_block,
+                       const void* w_q, const float* w_scale, const uint8_t* w_fp4,
+                       const uint8_t* w_e8m0, void* act_ws, size_t act_ws_bytes, uint16_t* y_bf16,
+                       void* stream) {
+  if (ctx == nullptr) return TABIT_EINVAL;
+  if (fmt_dev == nullptr || x_bf16 == nullptr || y_bf16 == nullptr || act_ws == nullptr ||
+      w_q == nullptr || w_scale == nullptr || w_fp4 == nullptr || w_e8m0 == nullptr)
+    return fail(ctx, TABIT_EINVAL, "null pointer (both weight formats are required)");
+  if (path != TABIT_PATH_MASKED && path != TABIT_PATH_PLANES)
+    return fail(ctx, TABIT_EINVAL, "gated linear takes the masked or plane-major path (got %d)", path);
+  if (k_bits < 0 || k_bits > 7) return fail(ctx, TABIT_ERANGE, "k_bits must be in [0, 7] (got %d)", k_bits);
+  int st = check_k_shape(ctx, M, K, had_block);
+  if (st != TABIT_OK) return st;
+  if (had_block != 0 && had_block != 32)
+    return fail(ctx, TABIT_ERANGE, "MXFP4 takes had_block 0 or 32 (got %d)", had_block);
+  if (N < 0 || N % 32 != 0)
+    return fail(ctx, TABIT_ESHAPE, "N must be a non-negative multiple of 32 (got %d)", N);
+  if ((size_t)M * (size_t)K > kMaxOperandBytes || (size_t)N * (size_t)K > kMaxOperandBytes ||
+      (path == TABIT_PATH_PLANES && N > 0 && tabit::planes_bytes(N, K) > kMaxOperandBytes))
+    return fail(ctx, TABIT_ESHAPE, "operands must stay below 2 GiB");
+  if (!aligned(x_bf16, 16) || !aligned(y_bf16, 16) || !aligned(act_ws, 16) || !aligned(w_q, 16) ||
+      !aligned(w_fp4, 16) || !aligned(w_scale, 4))
+    return fail(ctx, TABIT_EALIGN, "misaligned pointer");
+  if (act_ws_bytes < tabit_act_workspace_bytes(M, K))
+    return fail(ctx, TABIT_ESHAPE, "act_ws holds %zu bytes, %zu needed", act_ws_bytes,
+                tabit_act_workspace_bytes(M, K));
+  if (M == 0 || N == 0) return TABIT_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(act_ws);
+  const size_t mk = (size_t)M * (size_t)K;
+  const int num_cus = tabit::device_num_cus();
+  // INT8 branch: runs when *fmt_dev == TABIT_FMT_INT8
+  int8_t* xq = reinterpret_cast<int8_t*>(ws);
+  float* sa = reinterpret_cast<float*>(ws + align256(mk));
+  hipError_t e = tabit::launch_quant_int8(x_bf16, M, K, had_block, 1.0f, xq, sa, s, fmt_dev);
+  if (e != hipSuccess) return hip_status(ctx, e, "gated quantizer launch");
+  e = launch_int8_family(ctx, path, xq, sa, w_q, w_scale, M, N, K, k_bits, y_bf16, nullptr, s,
+                         num_cus, nullptr, nullptr, fmt_dev);
+  if (e != hipSuccess) return hip_status(ctx, e, "gated GEMM launch");
+  // MXFP4 branch: runs when *fmt_dev == TABIT_FMT_MXFP4 (same workspace; only one branch runs)
+  uint8_t* xf = ws;
+  uint8_t* xe = ws + align256(mk / 2);
+  e = tabit::launch_quant_mx(x_bf16, M, K, had_block, xf, xe, s, fmt_dev);
+  if (e != hipSuccess) return hip_status(ctx, e, "gated MX quantizer launch");
+  int cfg = ctx->force_mx_cfg;
+  if (cfg < 0) cfg = ctx->tuned_cfg(2, M, N, K);
+  if (cfg < 0) cfg = tabit::mx_config_choose(M, N, K, num_cus);
+  e = tabit::launch_gemm_mxfp4(cfg, xf, xe, w_fp4, w_e8m0, M, N, K,
+                               1.0f / (float)(had_block > 0 ? had_block : 1), y_bf16, nullptr, s,
+                               nullptr, nullptr, fmt_dev);
+  return hip_status(ctx, e, "gated MXFP4 GEMM launch");
 }
 
 int tabit_run_schedule(tabit_ctx* ctx, int first_step, int num_steps, const tabit_layer* layers,

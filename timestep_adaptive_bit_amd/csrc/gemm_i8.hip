@@ -41,7 +41,8 @@ __global__ void __launch_bounds__(WM* WN * 64)
 gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
                const int8_t* __restrict__ B, const float* __restrict__ SB, int M, int N, int K,
                int kbits, uint16_t* __restrict__ Y, int32_t* __restrict__ ACC, int tiles_m,
-               int tiles_n) {
+               int tiles_n, const uint8_t* __restrict__ gate) {
+  if (gate != nullptr && *gate != 0) return;   // device-selected format is not INT8
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;   // 32 x 32 MFMA blocks per wave
@@ -203,16 +204,16 @@ constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 template <int BM, int BN, int WM, int WN, int RB, int NST>
 hipError_t launch_cfg(bool bitserial, const int8_t* xq, const float* sa, const int8_t* wq,
                       const float* sw, int M, int N, int K, int kbits, uint16_t* y, int32_t* acc,
-                      hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+                      hipStream_t s, hipEvent_t ev0, hipEvent_t ev1, const uint8_t* gate) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const dim3 grid(tiles_m * tiles_n), block(WM * WN * 64);
   auto kern = bitserial ? gemm_i8_kernel<BM, BN, WM, WN, RB, NST, true>
                         : gemm_i8_kernel<BM, BN, WM, WN, RB, NST, false>;
   if (ev0 != nullptr || ev1 != nullptr)   // timestamps of this dispatch itself
     hipExtLaunchKernelGGL(kern, grid, block, 0, s, ev0, ev1, 0, xq, sa, wq, sw, M, N, K, kbits, y,
-                          acc, tiles_m, tiles_n);
+                          acc, tiles_m, tiles_n, gate);
   else
-    kern<<<grid, block, 0, s>>>(xq, sa, wq, sw, M, N, K, kbits, y, acc, tiles_m, tiles_n);
+    kern<<<grid, block, 0, s>>>(xq, sa, wq, sw, M, N, K, kbits, y, acc, tiles_m, tiles_n, gate);
   return hipGetLastError();
 }
 
@@ -248,11 +249,11 @@ int gemm_config_choose(int M, int N, int K, int num_cus) {
 hipError_t launch_gemm_i8(int cfg, bool bitserial, const int8_t* xq, const float* sa,
                           const int8_t* wq, const float* sw, int M, int N, int K, int kbits,
                           uint16_t* y, int32_t* acc, hipStream_t stream, hipEvent_t ev0,
-                          hipEvent_t ev1) {
+                          hipEvent_t ev1, const uint8_t* gate) {
 #define TABIT_CASE(I, BM, BN, WM, WN, RB, NST, SLOTS, RATE) \
   case I:                                            \
     return launch_cfg<BM, BN, WM, WN, RB, NST>(bitserial, xq, sa, wq, sw, M, N, K, kbits, y, acc, \
-                                               stream, ev0, ev1);
+                                               stream, ev0, ev1, gate);
   switch (cfg) {
     TABIT_I8_CONFIGS(TABIT_CASE)
     default: return hipErrorInvalidValue;

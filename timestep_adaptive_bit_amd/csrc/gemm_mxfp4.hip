@@ -34,7 +34,8 @@ __global__ void __launch_bounds__(WM* WN * 64)
 gemm_mxfp4_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ AE,
                   const uint8_t* __restrict__ B, const uint8_t* __restrict__ BE, int M, int N,
                   int K, float out_scale, uint16_t* __restrict__ Y, float* __restrict__ ACC,
-                  int tiles_m, int tiles_n) {
+                  int tiles_m, int tiles_n, const uint8_t* __restrict__ gate) {
+  if (gate != nullptr && *gate != 1) return;   // device-selected format is not MXFP4
   constexpr int NT = WM * WN * 64, NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -187,15 +188,15 @@ constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_cfg(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq, const uint8_t* we,
                       int M, int N, int K, float out_scale, uint16_t* y, float* acc,
-                      hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+                      hipStream_t s, hipEvent_t ev0, hipEvent_t ev1, const uint8_t* gate) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const dim3 grid(tiles_m * tiles_n), block(WM * WN * 64);
   if (ev0 != nullptr || ev1 != nullptr)   // timestamps of this dispatch itself
     hipExtLaunchKernelGGL(gemm_mxfp4_kernel<BM, BN, WM, WN>, grid, block, 0, s, ev0, ev1, 0, xq, xe,
-                          wq, we, M, N, K, out_scale, y, acc, tiles_m, tiles_n);
+                          wq, we, M, N, K, out_scale, y, acc, tiles_m, tiles_n, gate);
   else
     gemm_mxfp4_kernel<BM, BN, WM, WN><<<grid, block, 0, s>>>(xq, xe, wq, we, M, N, K, out_scale, y,
-                                                             acc, tiles_m, tiles_n);
+                                                             acc, tiles_m, tiles_n, gate);
   return hipGetLastError();
 }
 
@@ -226,11 +227,12 @@ int mx_config_choose(int M, int N, int K, int num_cus) {
 
 hipError_t launch_gemm_mxfp4(int cfg, const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
                              const uint8_t* we, int M, int N, int K, float out_scale, uint16_t* y,
-                             float* acc, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+                             float* acc, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1,
+                             const uint8_t* gate) {
 #define TABIT_CASE(I, BM, BN, WM, WN, SLOTS, RATE) \
   case I:                                           \
     return launch_cfg<BM, BN, WM, WN>(xq, xe, wq, we, M, N, K, out_scale, y, acc, stream, \
-                                      ev0, ev1);
+                                      ev0, ev1, gate);
   switch (cfg) {
     TABIT_MX_CONFIGS(TABIT_CASE)
     default: return hipErrorInvalidValue;

@@ -96,7 +96,8 @@ __global__ void __launch_bounds__(WM* WN * 64)
 gemm_planes_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
                    const uint32_t* __restrict__ P, const float* __restrict__ SB, int M, int N,
                    int K, int kbits, uint16_t* __restrict__ Y, int32_t* __restrict__ ACC,
-                   int tiles_m, int tiles_n) {
+                   int tiles_m, int tiles_n, const uint8_t* __restrict__ gate) {
+  if (gate != nullptr && *gate != 0) return;   // device-selected format is not INT8
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -247,15 +248,16 @@ constexpr int kNumPlaneCfgs = sizeof(kPlaneCfgs) / sizeof(kPlaneCfgs[0]);
 template <int BM, int BN, int WM, int WN, int NST>
 hipError_t launch_planes_cfg(const int8_t* xq, const float* sa, const uint32_t* wp,
                              const float* sw, int M, int N, int K, int kbits, uint16_t* y,
-                             int32_t* acc, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+                             int32_t* acc, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
+                             const uint8_t* gate) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const dim3 grid(tiles_m * tiles_n), block(WM * WN * 64);
   auto kern = gemm_planes_kernel<BM, BN, WM, WN, NST>;
   if (ev0 != nullptr || ev1 != nullptr)
     hipExtLaunchKernelGGL(kern, grid, block, 0, s, ev0, ev1, 0, xq, sa, wp, sw, M, N, K, kbits, y,
-                          acc, tiles_m, tiles_n);
+                          acc, tiles_m, tiles_n, gate);
   else
-    kern<<<grid, block, 0, s>>>(xq, sa, wp, sw, M, N, K, kbits, y, acc, tiles_m, tiles_n);
+    kern<<<grid, block, 0, s>>>(xq, sa, wp, sw, M, N, K, kbits, y, acc, tiles_m, tiles_n, gate);
   return hipGetLastError();
 }
 
@@ -298,11 +300,12 @@ int plane_config_choose(int M, int N, int K, int num_cus) {
 
 hipError_t launch_gemm_planes(int cfg, const int8_t* xq, const float* sa, const uint32_t* wp,
                               const float* sw, int M, int N, int K, int kbits, uint16_t* y,
-                              int32_t* acc, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+                              int32_t* acc, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1,
+                              const uint8_t* gate) {
 #define TABIT_PCASE(I, BM, BN, WM, WN, NST, RATE) \
   case I:                                        \
     return launch_planes_cfg<BM, BN, WM, WN, NST>(xq, sa, wp, sw, M, N, K, kbits, y, acc, stream, \
-                                                  ev0, ev1);
+                                                  ev0, ev1, gate);
   switch (cfg) {
     TABIT_PLANE_CONFIGS(TABIT_PCASE)
     default: return hipErrorInvalidValue;

@@ -104,7 +104,8 @@ __device__ __forceinline__ int row_of(int c, int cr, float inv_cr) {
 template <int B, int NT, int CPT>
 __global__ void __launch_bounds__(NT)
 quant_int8_kernel(const uint16_t* __restrict__ x, int M, int K, int rows_per_wg, float scale_div,
-                  int8_t* __restrict__ q, float* __restrict__ scale) {
+                  int8_t* __restrict__ q, float* __restrict__ scale, const uint8_t* __restrict__ gate) {
+  if (gate != nullptr && *gate != 0) return;   // device-selected format is not INT8
   __shared__ unsigned s_amax[NT * CPT / 2];
   __shared__ float s_r[NT * CPT / 2];
   const int tid = threadIdx.x;
@@ -180,7 +181,8 @@ __device__ __forceinline__ uint32_t e2m1_code(float t) {
 template <int B, int CPT>
 __global__ void __launch_bounds__(QT)
 quant_mx_kernel(const uint16_t* __restrict__ x, long long nchunks, uint8_t* __restrict__ qf,
-                uint8_t* __restrict__ e8) {
+                uint8_t* __restrict__ e8, const uint8_t* __restrict__ gate) {
+  if (gate != nullptr && *gate != 1) return;   // device-selected format is not MXFP4
   const int tid = threadIdx.x;
   const int lane = tid & 63;
 #pragma unroll
@@ -224,10 +226,10 @@ quant_mx_kernel(const uint16_t* __restrict__ x, long long nchunks, uint8_t* __re
 
 template <int B>
 hipError_t dispatch_int8(int nt, int cpt, int grid, int rows, const uint16_t* x, int M, int K,
-                         float scale_div, int8_t* q, float* scale, hipStream_t s) {
+                         float scale_div, int8_t* q, float* scale, hipStream_t s, const uint8_t* gate) {
 #define TABIT_Q(NT_, CPT_)                                                                   \
   if (nt == NT_ && cpt == CPT_) {                                                            \
-    quant_int8_kernel<B, NT_, CPT_><<<grid, NT_, 0, s>>>(x, M, K, rows, scale_div, q, scale); \
+    quant_int8_kernel<B, NT_, CPT_><<<grid, NT_, 0, s>>>(x, M, K, rows, scale_div, q, scale, gate); \
     return hipGetLastError();                                                                \
   }
   TABIT_Q(256, 1) TABIT_Q(512, 1) TABIT_Q(1024, 1) TABIT_Q(1024, 2)
@@ -238,7 +240,7 @@ hipError_t dispatch_int8(int nt, int cpt, int grid, int rows, const uint16_t* x,
 }  // namespace
 
 hipError_t launch_quant_int8(const uint16_t* x, int M, int K, int had_block, float scale_div,
-                             int8_t* q, float* scale, hipStream_t stream) {
+                             int8_t* q, float* scale, hipStream_t stream, const uint8_t* gate) {
   if (M <= 0) return hipSuccess;
   const int cr = K / 16;
   // Workgroup shape: one 16-element chunk per thread and as few rows per
@@ -254,24 +256,24 @@ hipError_t launch_quant_int8(const uint16_t* x, int M, int K, int had_block, flo
   const int rows = (nt * cpt) / cr;
   const int grid = (M + rows - 1) / rows;
   switch (had_block) {
-    case 0: return dispatch_int8<0>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream);
-    case 32: return dispatch_int8<32>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream);
-    case 64: return dispatch_int8<64>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream);
-    default: return dispatch_int8<128>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream);
+    case 0: return dispatch_int8<0>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream, gate);
+    case 32: return dispatch_int8<32>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream, gate);
+    case 64: return dispatch_int8<64>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream, gate);
+    default: return dispatch_int8<128>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream, gate);
   }
 }
 
 hipError_t launch_quant_mx(const uint16_t* x, int M, int K, int had_block, uint8_t* q_fp4,
-                           uint8_t* e8m0, hipStream_t stream) {
+                           uint8_t* e8m0, hipStream_t stream, const uint8_t* gate) {
   if (M <= 0) return hipSuccess;
   constexpr int CPT = 1;   // one chunk per thread: 7-36% faster than 2-8 on MI355X
   const long long nchunks = (long long)M * K / 16;
   const long long per_wg = (long long)QT * CPT;
   const int grid = (int)((nchunks + per_wg - 1) / per_wg);
   if (had_block == 32) {
-    quant_mx_kernel<32, CPT><<<grid, QT, 0, stream>>>(x, nchunks, q_fp4, e8m0);
+    quant_mx_kernel<32, CPT><<<grid, QT, 0, stream>>>(x, nchunks, q_fp4, e8m0, gate);
   } else {
-    quant_mx_kernel<0, CPT><<<grid, QT, 0, stream>>>(x, nchunks, q_fp4, e8m0);
+    quant_mx_kernel<0, CPT><<<grid, QT, 0, stream>>>(x, nchunks, q_fp4, e8m0, gate);
   }
   return hipGetLastError();
 }

@@ -18,12 +18,16 @@ namespace tabit {
 // Per-row INT8 quantization with an optional block FWHT (activations and
 // weights).  scale_div divides the per-row scale a/127 (1 for activations,
 // max(b, 1) for weights).
+// gate (optional, every launcher below): device byte holding the format the
+// caller's schedule selected; a kernel whose format differs returns at once.
 hipError_t launch_quant_int8(const uint16_t* x, int M, int K, int had_block, float scale_div,
-                             int8_t* q, float* scale, hipStream_t stream);
+                             int8_t* q, float* scale, hipStream_t stream,
+                             const uint8_t* gate = nullptr);
 
 // MXFP4 quantization (block 32, optional FWHT32).
 hipError_t launch_quant_mx(const uint16_t* x, int M, int K, int had_block,
-                           uint8_t* q_fp4, uint8_t* e8m0, hipStream_t stream);
+                           uint8_t* q_fp4, uint8_t* e8m0, hipStream_t stream,
+                           const uint8_t* gate = nullptr);
 
 // ---------------------------------------------------------------- INT8 GEMM
 struct GemmConfig {
@@ -37,7 +41,8 @@ int gemm_config_choose(int M, int N, int K, int num_cus);
 hipError_t launch_gemm_i8(int cfg, bool bitserial, const int8_t* xq, const float* sa,
                           const int8_t* wq, const float* sw, int M, int N, int K, int kbits,
                           uint16_t* y, int32_t* acc, hipStream_t stream,
-                          hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+                          hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr,
+                          const uint8_t* gate = nullptr);
 
 // ---------------------------------------------------------------- MXFP4 GEMM
 int mx_config_count();
@@ -47,7 +52,8 @@ int mx_config_choose(int M, int N, int K, int num_cus);
 hipError_t launch_gemm_mxfp4(int cfg, const uint8_t* xq, const uint8_t* xe, const uint8_t* wq,
                              const uint8_t* we, int M, int N, int K, float out_scale,
                              uint16_t* y, float* acc, hipStream_t stream,
-                             hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+                             hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr,
+                             const uint8_t* gate = nullptr);
 
 // ---------------------------------------------------------------- plane-major storage
 // uint32 P[8][ceil(K/128)][N][4]: word P[b][s][n][j] holds bit b of
@@ -60,7 +66,15 @@ int plane_config_choose(int M, int N, int K, int num_cus);
 hipError_t launch_gemm_planes(int cfg, const int8_t* xq, const float* sa, const uint32_t* wp,
                               const float* sw, int M, int N, int K, int kbits, uint16_t* y,
                               int32_t* acc, hipStream_t stream, hipEvent_t ev0 = nullptr,
-                              hipEvent_t ev1 = nullptr);
+                              hipEvent_t ev1 = nullptr, const uint8_t* gate = nullptr);
+
+// ---------------------------------------------------------------- DMPQ selector
+// Gamma = sum |out - in| / sum |in| of a block's hidden states in the fixed
+// fp64 order; fmt[l] = Gamma > theta[l] ? INT8 : MXFP4.  rows: M x 2 doubles.
+size_t dmpq_workspace_bytes(int M);
+hipError_t launch_dmpq_select(const uint16_t* xin, const uint16_t* xout, int M, int H, double* rows,
+                              const float* theta, int n_layers, uint8_t* fmt, double* gamma,
+                              hipStream_t s);
 
 // Compute units of the current device (cached per device id).
 int device_num_cus();
