@@ -284,6 +284,102 @@ def k_sweep(ctx, T, torch, wl, weights, xs, ys, b, cold=False):
     return res
 
 
+def dmpq_bench(args, T, torch, dev) -> dict:
+    """CogVideoX-shaped schedule with the online selector in the loop.
+
+    Per step t and block j: the selector reads block j's input/output of step
+    t-1 (a seeded pair drawn from a stable/unstable pool), writes the formats of
+    the block's 4 linears into a device table, and the 4 gated linears run from
+    that table.  Timed against the host-scheduled run of the realized table, and
+    the selector alone against HBM bandwidth.  Activations: one per (M, K).
+    """
+    import tabit_synth as S
+    wl = S.c5_cogvideox()
+    b, L = wl.had_block, wl.num_layers
+    Tn = args.dmpq_steps or wl.steps
+    blocks, H, M = L // 4, wl.layers[0].K, wl.layers[0].M
+    ctx = T.Context()
+    weights = []
+    for li, layer in enumerate(wl.layers):
+        w = S.gen_weight(layer.N, layer.K, seed=li).to(dev)
+        weights.append(ctx.quantize_weights(w, b, int8=True, mx=True))
+        del w
+    xs = {}
+    for layer in wl.layers:
+        if (layer.M, layer.K) not in xs:
+            xs[(layer.M, layer.K)] = S.gen_activation(layer.M, layer.K,
+                                                      seed=S.activation_seed(0, layer.K)).to(dev)
+    ys = [torch.empty((l.M, l.N), dtype=torch.bfloat16, device=dev) for l in wl.layers]
+    act_ws = torch.empty(max(T.act_workspace_bytes(l.M, l.K) for l in wl.layers), dtype=torch.uint8,
+                         device=dev)
+    pool = [tuple(t.to(dev) for t in S.gen_block_io(M, H, seed=80 + i, delta=d))
+            for i, d in enumerate(S.DMPQ_DELTAS)]
+    draws = S.dmpq_pool_draws(Tn, blocks)
+    theta = torch.full((4,), args.dmpq_theta, dtype=torch.float32, device=dev)
+    fmt = torch.zeros((Tn, L), dtype=torch.uint8, device=dev)      # step 0: INT8 everywhere
+    gamma = torch.zeros((Tn, blocks), dtype=torch.float64, device=dev)
+    dws = torch.empty(T.dmpq_workspace_bytes(M), dtype=torch.uint8, device=dev)
+
+    def gated_pass():
+        for t in range(Tn):
+            for j in range(blocks):
+                if t > 0:
+                    xi, xo = pool[draws[t - 1, j]]
+                    ctx.dmpq_select(xi, xo, theta, fmt[t, 4 * j:4 * j + 4], gamma[t, j:j + 1], dws)
+                for i in range(4):
+                    li = 4 * j + i
+                    layer = wl.layers[li]
+                    ctx.gated_linear(fmt[t, li:li + 1], 0, xs[(layer.M, layer.K)], weights[li], b,
+                                     act_ws, y=ys[li])
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n
+
+    ms_gated = timed(gated_pass, args.steps)
+    realized = fmt.cpu().numpy()
+    # the host-scheduled run of the same formats (no selector, no gated launches)
+    ctx.set_step_schedule(np.zeros((Tn, L), np.uint8), realized)
+    layers = (T.Layer * L)()
+    for li, (layer, wt) in enumerate(zip(wl.layers, weights)):
+        layers[li].M, layers[li].N, layers[li].K = layer.M, layer.N, layer.K
+        layers[li].w_q, layers[li].w_scale = wt["w_q"].data_ptr(), wt["w_scale"].data_ptr()
+        layers[li].w_fp4, layers[li].w_e8m0 = wt["w_fp4"].data_ptr(), wt["w_e8m0"].data_ptr()
+        layers[li].y_bf16 = ys[li].data_ptr()
+    x_ptrs = (ctypes.c_void_p * (Tn * L))()
+    for t in range(Tn):
+        for li, layer in enumerate(wl.layers):
+            x_ptrs[t * L + li] = xs[(layer.M, layer.K)].data_ptr()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    ms_host = timed(lambda: ctx.run_schedule(0, Tn, layers, x_ptrs, b, act_ws, stream=stream),
+                    args.steps)
+    # the selector alone
+    xi, xo = pool[0]
+    sel_us = timed(lambda: [ctx.dmpq_select(xi, xo, theta, fmt[0, :4], gamma[0, :1], dws)
+                            for _ in range(20)], 1) * 1e3 / 20
+    sel_bytes = 2 * M * H * 2 + 16 * M
+    ops = 2 * sum(l.M * l.N * l.K for l in wl.layers) * Tn
+    ctx.close()
+    return {
+        "mode": "dmpq", "workload": wl.name, "denoise_steps": Tn, "blocks": blocks,
+        "theta": args.dmpq_theta,
+        "ms_per_schedule_gated": round(ms_gated, 3),
+        "ms_per_schedule_host_same_formats": round(ms_host, 3),
+        "selector_and_gating_overhead_ms": round(ms_gated - ms_host, 3),
+        "tops_gated": round(ops / (ms_gated / 1e3) / 1e12, 2),
+        "mxfp4_fraction": round(float(realized[1:].mean()), 4) if Tn > 1 else 0.0,
+        "selector_us": round(sel_us, 2),
+        "selector_GBps": round(sel_bytes / (sel_us / 1e6) / 1e9, 1),
+        "selector_frac_of_hbm": round(sel_bytes / (sel_us / 1e6) / 8e12, 4),
+        "selector_bytes": sel_bytes,
+    }
+
+
 def gemm_tiles(T, wl, tuned, path=0):
     """Tile shape (BM, BN) each distinct GEMM shape runs with."""
     out = {}
@@ -319,6 +415,10 @@ def main() -> int:
                          "calibrated choice, which keeps counter runs on the same kernels)")
     ap.add_argument("--shared-x", action="store_true",
                     help="reuse step 0's activations at every step (same work, faster set-up)")
+    ap.add_argument("--dmpq", action="store_true",
+                    help="only run the CogVideoX-shaped schedule with the online INT8/4-bit selector")
+    ap.add_argument("--dmpq-steps", type=int, default=0, help="denoising steps for --dmpq (0 = 50)")
+    ap.add_argument("--dmpq-theta", type=float, default=0.2, help="selector threshold on Gamma")
     ap.add_argument("--cold", action="store_true",
                     help="with --k-sweep: every launch reads weights cold from HBM")
     ap.add_argument("--k-sweep", action="store_true",
@@ -357,6 +457,9 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.dmpq:
+        print(json.dumps(dmpq_bench(args, T, torch, dev)), flush=True)
+        return 0
     wl = S.WORKLOADS[args.workload]() if args.had_block is None else \
         S.WORKLOADS[args.workload](had_block=args.had_block)
     b = wl.had_block

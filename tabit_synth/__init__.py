@@ -193,6 +193,26 @@ def c5_cogvideox(had_block: int = 32) -> Workload:
                     np.zeros((T, L), dtype=np.uint8), fmt)
 
 
+# Block input/output pairs for the online INT8 / 4-bit selector: out = in +
+# delta * noise * mean|in| per row.  A small pool of deltas stands for stable
+# (small) and unstable (large) blocks; each (step, block) draws one pair.
+DMPQ_DELTAS = (0.02, 0.05, 0.4, 0.8)
+DMPQ_POOL_P = (0.3, 0.3, 0.2, 0.2)
+
+
+def gen_block_io(M: int, H: int, seed: int, delta: float) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Seeded bf16 block input and output [M][H]."""
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(M, H, generator=g)
+    y = x + delta * torch.randn(M, H, generator=g) * x.abs().mean(dim=1, keepdim=True)
+    return x.to(torch.bfloat16), y.to(torch.bfloat16)
+
+
+def dmpq_pool_draws(steps: int, blocks: int, seed: int = 70) -> np.ndarray:
+    """Index into DMPQ_DELTAS per (step, block), int [steps][blocks]."""
+    return _rng(seed).choice(len(DMPQ_DELTAS), size=(steps, blocks), p=DMPQ_POOL_P)
+
+
 WORKLOADS = {
     "c1": c1_single_linear,
     "c2": c2_pixart_sigma,

@@ -125,7 +125,7 @@ def test_dmpq_validation(lib, ctx):
     assert d(H=65536) == T.ESHAPE
     assert d(nb=16) == T.ESHAPE                        # workspace below 16 bytes per row
     assert d(g=FAKE + 4) == T.EALIGN
-    assert T.dmpq_workspace_bytes(100) == 1600
+    assert T.dmpq_workspace_bytes(100) >= 1600 and T.dmpq_workspace_bytes(0) == 0
 
 
 def test_gated_linear_validation(lib, ctx):

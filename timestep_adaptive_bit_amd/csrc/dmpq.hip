@@ -15,8 +15,6 @@
 // the row sums by a pairwise tree; trees zero-padded to a power of two.  A
 // butterfly (lane XOR 1, 2, 4, ...) over a power-of-two group computes exactly
 // that pairwise tree in every lane, because fp addition is commutative.
-#include <algorithm>
-
 #include "tabit_internal.h"
 
 namespace tabit {
@@ -109,65 +107,58 @@ dmpq_rows_kernel(const uint16_t* __restrict__ xin, const uint16_t* __restrict__ 
   }
 }
 
-constexpr int FT = 1024;   // threads of the finishing workgroup
+constexpr int FT = 1024;   // leaves per workgroup of a tree level
 
-// Pairwise tree over the M row sums (padded with zeros to FT * G leaves, G a
-// power of two), then Gamma and the per-layer decisions.  Thread t reduces
-// leaves [tG, tG + G) with a carry stack (merging equal-size partial sums
-// left + right reproduces the balanced tree), then a butterfly and a tree over
-// the waves finish it.
+// One level of the pairwise tree over (sum |out - in|, sum |in|) pairs: group g
+// sums leaves [1024g, 1024g + 1024) (zeros past n) with a butterfly and a tree
+// over the waves.  Aligned power-of-two groups of a zero-padded pairwise tree
+// are its subtrees, so chaining levels reproduces the whole tree.  The last
+// level (one group) also forms Gamma and the per-layer decisions.
 __global__ void __launch_bounds__(FT)
-dmpq_finish_kernel(const double* __restrict__ rows, int M, int G, const float* __restrict__ theta,
-                   int n_layers, uint8_t* __restrict__ fmt, double* __restrict__ gamma_out) {
+dmpq_tree_kernel(const double* __restrict__ in, long long n, double* __restrict__ out,
+                 const float* __restrict__ theta, int n_layers, uint8_t* __restrict__ fmt,
+                 double* __restrict__ gamma_out, int last) {
   constexpr int NW = FT / 64;
   __shared__ double sd[NW], sa[NW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  double std_[32], sta[32];
-  int depth = 0;
-  for (int i = 0; i < G; ++i) {
-    const long long leaf = (long long)tid * G + i;
-    double d = 0.0, a = 0.0;
-    if (leaf < M) {
-      d = rows[2 * leaf];
-      a = rows[2 * leaf + 1];
-    }
-    for (int j = i; j & 1; j >>= 1) {   // a completed pair of equal subtrees: left + right
-      --depth;
-      d = std_[depth] + d;
-      a = sta[depth] + a;
-    }
-    std_[depth] = d;
-    sta[depth] = a;
-    ++depth;
+  const long long leaf = (long long)blockIdx.x * FT + tid;
+  double d = 0.0, a = 0.0;
+  if (leaf < n) {
+    d = in[2 * leaf];
+    a = in[2 * leaf + 1];
   }
-  double d = wave_tree(std_[0]);
-  double a = wave_tree(sta[0]);
+  d = wave_tree(d);
+  a = wave_tree(a);
   if (lane == 0) {
     sd[wave] = d;
     sa[wave] = a;
   }
   __syncthreads();
-  if (tid == 0) {
-    double vd[NW], va[NW];
+  if (tid != 0) return;
+  double vd[NW], va[NW];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      vd[w] = sd[w];
-      va[w] = sa[w];
-    }
-#pragma unroll
-    for (int n = NW; n > 1; n >>= 1)
-#pragma unroll
-      for (int w = 0; w < n / 2; ++w) {
-        vd[w] = vd[2 * w] + vd[2 * w + 1];
-        va[w] = va[2 * w] + va[2 * w + 1];
-      }
-    const double num = vd[0], den = va[0];
-    double g;
-    if (den == 0.0) g = num == 0.0 ? 0.0 : __builtin_huge_val();
-    else g = num / den;
-    if (gamma_out != nullptr) gamma_out[0] = g;
-    for (int l = 0; l < n_layers; ++l) fmt[l] = g > (double)theta[l] ? (uint8_t)0 : (uint8_t)1;
+  for (int w = 0; w < NW; ++w) {
+    vd[w] = sd[w];
+    va[w] = sa[w];
   }
+#pragma unroll
+  for (int k = NW; k > 1; k >>= 1)
+#pragma unroll
+    for (int w = 0; w < k / 2; ++w) {
+      vd[w] = vd[2 * w] + vd[2 * w + 1];
+      va[w] = va[2 * w] + va[2 * w + 1];
+    }
+  if (!last) {
+    out[2 * blockIdx.x] = vd[0];
+    out[2 * blockIdx.x + 1] = va[0];
+    return;
+  }
+  const double num = vd[0], den = va[0];
+  double g;
+  if (den == 0.0) g = num == 0.0 ? 0.0 : __builtin_huge_val();
+  else g = num / den;
+  if (gamma_out != nullptr) gamma_out[0] = g;
+  for (int l = 0; l < n_layers; ++l) fmt[l] = g > (double)theta[l] ? (uint8_t)0 : (uint8_t)1;
 }
 
 int next_pow2(long long v) {
@@ -176,9 +167,21 @@ int next_pow2(long long v) {
   return p;
 }
 
+long long groups(long long n) { return (n + FT - 1) / FT; }
+
 }  // namespace
 
-size_t dmpq_workspace_bytes(int M) { return M <= 0 ? 0 : (size_t)M * 16u; }
+// Row sums, then the partial sums of each tree level (at most 4 levels for
+// M < 2^26 rows).
+size_t dmpq_workspace_bytes(int M) {
+  if (M <= 0) return 0;
+  long long pairs = M, n = M;
+  while (n > 1) {
+    n = groups(n);
+    pairs += n;
+  }
+  return (size_t)(pairs + 1) * 16u;
+}
 
 hipError_t launch_dmpq_select(const uint16_t* xin, const uint16_t* xout, int M, int H, double* rows,
                               const float* theta, int n_layers, uint8_t* fmt, double* gamma,
@@ -192,11 +195,18 @@ hipError_t launch_dmpq_select(const uint16_t* xin, const uint16_t* xout, int M, 
   else if (p == 1024) dmpq_rows_kernel<1024, 1><<<M, 1024, 0, s>>>(xin, xout, H, rows);
   else dmpq_rows_kernel<1024, 2><<<M, 1024, 0, s>>>(xin, xout, H, rows);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const long long leaves = std::max<long long>(FT, 1LL << next_pow2(M));
-  const int G = (int)(leaves / FT);
-  dmpq_finish_kernel<<<1, FT, 0, s>>>(rows, M, G, theta, n_layers, fmt, gamma);
-  return hipGetLastError();
+  double* src = rows;
+  long long n = M;
+  while (e == hipSuccess) {
+    const long long g = groups(n);
+    double* dst = src + 2 * n;
+    dmpq_tree_kernel<<<(unsigned)g, FT, 0, s>>>(src, n, dst, theta, n_layers, fmt, gamma, g == 1);
+    e = hipGetLastError();
+    if (g == 1) break;
+    src = dst;
+    n = g;
+  }
+  return e;
 }
 
 }  // namespace tabit
