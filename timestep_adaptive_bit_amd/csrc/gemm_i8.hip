@@ -184,19 +184,18 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
 
 struct CfgDesc {
   int bm, bn, wm, wn, rb, nst;
-  int slots;    // workgroups one CU holds at once (LDS and register limits)
-  float rate;   // relative per-CU throughput when busy (measured on MI355X)
+  float rate;   // relative throughput per CU on its tiles (fitted to MI355X sweeps)
 };
-// index, BM, BN, WM, WN, stage row bytes, LDS stages, slots per CU, rate
-#define TABIT_I8_CONFIGS(X)                \
-  X(0, 256, 256, 2, 4, 128, 2, 1, 1.00f)    \
-  X(1, 192, 192, 2, 3, 128, 3, 1, 0.80f)    \
-  X(2, 128, 128, 2, 2, 128, 2, 2, 0.95f)    \
-  X(3, 256, 128, 2, 2, 128, 3, 1, 0.75f)    \
-  X(4, 128, 64, 2, 2, 128, 2, 3, 0.75f)     \
-  X(5, 64, 64, 2, 2, 128, 2, 4, 0.55f)      \
-  X(6, 192, 128, 2, 2, 128, 2, 1, 0.70f)
-#define TABIT_DESC(I, BM, BN, WM, WN, RB, NST, SLOTS, RATE) {BM, BN, WM, WN, RB, NST, SLOTS, RATE},
+// index, BM, BN, WM, WN, stage row bytes, LDS stages, rate
+#define TABIT_I8_CONFIGS(X)             \
+  X(0, 256, 256, 2, 4, 128, 2, 1.00f)    \
+  X(1, 192, 192, 2, 3, 128, 3, 0.71f)    \
+  X(2, 128, 128, 2, 2, 128, 2, 0.79f)    \
+  X(3, 256, 128, 2, 2, 128, 3, 0.68f)    \
+  X(4, 128, 64, 2, 2, 128, 2, 0.665f)    \
+  X(5, 64, 64, 2, 2, 128, 2, 0.52f)      \
+  X(6, 192, 128, 2, 2, 128, 2, 0.66f)
+#define TABIT_DESC(I, BM, BN, WM, WN, RB, NST, RATE) {BM, BN, WM, WN, RB, NST, RATE},
 constexpr CfgDesc kCfgs[] = {TABIT_I8_CONFIGS(TABIT_DESC)};
 #undef TABIT_DESC
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
@@ -223,10 +222,12 @@ int gemm_config_count() { return kNumCfgs; }
 
 GemmConfig gemm_config(int index) { return GemmConfig{kCfgs[index].bm, kCfgs[index].bn, 1}; }
 
-// Estimated time of a configuration: tiles run in rounds of (CUs x slots);
-// each round costs slots x BM x BN x K / rate (the CU's throughput is shared
-// by the workgroups it holds).  The rates come from sweeps on MI355X; callers
-// that want the measured best use tabit_autotune_gemm.
+// Estimated time of a configuration: tiles land round-robin on the CUs, so
+// the busiest CU runs ceil(tiles / CUs) of them (several at once when they
+// fit, sharing its throughput); its time is that count x BM x BN x K / rate.
+// The rates are fitted to sweeps of every configuration over the workloads'
+// shapes on MI355X; callers that want the measured best use
+// tabit_autotune_gemm.
 int gemm_config_choose(int M, int N, int K, int num_cus) {
   (void)K;
   if (num_cus <= 0) num_cus = 256;
@@ -235,9 +236,8 @@ int gemm_config_choose(int M, int N, int K, int num_cus) {
   for (int i = 0; i < kNumCfgs; ++i) {
     const CfgDesc& c = kCfgs[i];
     const long long tiles = (long long)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
-    const long long per_round = (long long)num_cus * c.slots;
-    const long long rounds = (tiles + per_round - 1) / per_round;
-    const double cost = (double)rounds * c.slots * c.bm * c.bn / c.rate;
+    const long long per_cu = (tiles + num_cus - 1) / num_cus;
+    const double cost = (double)per_cu * c.bm * c.bn / c.rate;
     if (cost < best_cost * 0.999) {
       best_cost = cost;
       best = i;
@@ -250,7 +250,7 @@ hipError_t launch_gemm_i8(int cfg, bool bitserial, const int8_t* xq, const float
                           const int8_t* wq, const float* sw, int M, int N, int K, int kbits,
                           uint16_t* y, int32_t* acc, hipStream_t stream, hipEvent_t ev0,
                           hipEvent_t ev1, const uint8_t* gate) {
-#define TABIT_CASE(I, BM, BN, WM, WN, RB, NST, SLOTS, RATE) \
+#define TABIT_CASE(I, BM, BN, WM, WN, RB, NST, RATE) \
   case I:                                            \
     return launch_cfg<BM, BN, WM, WN, RB, NST>(bitserial, xq, sa, wq, sw, M, N, K, kbits, y, acc, \
                                                stream, ev0, ev1, gate);
