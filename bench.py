@@ -107,6 +107,60 @@ def _pmc_values(root: str, counter: str, name_part: str):
     return vals
 
 
+def _pmc_rows(root: str, name_part: str):
+    """{dispatch_id: {counter: value, "_dur_ns": duration, "_name": kernel}} for matching kernels."""
+    import sqlite3
+    out = {}
+    for db in sorted(glob.glob(os.path.join(root, "**", "*.db"), recursive=True)):
+        c = sqlite3.connect(db)
+        q = ("select dispatch_id, kernel_name, counter_name, value, duration from counters_collection "
+             "where kernel_name like ?")
+        for d, name, cn, v, dur in c.execute(q, (f"%{name_part}%",)):
+            r = out.setdefault((db, d), {"_dur_ns": dur, "_name": name})
+            r[cn] = r.get(cn, 0.0) + v
+    return list(out.values())
+
+
+def summarize_counters(mfma_dir: str, fetch_dir: str, write_dir: str, cal_fetch_dir: str,
+                       cal_write_dir: str, cal_bytes: int, workload: str) -> None:
+    """Counter evidence per kernel shape: MFMA ops executed vs the algorithmic 2MNK and MFMA
+    busy share for the GEMMs; copy-calibrated HBM bytes and GB/s for the quantizers."""
+    import tabit_synth as S
+    wl = S.WORKLOADS[workload]()
+    simds, xcds = 1024, 8  # 256 CUs x 4 SIMDs; GRBM_GUI_ACTIVE arrives summed over the 8 XCDs
+
+    def short(name):
+        return name.replace("void ", "").replace("tabit::(anonymous namespace)::", "").split("(")[0]
+    print("# GEMM (per dispatch, grouped by tile config): MFMA ops executed = MOPS_I8 x 512;")
+    print("# MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs), rocprof's MfmaUtil")
+    print(f"{'kernel':58s} {'n':>5s} {'MFMA Gop':>9s} {'util%':>6s} {'us':>7s} {'TOPS':>7s}")
+    groups = {}
+    for r in _pmc_rows(mfma_dir, "gemm_i8"):
+        groups.setdefault(short(r["_name"]), []).append(r)
+    for k, rs in sorted(groups.items()):
+        ops = sum(r.get("SQ_INSTS_VALU_MFMA_MOPS_I8", 0) * 512 for r in rs) / len(rs)
+        busy = sum(r.get("SQ_VALU_MFMA_BUSY_CYCLES", 0)
+                   / max(1.0, r.get("GRBM_GUI_ACTIVE", 1) / xcds * simds) for r in rs) / len(rs)
+        us = sum(r["_dur_ns"] for r in rs) / len(rs) / 1e3
+        print(f"{k:58s} {len(rs):5d} {ops / 1e9:9.2f} {100 * busy:6.1f} {us:7.2f} {ops / us / 1e6:7.1f}")
+    shapes = sorted({(l.M, l.N, l.K) for l in wl.layers})
+    print("# algorithmic 2MNK per shape (Gop): " +
+          ", ".join(f"{m}x{n}x{k} {2 * m * n * k / 1e9:.2f}" for m, n, k in shapes))
+    cf = max(_pmc_values(cal_fetch_dir, "FETCH_SIZE", "")) * 1024.0 / cal_bytes
+    cw = max(_pmc_values(cal_write_dir, "WRITE_SIZE", "")) * 1024.0 / cal_bytes
+    print(f"# quantizers (FETCH x {1 / cf:.2f}, WRITE x {1 / cw:.2f} from the copy calibration)")
+    print(f"{'kernel':58s} {'n':>5s} {'read MB':>8s} {'write MB':>9s} {'us':>7s} {'GB/s':>8s} {'%8TB/s':>7s}")
+    f_rows, w_rows = _pmc_rows(fetch_dir, "quant_"), _pmc_rows(write_dir, "quant_")
+    for k in sorted({r["_name"] for r in f_rows}):
+        fr = [r for r in f_rows if r["_name"] == k]
+        wr = [r for r in w_rows if r["_name"] == k]
+        rd = sum(r["FETCH_SIZE"] for r in fr) / len(fr) * 1024 / cf
+        wb = sum(r["WRITE_SIZE"] for r in wr) / len(wr) * 1024 / cw
+        us = sum(r["_dur_ns"] for r in fr + wr) / len(fr + wr) / 1e3
+        print(f"{short(k):58s} {len(fr):5d} {rd / 1e6:8.2f} {wb / 1e6:9.2f} {us:7.2f} "
+              f"{(rd + wb) / us / 1e3:8.0f} {100 * (rd + wb) / us / 8e6:7.1f}")
+
+
 def record_traffic(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_bytes, n_last,
                    workload, path):
     """HBM bytes per GEMM launch: FETCH_SIZE + WRITE_SIZE (KiB per dispatch) of the last
@@ -431,6 +485,9 @@ def main() -> int:
                                                           "CAL_WRITE_DIR", "N_LAST"), default=None,
                     help="only turn counter runs into the per-launch GEMM traffic record")
     ap.add_argument("--copy-mib", type=int, default=256, help="size of the calibration copy")
+    ap.add_argument("--summarize-counters", nargs=5, metavar=("MFMA_DIR", "FETCH_DIR", "WRITE_DIR",
+                                                             "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
+                    default=None, help="only print MFMA and quantizer HBM counter evidence")
     args = ap.parse_args()
     if args.record_traffic:
         fd, wd, cfd, cwd, n = args.record_traffic
@@ -440,6 +497,9 @@ def main() -> int:
         return 0
     if args.summarize:
         summarize_rocpd(args.summarize)
+        return 0
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.copy_mib << 20, args.workload)
         return 0
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
