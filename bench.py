@@ -334,6 +334,14 @@ def k_sweep(ctx, T, torch, wl, weights, xs, ys, b, cold=False):
                 times.append(round(e0.elapsed_time(e1) * 1e3 / reps, 2))
             row[name] = times
             del copies
+        bs = row.get("bitserial")
+        if bs:
+            xs_ = np.arange(8, 0, -1, dtype=np.float64)         # planes 8 - k for k = 0..7
+            ys_ = np.asarray(bs, dtype=np.float64)
+            slope, icpt = np.polyfit(xs_, ys_, 1)
+            r2 = 1 - ((ys_ - (slope * xs_ + icpt)) ** 2).sum() / ((ys_ - ys_.mean()) ** 2).sum()
+            row["bitserial_fit_us"] = {"per_plane": round(float(slope), 3),
+                                       "intercept": round(float(icpt), 3), "r2": round(float(r2), 4)}
         res["x".join(map(str, key))] = row
     return res
 
@@ -432,6 +440,52 @@ def dmpq_bench(args, T, torch, dev) -> dict:
         "selector_frac_of_hbm": round(sel_bytes / (sel_us / 1e6) / 8e12, 4),
         "selector_bytes": sel_bytes,
     }
+
+
+def quant_bandwidth(ctx, T, torch, wl, xs, b, act_ws) -> dict:
+    """Activation quantizer per distinct (M, K) of the schedule: time per launch (HIP events
+    around 20 back-to-back launches, launch gaps included), bytes 3MK + 4M (INT8) or
+    2MK + MK/2 + MK/32 (MXFP4), against 8 TB/s and a device copy of the same bytes."""
+    out = {}
+    seen = set()
+    for li, layer in enumerate(wl.layers):
+        for fmt in sorted(set(int(f) for f in wl.fmt[:, li])):
+            key = (fmt, layer.M, layer.K)
+            if key in seen:
+                continue
+            seen.add(key)
+            M, K = layer.M, layer.K
+            x = xs[(0, M, K)]
+            if fmt == 0:
+                q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+                sc = torch.empty((M,), dtype=torch.float32, device=x.device)
+                nbytes = 3 * M * K + 4 * M
+            else:
+                q = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+                sc = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+                nbytes = 2 * M * K + M * K // 2 + M * K // 32
+            src = torch.empty(nbytes // 2 // 16 * 16, dtype=torch.uint8, device=x.device)
+            dst = torch.empty_like(src)
+
+            def timed(fn, n=20):
+                fn()
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(n):
+                    fn()
+                e1.record()
+                torch.cuda.synchronize()
+                return e0.elapsed_time(e1) * 1e3 / n
+            us = timed(lambda: ctx.hadamard_quant_act(x, b, T.FMT_MXFP4 if fmt else T.FMT_INT8, q, sc))
+            cus = timed(lambda: dst.copy_(src))        # reads + writes the same number of bytes
+            out[f"{'mxfp4' if fmt else 'int8'} {M}x{K}"] = {
+                "us_per_launch": round(us, 2), "GBps": round(nbytes / us / 1e3, 1),
+                "frac_of_8TBps": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                "copy_GBps_same_bytes": round(2 * src.numel() / cus / 1e3, 1)}
+            del q, sc, src, dst
+    return out
 
 
 def gemm_tiles(T, wl, tuned, path=0):
@@ -648,6 +702,25 @@ def main() -> int:
                     else:
                         gemm_ms_mx += ms
                         n_mx += 1
+        per_shape = {}
+        for s_ in range(args.steps):
+            ev = ev_sets[s_]
+            for t in range(Tn):
+                for li, layer in enumerate(wl.layers):
+                    if wl.fmt[t, li] != 0:
+                        continue
+                    i = t * L + li
+                    per_shape.setdefault((layer.M, layer.N, layer.K), []).append(
+                        hip.elapsed_ms(ev[2 * i], ev[2 * i + 1]))
+        detail["per_shape"] = {}
+        for (m, n, k_), v in sorted(per_shape.items()):
+            us = sum(v) / len(v) * 1e3
+            tops = 2 * m * n * k_ / us / 1e6
+            ai = 2 * m * n * k_ / (m * k_ + n * k_ + 2 * m * n)        # INT8 ops per HBM byte
+            roof = min(INT8_PEAK_TOPS, ai * HBM_PEAK_GBS / 1e3)
+            detail["per_shape"][f"{m}x{n}x{k_}"] = {
+                "us": round(us, 2), "tops": round(tops, 1), "ai_op_per_byte": round(ai, 1),
+                "roofline_tops": round(roof, 1), "frac_of_roofline": round(tops / roof, 4)}
         for e in ev_sets:
             hip.destroy(e)
         if n_i8:
@@ -675,6 +748,7 @@ def main() -> int:
     if int8_ops > 0 and not args.no_events:
         detail["quantizer_and_gaps_ms_per_step"] = round(ms_per_step - detail["gemm_int8_ms_per_step"]
                                                          - detail.get("gemm_mxfp4_ms_per_step", 0.0), 3)
+    detail["quantizer"] = quant_bandwidth(ctx, T, torch, wl, xs, b, act_ws)
     if args.k_sweep:
         detail["k_sweep_us" + ("_cold" if args.cold else "")] = k_sweep(ctx, T, torch, wl, weights, xs,
                                                                         ys, b, cold=args.cold)
