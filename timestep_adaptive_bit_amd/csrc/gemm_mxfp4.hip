@@ -13,7 +13,8 @@
 // -- and that block's E8M0 byte as its scale operand.  The tile skeleton is
 // the INT8 GEMM's: packed operand stages of 128 bytes (256 elements) copied
 // global->LDS by buffer loads into a double-buffered ring, one barrier per
-// stage.  The 8 scale bytes per row and stage go through registers into a
+// stage; each wave reads the next K-step's fragments and scale bytes from LDS
+// while the matrix cores work on the current one.  The 8 scale bytes per row and stage go through registers into a
 // small LDS table next to the data (their loads are issued before the stage's
 // copies so waiting for them never waits for the copies).
 #include "tabit_internal.h"
@@ -116,31 +117,38 @@ gemm_mxfp4_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ AE,
     const int8_t* sb = sa + BM * RB;
     const uint8_t* ssa = sscale[kt & 1];
     const uint8_t* ssb = ssa + BM * SPR;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    // fragments and scale bytes of K-step ks + 1 are read from LDS while the
+    // matrix cores work on K-step ks
+    v4i a[2][FM], b[2][FN];
+    int ea[2][FM], eb[2][FN];
+    auto load = [&](int ks, int buf) {
       const int c = ks * 2 + khalf;     // 16-byte chunk = one 32-element MX block
-      v4i a[FM], b[FN];
-      int ea[FM], eb[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int r = ra0 + i * 32;
-        a[i] = *reinterpret_cast<const v4i*>(sa + tile::lds_off<RB>(r, c));
-        ea[i] = ssa[r * SPR + c];
+        a[buf][i] = *reinterpret_cast<const v4i*>(sa + tile::lds_off<RB>(r, c));
+        ea[buf][i] = ssa[r * SPR + c];
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int r = rb0 + j * 32;
-        b[j] = *reinterpret_cast<const v4i*>(sb + tile::lds_off<RB>(r, c));
-        eb[j] = ssb[r * SPR + c];
+        b[buf][j] = *reinterpret_cast<const v4i*>(sb + tile::lds_off<RB>(r, c));
+        eb[buf][j] = ssb[r * SPR + c];
       }
+    };
+    load(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < KS) load(ks + 1, cur ^ 1);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const v8i a8 = {a[i][0], a[i][1], a[i][2], a[i][3], 0, 0, 0, 0};
+        const v8i a8 = {a[cur][i][0], a[cur][i][1], a[cur][i][2], a[cur][i][3], 0, 0, 0, 0};
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          const v8i b8 = {b[j][0], b[j][1], b[j][2], b[j][3], 0, 0, 0, 0};
+          const v8i b8 = {b[cur][j][0], b[cur][j][1], b[cur][j][2], b[cur][j][3], 0, 0, 0, 0};
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc[i][j], 4, 4, 0,
-                                                                       ea[i], 0, eb[j]);
+                                                                       ea[cur][i], 0, eb[cur][j]);
         }
       }
     }
@@ -171,16 +179,17 @@ gemm_mxfp4_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ AE,
 
 struct CfgDesc {
   int bm, bn, wm, wn;
-  int slots;
-  float rate;
+  float rate;   // relative throughput per CU on its tiles (fitted to MI355X sweeps)
 };
-// index, BM, BN, WM, WN, slots per CU, rate
-#define TABIT_MX_CONFIGS(X)          \
-  X(0, 256, 128, 2, 2, 1, 1.00f)     \
-  X(1, 128, 128, 2, 2, 2, 0.95f)     \
-  X(2, 128, 64, 2, 2, 3, 0.75f)      \
-  X(3, 64, 64, 2, 2, 4, 0.55f)
-#define TABIT_DESC(I, BM, BN, WM, WN, SLOTS, RATE) {BM, BN, WM, WN, SLOTS, RATE},
+// index, BM, BN, WM, WN, rate
+#define TABIT_MX_CONFIGS(X)       \
+  X(0, 256, 128, 2, 2, 0.815f)    \
+  X(1, 128, 128, 2, 2, 0.958f)    \
+  X(2, 128, 64, 2, 2, 0.853f)     \
+  X(3, 64, 64, 2, 2, 0.713f)      \
+  X(4, 256, 128, 2, 4, 0.972f)    \
+  X(5, 128, 256, 2, 4, 1.00f)
+#define TABIT_DESC(I, BM, BN, WM, WN, RATE) {BM, BN, WM, WN, RATE},
 constexpr CfgDesc kCfgs[] = {TABIT_MX_CONFIGS(TABIT_DESC)};
 #undef TABIT_DESC
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
@@ -206,6 +215,9 @@ int mx_config_count() { return kNumCfgs; }
 
 GemmConfig mx_config(int index) { return GemmConfig{kCfgs[index].bm, kCfgs[index].bn, 1}; }
 
+// Same model as the INT8 GEMM's: the busiest CU runs ceil(tiles / CUs) tiles;
+// cost = that x BM x BN / rate, rates fitted to sweeps of every configuration
+// over the 4-bit layers' shapes on MI355X.
 int mx_config_choose(int M, int N, int K, int num_cus) {
   (void)K;
   if (num_cus <= 0) num_cus = 256;
@@ -214,9 +226,8 @@ int mx_config_choose(int M, int N, int K, int num_cus) {
   for (int i = 0; i < kNumCfgs; ++i) {
     const CfgDesc& c = kCfgs[i];
     const long long tiles = (long long)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
-    const long long per_round = (long long)num_cus * c.slots;
-    const long long rounds = (tiles + per_round - 1) / per_round;
-    const double cost = (double)rounds * c.slots * c.bm * c.bn / c.rate;
+    const long long per_cu = (tiles + num_cus - 1) / num_cus;
+    const double cost = (double)per_cu * c.bm * c.bn / c.rate;
     if (cost < best_cost * 0.999) {
       best_cost = cost;
       best = i;
@@ -229,7 +240,7 @@ hipError_t launch_gemm_mxfp4(int cfg, const uint8_t* xq, const uint8_t* xe, cons
                              const uint8_t* we, int M, int N, int K, float out_scale, uint16_t* y,
                              float* acc, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1,
                              const uint8_t* gate) {
-#define TABIT_CASE(I, BM, BN, WM, WN, SLOTS, RATE) \
+#define TABIT_CASE(I, BM, BN, WM, WN, RATE) \
   case I:                                           \
     return launch_cfg<BM, BN, WM, WN>(xq, xe, wq, we, M, N, K, out_scale, y, acc, stream, \
                                       ev0, ev1, gate);
