@@ -434,6 +434,38 @@ def mxfp4_gemm(x_fp4, x_e8m0, w_fp4, w_e8m0, out_scale: float) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# HQ-DM single Hadamard: rotate only the activations, keep the weights as they are
+# --------------------------------------------------------------------------
+#
+# HQ-DM section 2.1: the activations are multiplied by a block-diagonal
+# Hadamard H and quantized; the weights are left untransformed; inference
+# recovers X through the orthogonality of H, X_hat = S_XH (XH)_int H, with the
+# Hadamard normalization moved into the fp scale, so the core stays an integer
+# product.  With the unnormalized +-1 H (H H = b I): X ~ (s_a / b) Z with the
+# integer matrix Z = (XH)_int H, |Z| <= 127 b.  Z does not fit int8, so it is
+# split Z = 128 hi + lo (hi = floor(Z / 128), lo in [0, 127]) and the product
+# runs as two INT8 products against the TASQ-truncated, unrotated weights:
+# Z W_k^T = 128 (hi W_k^T) + lo W_k^T.
+
+
+def hqdm_quantize_act(x_bits: np.ndarray, had_block: int) -> Dict[str, np.ndarray]:
+    """Per token: codes of XH (as quantize_act_int8), Z = FWHT(codes), hi/lo planes, scale s_a / b."""
+    b = max(had_block, 1)
+    q, s_a = quantize_act_int8(x_bits, had_block)
+    z = block_fwht_f32(q.astype(np.float32), had_block).astype(np.int64)   # exact: |Z| <= 127 b < 2^24
+    hi = np.floor_divide(z, 128)
+    lo = z - 128 * hi
+    return {"q": q, "z": z, "hi": hi.astype(np.int8), "lo": lo.astype(np.int8),
+            "scale": (s_a / np.float32(b)).astype(np.float32)}
+
+
+def hqdm_gemm_i64(z: np.ndarray, w_q: np.ndarray, k: int) -> np.ndarray:
+    """Exact Z . W_k^T (int64), W_k the truncated, unrotated weight codes (TASQ section 2)."""
+    w = lsb_truncate(w_q, k).astype(np.int64)
+    return np.asarray(z, dtype=np.int64) @ w.T
+
+
+# --------------------------------------------------------------------------
 # DMPQ: the online INT8 / 4-bit selector (6Bit-Diffusion section 2A)
 # --------------------------------------------------------------------------
 #

@@ -298,6 +298,59 @@ def test_plane_gemm_brute_force(k):
     assert O.plane_gemm_i32(X, O.pack_weight_planes(Wq), k).tolist() == _brute_gemm(X, Wt)
 
 
+# ---------------------------------------------------------------- HQ-DM single Hadamard
+@pytest.mark.parametrize("b", [32, 64, 128])
+def test_hqdm_codes_unrotate_by_matrix(b):
+    """Z equals the codes times the explicit block-diagonal Sylvester matrix (exact integers)."""
+    x = S.gen_activation(5, 2 * b, seed=b)
+    r = O.hqdm_quantize_act(S.bf16_bits(x), b)
+    h = O.sylvester_hadamard(b).astype(np.int64)
+    blk = np.kron(np.eye(2, dtype=np.int64), h)
+    assert np.array_equal(r["z"], r["q"].astype(np.int64) @ blk)
+    assert np.array_equal(r["q"], O.quantize_act_int8(S.bf16_bits(x), b)[0])
+
+
+def test_hqdm_hi_lo_split_exhaustive():
+    z = np.arange(-127 * 128, 127 * 128 + 1, dtype=np.int64)
+    hi = np.floor_divide(z, 128)
+    lo = z - 128 * hi
+    assert hi.min() == -127 and hi.max() == 127 and lo.min() == 0 and lo.max() == 127   # both fit int8
+    assert np.array_equal(128 * hi + lo, z)
+    # the oracle's planes reproduce Z on real codes
+    r = O.hqdm_quantize_act(S.bf16_bits(S.gen_activation(9, 256, seed=2)), 128)
+    assert np.array_equal(128 * r["hi"].astype(np.int64) + r["lo"].astype(np.int64), r["z"])
+    assert r["lo"].min() >= 0
+
+
+@pytest.mark.parametrize("b", [32, 64, 128])
+def test_hqdm_recovers_activation_within_half_step(b):
+    """HQ-DM section 2.1 recovery: X_hat = (s_a / b) Z; each element is within s_a / 2 of X,
+    because the per-block code error (<= s_a/2 each) is mixed by H / b."""
+    x = S.gen_activation(6, 4 * b, seed=7 + b)
+    xf = O.bf16_to_f32(S.bf16_bits(x)).astype(np.float64)
+    r = O.hqdm_quantize_act(S.bf16_bits(x), b)
+    s_a = r["scale"].astype(np.float64) * b
+    xhat = r["scale"].astype(np.float64)[:, None] * r["z"]
+    assert np.all(np.abs(xf - xhat) <= s_a[:, None] * 0.5 * (1 + 1e-5) + 1e-30)
+
+
+@pytest.mark.parametrize("k", [0, 3, 7])
+def test_hqdm_gemm_brute_force(k):
+    z = S.gen_int8((3, 32), seed=41).astype(np.int64) * 97       # int14-range values
+    wq = S.gen_int8((4, 32), seed=42, lo=-128, hi=127)
+    ref = [[sum(int(z[m][j]) * ((int(wq[n][j]) >> k) << k) for j in range(32)) for n in range(4)]
+           for m in range(3)]
+    assert O.hqdm_gemm_i64(z, wq, k).tolist() == ref
+
+
+def test_hqdm_without_rotation_is_the_masked_gemm():
+    x = S.gen_activation(8, 96, seed=12)
+    wq = S.gen_int8((16, 96), seed=13, lo=-128, hi=127)
+    r = O.hqdm_quantize_act(S.bf16_bits(x), 0)
+    assert np.array_equal(r["z"], r["q"].astype(np.int64))
+    assert np.array_equal(O.hqdm_gemm_i64(r["z"], wq, 2), O.masked_gemm_i32(r["q"], wq, 2))
+
+
 # ---------------------------------------------------------------- DMPQ selector
 def _bf(vals):
     return S.bf16_bits(torch.tensor(vals, dtype=torch.float32).to(torch.bfloat16))
