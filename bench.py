@@ -497,7 +497,7 @@ def gemm_tiles(T, wl, tuned, path=0):
             name = f"{'mxfp4' if fmt else 'int8'} {layer.M}x{layer.N}x{layer.K}"
             if name in out:
                 continue
-            if fmt == 0 and path == T.PATH_PLANES:
+            if fmt == 0 and path in (T.PATH_PLANES, T.PATH_HQDM):
                 out[name] = "tuned" if key in tuned else "auto"
             elif fmt == 0:
                 cfg = tuned.get(key, T.gemm_config_choose(layer.M, layer.N, layer.K))
@@ -513,7 +513,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=5, help="timed schedule passes")
     ap.add_argument("--warmup", type=int, default=2, help="untimed schedule passes")
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
-    ap.add_argument("--path", default="masked", choices=["masked", "bitserial", "planes"])
+    ap.add_argument("--path", default="masked", choices=["masked", "bitserial", "planes", "hqdm"])
     ap.add_argument("--had-block", type=int, default=None, help="override the workload's block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="token rows per shape in the oracle sample")
@@ -580,7 +580,8 @@ def main() -> int:
     L, Tn = wl.num_layers, wl.steps
     ctx = T.Context()
     ctx.set_step_schedule(wl.k_bits, wl.fmt)
-    path = {"masked": T.PATH_MASKED, "bitserial": T.PATH_BITSERIAL, "planes": T.PATH_PLANES}[args.path]
+    path = {"masked": T.PATH_MASKED, "bitserial": T.PATH_BITSERIAL, "planes": T.PATH_PLANES,
+            "hqdm": T.PATH_HQDM}[args.path]
 
     # ---- weights: one shared INT8 buffer per layer (+ MX copy where scheduled)
     weights = []
@@ -588,7 +589,12 @@ def main() -> int:
         w = S.gen_weight(layer.N, layer.K, seed=li).to(dev)
         needs_mx = bool(wl.fmt[:, li].any())
         needs_i8 = bool((wl.fmt[:, li] == 0).any())
-        weights.append(ctx.quantize_weights(w, b, int8=needs_i8, mx=needs_mx))
+        if path == T.PATH_HQDM:                  # HQ-DM: INT8 weights stay unrotated
+            weights.append(ctx.quantize_weights(w, 0, int8=needs_i8, mx=False))
+            if needs_mx:
+                weights[-1].update(ctx.quantize_weights(w, b, int8=False, mx=True))
+        else:
+            weights.append(ctx.quantize_weights(w, b, int8=needs_i8, mx=needs_mx))
         if needs_i8 and path == T.PATH_PLANES:   # the same buffer stored plane by plane
             weights[-1]["w_planes"] = ctx.pack_weight_planes(weights[-1].pop("w_q"))
         del w
@@ -630,6 +636,8 @@ def main() -> int:
                 if key in tuned:
                     continue
                 x = xs[(0, layer.M, layer.K)]
+                if fmt == 0 and path == T.PATH_HQDM:
+                    continue                     # the HQ-DM GEMM has no autotune entry
                 if fmt == 0:
                     xq, xs_ = ctx.hadamard_quant_act(x, b, T.FMT_INT8)
                     tuned[key] = ctx.autotune_gemm(path, xq, xs_,
@@ -730,7 +738,8 @@ def main() -> int:
                         "traffic": recorded_traffic(wl.name, args.path),
                         "kernel": {T.PATH_MASKED: "gemm_i8_kernel (masked)",
                                    T.PATH_BITSERIAL: "gemm_i8_kernel (bitserial)",
-                                   T.PATH_PLANES: "gemm_planes_kernel"}[path],
+                                   T.PATH_PLANES: "gemm_planes_kernel",
+                                   T.PATH_HQDM: "gemm_hqdm_kernel"}[path],
                         "avg_launch_us": round(gemm_ms_i8 * 1e3 / n_i8, 3),
                         "timing": "start/stop events of each GEMM dispatch (hipExtLaunchKernel)"}
             detail["gemm_int8_ms_per_step"] = round(gemm_ms_i8 / args.steps, 3)

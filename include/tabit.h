@@ -69,7 +69,12 @@ enum tabit_status {
 };
 
 enum tabit_fmt { TABIT_FMT_INT8 = 0, TABIT_FMT_MXFP4 = 1 };
-enum tabit_path { TABIT_PATH_MASKED = 0, TABIT_PATH_BITSERIAL = 1, TABIT_PATH_PLANES = 3 };
+enum tabit_path {
+  TABIT_PATH_MASKED = 0,
+  TABIT_PATH_BITSERIAL = 1,
+  TABIT_PATH_PLANES = 3,
+  TABIT_PATH_HQDM = 4
+};
 
 /* Create / destroy a context (host memory only; makes no HIP call).
  * tabit_create returns TABIT_EINVAL if out is NULL, TABIT_ENOMEM on failure. */
@@ -201,6 +206,34 @@ int tabit_plane_qgemm(tabit_ctx* ctx, const int8_t* x_q, const float* x_scale,
                       int k_bits, uint16_t* y_bf16, int32_t* acc, void* stream);
 
 /*
+ * HQ-DM single-Hadamard activation quantizer (HQ-DM section 2.1: only the
+ * activations are rotated; inference recovers X_hat = S (XH)_int H, the
+ * Hadamard normalization living in the fp scale).  Per token m: codes q of
+ * blockFWHT_b(x_m) exactly as tabit_hadamard_quant_act (INT8), then
+ * Z = blockFWHT_b(q) (integers, |Z| <= 127 b), written as two planes
+ * Z = 128 * x_hi + x_lo (x_hi = floor(Z / 128), x_lo in [0, 127]);
+ * x_scale[m] = (a / 127) / max(b, 1), so X ~ x_scale * Z.
+ *   x_bf16 device [M][K]; x_hi, x_lo device int8 [M][K]; x_scale fp32 [M].
+ */
+int tabit_hqdm_quant_act(tabit_ctx* ctx, const uint16_t* x_bf16, int M, int K, int had_block,
+                         int8_t* x_hi, int8_t* x_lo, float* x_scale, void* stream);
+
+/*
+ * HQ-DM single-Hadamard GEMM against the untransformed weights (quantized with
+ * had_block = 0), with the TASQ LSB mask (TASQ section 2):
+ *   acc[m][n] = sum_k Z[m][k] * ((w_q[n][k] >> k_bits) << k_bits),
+ *               Z = 128 x_hi + x_lo, computed as two INT8 products (exact)
+ *   y[m][n]   = bf16_rne(((float)acc[m][n] * x_scale[m]) * w_scale[n])
+ *   acc device int64 [M][N] (may be NULL), y_bf16 device [M][N] (may be NULL),
+ *   at least one.  Other arguments, layouts and errors as tabit_masked_qgemm.
+ * tabit_scheduled_linear / tabit_run_schedule run this pair for INT8 steps
+ * with path = TABIT_PATH_HQDM (w_q then holds unrotated codes).
+ */
+int tabit_hqdm_qgemm(tabit_ctx* ctx, const int8_t* x_hi, const int8_t* x_lo, const float* x_scale,
+                     const int8_t* w_q, const float* w_scale, int M, int N, int K, int k_bits,
+                     uint16_t* y_bf16, int64_t* acc, void* stream);
+
+/*
  * MXFP4 (W4A4) GEMM for layer-steps scheduled to 4 bits (6Bit-Diffusion
  * section 2A).  acc[m][n] = sum over 32-blocks j of 2^(xe[m][j] + we[n][j] - 254)
  * * sum_i e2m1(x)*e2m1(w), accumulated in fp32 by the scaled matrix cores
@@ -214,7 +247,8 @@ int tabit_mxfp4_qgemm(tabit_ctx* ctx, const uint8_t* x_fp4, const uint8_t* x_e8m
                       float out_scale, uint16_t* y_bf16, float* acc_f32, void* stream);
 
 /* Bytes of device workspace tabit_scheduled_linear needs for M x K activations
- * (quantized codes plus scales, either format). */
+ * (quantized codes -- two int8 planes on the HQ-DM path -- plus scales, any
+ * format). */
 size_t tabit_act_workspace_bytes(int M, int K);
 
 /*
@@ -223,8 +257,10 @@ size_t tabit_act_workspace_bytes(int M, int K);
  * switching overhead -- here a switch is one table lookup and a scalar kernel
  * argument.  Looks up (k, fmt); INT8: quantizes x into act_ws and runs the
  * masked GEMM (path = TABIT_PATH_MASKED), the bit-plane GEMM
- * (TABIT_PATH_BITSERIAL) or the plane-major GEMM (TABIT_PATH_PLANES: w_q then
- * points at the words of tabit_pack_weight_planes) with k; MXFP4: MX-quantizes x and runs the MXFP4 GEMM
+ * (TABIT_PATH_BITSERIAL), the plane-major GEMM (TABIT_PATH_PLANES: w_q then
+ * points at the words of tabit_pack_weight_planes) or HQ-DM's single-Hadamard
+ * pair (TABIT_PATH_HQDM: tabit_hqdm_quant_act + tabit_hqdm_qgemm, w_q holding
+ * unrotated codes) with k; MXFP4: MX-quantizes x and runs the MXFP4 GEMM
  * with out_scale 1/max(had_block, 1).
  *   w_q/w_scale required for INT8 steps, w_fp4/w_e8m0 for MXFP4 steps.
  *   act_ws device workspace of at least tabit_act_workspace_bytes(M, K),
@@ -329,10 +365,15 @@ int tabit_autotune_gemm(tabit_ctx* ctx, int path, const void* x_q, const void* x
 /*
  * Options (tests and tuning).  TABIT_OPT_GEMM_CONFIG forces the INT8 GEMM tile
  * configuration (value = index from tabit_gemm_config_info, -1 = automatic);
- * TABIT_OPT_MXFP4_CONFIG and TABIT_OPT_PLANE_CONFIG likewise for the MXFP4 and
- * plane-major GEMMs.  EINVAL for an unknown option or value.  Makes no HIP call.
+ * TABIT_OPT_MXFP4_CONFIG, TABIT_OPT_PLANE_CONFIG and TABIT_OPT_HQDM_CONFIG
+ * likewise for the MXFP4, plane-major and HQ-DM GEMMs.  EINVAL for an unknown option or value.  Makes no HIP call.
  */
-enum tabit_option { TABIT_OPT_GEMM_CONFIG = 0, TABIT_OPT_MXFP4_CONFIG = 1, TABIT_OPT_PLANE_CONFIG = 2 };
+enum tabit_option {
+  TABIT_OPT_GEMM_CONFIG = 0,
+  TABIT_OPT_MXFP4_CONFIG = 1,
+  TABIT_OPT_PLANE_CONFIG = 2,
+  TABIT_OPT_HQDM_CONFIG = 3
+};
 int tabit_set_option(tabit_ctx* ctx, int option, int value);
 
 /* Describe INT8 GEMM tile configuration `index` (0 <= index < count): block
@@ -345,6 +386,9 @@ int tabit_mxfp4_config_info(int index, int* bm, int* bn);
 
 /* As tabit_mxfp4_config_info, for the plane-major GEMM's tile configurations. */
 int tabit_plane_config_info(int index, int* bm, int* bn);
+
+/* As tabit_mxfp4_config_info, for the HQ-DM GEMM's tile configurations. */
+int tabit_hqdm_config_info(int index, int* bm, int* bn);
 
 /* The configuration the automatic choice would take for (M, N, K) on a device
  * with num_cus compute units (num_cus <= 0: 256).  Makes no HIP call. */

@@ -143,6 +143,26 @@ def test_gated_linear_validation(lib, ctx):
     assert g(M=0) == T.OK
 
 
+def test_hqdm_validation(lib, ctx):
+    def q(M=4, K=64, b=32, hi=FAKE, lo=FAKE, sc=FAKE):
+        return lib.tabit_hqdm_quant_act(ctx.handle, FAKE, M, K, b, hi, lo, sc, None)
+    assert q(lo=None) == T.EINVAL
+    assert q(b=16) == T.ERANGE
+    assert q(K=48) == T.ESHAPE
+    assert q(hi=MISALIGNED) == T.EALIGN
+    assert q(M=0) == T.OK
+
+    def g(M=8, N=32, K=64, k=0, lo=FAKE, y=FAKE, acc=None):
+        return lib.tabit_hqdm_qgemm(ctx.handle, FAKE, lo, FAKE, FAKE, FAKE, M, N, K, k, y, acc, None)
+    assert g(lo=None) == T.EINVAL
+    assert g(y=None) == T.EINVAL
+    assert g(k=8) == T.ERANGE
+    assert g(N=40) == T.ESHAPE
+    assert g(lo=MISALIGNED) == T.EALIGN
+    assert g(M=0) == T.OK
+    assert T.hqdm_config_info() >= 1
+
+
 def test_quant_act_validation(lib, ctx):
     def q(M=4, K=64, b=0, fmt=0, x=FAKE, xq=FAKE, xs=FAKE):
         return lib.tabit_hadamard_quant_act(ctx.handle, x, M, K, b, fmt, xq, xs, None)

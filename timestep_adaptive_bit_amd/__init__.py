@@ -11,8 +11,8 @@ from ._lib import (  # noqa: F401
     dmpq_workspace_bytes,
     header_functions, LIB_PATH,
     OK, EINVAL, ESHAPE, EALIGN, ERANGE, ENOSCHED, EHIP, ENOMEM,
-    FMT_INT8, FMT_MXFP4, PATH_MASKED, PATH_BITSERIAL, PATH_PLANES, PATH_MXFP4_GEMM,
-    OPT_GEMM_CONFIG, OPT_MXFP4_CONFIG, OPT_PLANE_CONFIG,
+    FMT_INT8, FMT_MXFP4, PATH_MASKED, PATH_BITSERIAL, PATH_PLANES, PATH_HQDM, PATH_MXFP4_GEMM,
+    OPT_GEMM_CONFIG, OPT_MXFP4_CONFIG, OPT_PLANE_CONFIG, OPT_HQDM_CONFIG, hqdm_config_info,
 )
 
 __all__ = [
@@ -20,4 +20,5 @@ __all__ = [
     "gemm_config_choose", "header_functions", "FMT_INT8", "FMT_MXFP4", "PATH_MASKED",
     "PATH_BITSERIAL", "PATH_PLANES", "OPT_GEMM_CONFIG", "OPT_MXFP4_CONFIG", "OPT_PLANE_CONFIG",
     "plane_config_info", "weight_planes_bytes", "dmpq_workspace_bytes",
+    "PATH_HQDM", "OPT_HQDM_CONFIG", "hqdm_config_info",
 ]

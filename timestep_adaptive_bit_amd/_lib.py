@@ -20,8 +20,8 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "tabit.h")
 
 OK, EINVAL, ESHAPE, EALIGN, ERANGE, ENOSCHED, EHIP, ENOMEM = 0, -1, -2, -3, -4, -5, -6, -7
 FMT_INT8, FMT_MXFP4 = 0, 1
-PATH_MASKED, PATH_BITSERIAL, PATH_PLANES = 0, 1, 3
-OPT_GEMM_CONFIG, OPT_MXFP4_CONFIG, OPT_PLANE_CONFIG = 0, 1, 2
+PATH_MASKED, PATH_BITSERIAL, PATH_PLANES, PATH_HQDM = 0, 1, 3, 4
+OPT_GEMM_CONFIG, OPT_MXFP4_CONFIG, OPT_PLANE_CONFIG, OPT_HQDM_CONFIG = 0, 1, 2, 3
 PATH_MXFP4_GEMM = 2
 
 _c_int, _c_void_p, _c_size_t, _c_float = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
@@ -66,6 +66,11 @@ _SIGNATURES = {
     "tabit_plane_config_info": (_c_int, [_c_int, _PINT, _PINT]),
     "tabit_weight_planes_bytes": (_c_size_t, [_c_int, _c_int]),
     "tabit_dmpq_workspace_bytes": (_c_size_t, [_c_int]),
+    "tabit_hqdm_quant_act": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p,
+                                      _c_void_p, _c_void_p, _c_void_p]),
+    "tabit_hqdm_qgemm": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                  _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
+    "tabit_hqdm_config_info": (_c_int, [_c_int, _PINT, _PINT]),
     "tabit_dmpq_select": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_void_p,
                                    _c_int, _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
     "tabit_gated_linear": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_void_p, _c_int, _c_int,
@@ -165,6 +170,18 @@ def mxfp4_config_info(index: int = -1):
         return int(lib.tabit_mxfp4_config_info(-1, None, None))
     bm, bn = ctypes.c_int(), ctypes.c_int()
     st = lib.tabit_mxfp4_config_info(index, ctypes.byref(bm), ctypes.byref(bn))
+    if st != OK:
+        raise TabitError(st, "bad config index")
+    return bm.value, bn.value
+
+
+def hqdm_config_info(index: int = -1):
+    """Number of HQ-DM GEMM configs (index < 0) or (bm, bn) of one."""
+    lib = load()
+    if index < 0:
+        return int(lib.tabit_hqdm_config_info(-1, None, None))
+    bm, bn = ctypes.c_int(), ctypes.c_int()
+    st = lib.tabit_hqdm_config_info(index, ctypes.byref(bm), ctypes.byref(bn))
     if st != OK:
         raise TabitError(st, "bad config index")
     return bm.value, bn.value
@@ -335,6 +352,39 @@ class Context:
                         want_acc=False):
         return self._gemm_i8(self._lib.tabit_qgemm_bitserial, x_q, x_scale, w_q, w_scale, k_bits, y,
                              acc, want_y, want_acc)
+
+    def hqdm_quant_act(self, x: torch.Tensor, had_block: int):
+        """HQ-DM single-Hadamard codes: (x_hi int8 [M,K], x_lo int8 [M,K], x_scale fp32 [M])."""
+        _dev(x, torch.bfloat16, "x")
+        M, K = x.shape
+        hi = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        lo = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        sc = torch.empty((M,), dtype=torch.float32, device=x.device)
+        st = self._lib.tabit_hqdm_quant_act(self._h, x.data_ptr(), M, K, had_block, hi.data_ptr(),
+                                            lo.data_ptr(), sc.data_ptr(), _stream(x.device))
+        self._check(st)
+        return hi, lo, sc
+
+    def hqdm_qgemm(self, x_hi, x_lo, x_scale, w_q, w_scale, k_bits, y=None, want_y=True,
+                   want_acc=False):
+        """y bf16 [M,N] and/or the exact int64 accumulator of Z . W_k^T."""
+        _dev(x_hi, torch.int8, "x_hi")
+        M, K = x_hi.shape
+        _dev(x_lo, torch.int8, "x_lo", (M, K))
+        _dev(w_q, torch.int8, "w_q")
+        N = w_q.shape[0]
+        if w_q.shape[1] != K:
+            raise ValueError("x and w_q disagree on K")
+        _dev(x_scale, torch.float32, "x_scale", (M,))
+        _dev(w_scale, torch.float32, "w_scale", (N,))
+        if want_y and y is None:
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=x_hi.device)
+        acc = torch.empty((M, N), dtype=torch.int64, device=x_hi.device) if want_acc else None
+        st = self._lib.tabit_hqdm_qgemm(self._h, x_hi.data_ptr(), x_lo.data_ptr(), x_scale.data_ptr(),
+                                        w_q.data_ptr(), w_scale.data_ptr(), M, N, K, k_bits, _ptr(y),
+                                        _ptr(acc), _stream(x_hi.device))
+        self._check(st)
+        return y, acc
 
     def pack_weight_planes(self, w_q: torch.Tensor, out: Optional[torch.Tensor] = None):
         """Plane-major copy of int8 codes [N][K]: int32 tensor [8][ceil(K/128)][N][4] (uint32 words)."""

@@ -93,7 +93,14 @@ hipError_t launch_int8_family(const tabit_ctx* ctx, int path, const int8_t* xq, 
 }
 
 bool valid_int8_path(int path) {
-  return path == TABIT_PATH_MASKED || path == TABIT_PATH_BITSERIAL || path == TABIT_PATH_PLANES;
+  return path == TABIT_PATH_MASKED || path == TABIT_PATH_BITSERIAL || path == TABIT_PATH_PLANES ||
+         path == TABIT_PATH_HQDM;
+}
+
+int hqdm_cfg(const tabit_ctx* ctx, int M, int N, int K, int num_cus) {
+  int cfg = ctx->force_hqdm_cfg;
+  if (cfg < 0) cfg = tabit::hqdm_config_choose(M, N, K, num_cus);
+  return cfg;
 }
 
 int gemm_i8_common(tabit_ctx* ctx, int path, const int8_t* x_q, const float* x_scale,
@@ -320,10 +327,58 @@ int tabit_mxfp4_qgemm(tabit_ctx* ctx, const uint8_t* x_fp4, const uint8_t* x_e8m
                     "mxfp4_qgemm launch");
 }
 
+int tabit_hqdm_quant_act(tabit_ctx* ctx, const uint16_t* x_bf16, int M, int K, int had_block,
+                         int8_t* x_hi, int8_t* x_lo, float* x_scale, void* stream) {
+  if (ctx == nullptr) return TABIT_EINVAL;
+  if (x_bf16 == nullptr || x_hi == nullptr || x_lo == nullptr || x_scale == nullptr)
+    return fail(ctx, TABIT_EINVAL, "null pointer");
+  int st = check_k_shape(ctx, M, K, had_block);
+  if (st != TABIT_OK) return st;
+  if ((size_t)M * (size_t)K > kMaxOperandBytes)
+    return fail(ctx, TABIT_ESHAPE, "activations must stay below 2 GiB");
+  if (!aligned(x_bf16, 16) || !aligned(x_hi, 16) || !aligned(x_lo, 16) || !aligned(x_scale, 4))
+    return fail(ctx, TABIT_EALIGN, "misaligned pointer");
+  if (M == 0) return TABIT_OK;
+  return hip_status(ctx,
+                    tabit::launch_quant_hqdm(x_bf16, M, K, had_block, x_hi, x_lo, x_scale,
+                                             static_cast<hipStream_t>(stream)),
+                    "hqdm_quant_act launch");
+}
+
+int tabit_hqdm_qgemm(tabit_ctx* ctx, const int8_t* x_hi, const int8_t* x_lo, const float* x_scale,
+                     const int8_t* w_q, const float* w_scale, int M, int N, int K, int k_bits,
+                     uint16_t* y_bf16, int64_t* acc, void* stream) {
+  if (ctx == nullptr) return TABIT_EINVAL;
+  if (x_lo == nullptr) return fail(ctx, TABIT_EINVAL, "null input pointer");
+  int st = check_gemm(ctx, x_hi, x_scale, w_q, w_scale, M, N, K, y_bf16, acc);
+  if (st != TABIT_OK) return st;
+  if (!aligned(x_lo, 16)) return fail(ctx, TABIT_EALIGN, "matrices must be 16-byte aligned");
+  if (!aligned(x_scale, 4) || !aligned(w_scale, 4))
+    return fail(ctx, TABIT_EALIGN, "scales must be 4-byte aligned");
+  if (k_bits < 0 || k_bits > 7) return fail(ctx, TABIT_ERANGE, "k_bits must be in [0, 7] (got %d)", k_bits);
+  if (M == 0 || N == 0) return TABIT_OK;
+  const int num_cus = tabit::device_num_cus();
+  return hip_status(ctx,
+                    tabit::launch_gemm_hqdm(hqdm_cfg(ctx, M, N, K, num_cus), x_hi, x_lo, x_scale,
+                                            w_q, w_scale, M, N, K, k_bits, y_bf16,
+                                            reinterpret_cast<long long*>(acc),
+                                            static_cast<hipStream_t>(stream)),
+                    "hqdm_qgemm launch");
+}
+
+int tabit_hqdm_config_info(int index, int* bm, int* bn) {
+  if (index < 0) return tabit::hqdm_config_count();
+  if (index >= tabit::hqdm_config_count() || bm == nullptr || bn == nullptr) return TABIT_EINVAL;
+  const tabit::GemmConfig c = tabit::hqdm_config(index);
+  *bm = c.bm;
+  *bn = c.bn;
+  return TABIT_OK;
+}
+
 size_t tabit_act_workspace_bytes(int M, int K) {
   if (M <= 0 || K <= 0) return 0;
   const size_t mk = (size_t)M * (size_t)K;
-  const size_t i8 = align256(mk) + align256((size_t)M * 4);
+  const size_t i8 = 2 * align256(mk) + align256((size_t)M * 4);   // HQ-DM: two planes
   const size_t mx = align256(mk / 2) + align256(mk / 32);
   return i8 > mx ? i8 : mx;
 }
@@ -361,7 +416,13 @@ int tabit_scheduled_linear(tabit_ctx* ctx, int step, int layer, int path, const 
   const size_t mk = (size_t)M * (size_t)K;
   if (fmt == TABIT_FMT_INT8) {
     int8_t* xq = reinterpret_cast<int8_t*>(ws);
-    float* sa = reinterpret_cast<float*>(ws + align256(mk));
+    float* sa = reinterpret_cast<float*>(ws + 2 * align256(mk));
+    if (path == TABIT_PATH_HQDM) {
+      int8_t* xl = reinterpret_cast<int8_t*>(ws + align256(mk));
+      st = tabit_hqdm_quant_act(ctx, x_bf16, M, K, had_block, xq, xl, sa, stream);
+      if (st != TABIT_OK) return st;
+      return tabit_hqdm_qgemm(ctx, xq, xl, sa, w_q, w_scale, M, N, K, k, y_bf16, nullptr, stream);
+    }
     st = tabit_hadamard_quant_act(ctx, x_bf16, M, K, had_block, TABIT_FMT_INT8, xq, sa, stream);
     if (st != TABIT_OK) return st;
     return gemm_i8_common(ctx, path, xq, sa, w_q, w_scale, M, N, K, k, y_bf16, nullptr, stream);
@@ -436,7 +497,7 @@ int tabit_gated_linear(tabit_ctx* ctx, const uint8_t* fmt_dev, int k_bits, int p
   const int num_cus = tabit::device_num_cus();
   // INT8 branch: runs when *fmt_dev == TABIT_FMT_INT8
   int8_t* xq = reinterpret_cast<int8_t*>(ws);
-  float* sa = reinterpret_cast<float*>(ws + align256(mk));
+  float* sa = reinterpret_cast<float*>(ws + 2 * align256(mk));
   hipError_t e = tabit::launch_quant_int8(x_bf16, M, K, had_block, 1.0f, xq, sa, s, fmt_dev);
   if (e != hipSuccess) return hip_status(ctx, e, "gated quantizer launch");
   e = launch_int8_family(ctx, path, xq, sa, w_q, w_scale, M, N, K, k_bits, y_bf16, nullptr, s,
@@ -519,11 +580,20 @@ int tabit_run_schedule(tabit_ctx* ctx, int first_step, int num_steps, const tabi
       hipError_t e;
       if (ctx->fmt[i] == TABIT_FMT_INT8) {
         int8_t* xq = reinterpret_cast<int8_t*>(ws);
-        float* sa = reinterpret_cast<float*>(ws + align256(mk));
-        e = tabit::launch_quant_int8(x, L.M, L.K, had_block, 1.0f, xq, sa, s);
-        if (e != hipSuccess) return hip_status(ctx, e, "run_schedule quantizer launch");
-        e = launch_int8_family(ctx, path, xq, sa, L.w_q, L.w_scale, L.M, L.N, L.K, ctx->k_bits[i],
-                               L.y_bf16, nullptr, s, num_cus, e0, e1);
+        float* sa = reinterpret_cast<float*>(ws + 2 * align256(mk));
+        if (path == TABIT_PATH_HQDM) {
+          int8_t* xl = reinterpret_cast<int8_t*>(ws + align256(mk));
+          e = tabit::launch_quant_hqdm(x, L.M, L.K, had_block, xq, xl, sa, s);
+          if (e != hipSuccess) return hip_status(ctx, e, "run_schedule HQ-DM quantizer launch");
+          e = tabit::launch_gemm_hqdm(hqdm_cfg(ctx, L.M, L.N, L.K, num_cus), xq, xl, sa, L.w_q,
+                                      L.w_scale, L.M, L.N, L.K, ctx->k_bits[i], L.y_bf16, nullptr,
+                                      s, e0, e1);
+        } else {
+          e = tabit::launch_quant_int8(x, L.M, L.K, had_block, 1.0f, xq, sa, s);
+          if (e != hipSuccess) return hip_status(ctx, e, "run_schedule quantizer launch");
+          e = launch_int8_family(ctx, path, xq, sa, L.w_q, L.w_scale, L.M, L.N, L.K, ctx->k_bits[i],
+                                 L.y_bf16, nullptr, s, num_cus, e0, e1);
+        }
         if (e != hipSuccess) return hip_status(ctx, e, "run_schedule GEMM launch");
       } else {
         uint8_t* xf = ws;
@@ -623,6 +693,11 @@ int tabit_set_option(tabit_ctx* ctx, int option, int value) {
       if (value < -1 || value >= tabit::plane_config_count())
         return fail(ctx, TABIT_EINVAL, "plane GEMM config %d out of range", value);
       ctx->force_plane_cfg = value;
+      return TABIT_OK;
+    case TABIT_OPT_HQDM_CONFIG:
+      if (value < -1 || value >= tabit::hqdm_config_count())
+        return fail(ctx, TABIT_EINVAL, "HQ-DM GEMM config %d out of range", value);
+      ctx->force_hqdm_cfg = value;
       return TABIT_OK;
     default:
       return fail(ctx, TABIT_EINVAL, "unknown option %d", option);

@@ -101,10 +101,15 @@ __device__ __forceinline__ int row_of(int c, int cr, float inv_cr) {
   return r;
 }
 
-template <int B, int NT, int CPT>
+// HQ = false: codes of the rotated row.  HQ = true (HQ-DM single Hadamard):
+// the codes are rotated back by the same block FWHT -- integers up to 127 b in
+// magnitude, exact in fp32 -- and written as two int8 planes Z = 128 hi + lo
+// (hi = floor(Z / 128) to q, lo in [0, 127] to q_lo).
+template <int B, int NT, int CPT, bool HQ>
 __global__ void __launch_bounds__(NT)
 quant_int8_kernel(const uint16_t* __restrict__ x, int M, int K, int rows_per_wg, float scale_div,
-                  int8_t* __restrict__ q, float* __restrict__ scale, const uint8_t* __restrict__ gate) {
+                  int8_t* __restrict__ q, float* __restrict__ scale, const uint8_t* __restrict__ gate,
+                  int8_t* __restrict__ q_lo) {
   if (gate != nullptr && *gate != 0) return;   // device-selected format is not INT8
   __shared__ unsigned s_amax[NT * CPT / 2];
   __shared__ float s_r[NT * CPT / 2];
@@ -152,17 +157,45 @@ quant_int8_kernel(const uint16_t* __restrict__ x, int M, int K, int rows_per_wg,
   }
   __syncthreads();
 
+  if constexpr (!HQ) {
 #pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int c = i * NT + tid;
-    if (c < nchunks) {
-      const float r = s_r[row_of(c, cr, inv_cr)];
-      uint4 o;
-      o.x = pack4_i8(v[i][0], v[i][1], v[i][2], v[i][3], r);
-      o.y = pack4_i8(v[i][4], v[i][5], v[i][6], v[i][7], r);
-      o.z = pack4_i8(v[i][8], v[i][9], v[i][10], v[i][11], r);
-      o.w = pack4_i8(v[i][12], v[i][13], v[i][14], v[i][15], r);
-      *reinterpret_cast<uint4*>(q + base + (size_t)c * 16) = o;
+    for (int i = 0; i < CPT; ++i) {
+      const int c = i * NT + tid;
+      if (c < nchunks) {
+        const float r = s_r[row_of(c, cr, inv_cr)];
+        uint4 o;
+        o.x = pack4_i8(v[i][0], v[i][1], v[i][2], v[i][3], r);
+        o.y = pack4_i8(v[i][4], v[i][5], v[i][6], v[i][7], r);
+        o.z = pack4_i8(v[i][8], v[i][9], v[i][10], v[i][11], r);
+        o.w = pack4_i8(v[i][12], v[i][13], v[i][14], v[i][15], r);
+        *reinterpret_cast<uint4*>(q + base + (size_t)c * 16) = o;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = i * NT + tid;
+      const float r = c < nchunks ? s_r[row_of(c, cr, inv_cr)] : 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e)   // the codes, as pack4_i8 forms them
+        v[i][e] = __builtin_amdgcn_fmed3f(rintf(v[i][e] * r), -127.0f, 127.0f);
+      fwht_chunk<B>(v[i], lane);      // every lane: the cross-lane stages need all of them
+      if (c < nchunks) {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          hw[d] = 0u;
+          lw[d] = 0u;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int z = (int)v[i][4 * d + e];
+            hw[d] |= (uint32_t)((z >> 7) & 0xFF) << (8 * e);
+            lw[d] |= (uint32_t)(z & 127) << (8 * e);
+          }
+        }
+        *reinterpret_cast<uint4*>(q + base + (size_t)c * 16) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        *reinterpret_cast<uint4*>(q_lo + base + (size_t)c * 16) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      }
     }
   }
 }
@@ -224,13 +257,15 @@ quant_mx_kernel(const uint16_t* __restrict__ x, long long nchunks, uint8_t* __re
   }
 }
 
-template <int B>
+template <int B, bool HQ>
 hipError_t dispatch_int8(int nt, int cpt, int grid, int rows, const uint16_t* x, int M, int K,
-                         float scale_div, int8_t* q, float* scale, hipStream_t s, const uint8_t* gate) {
-#define TABIT_Q(NT_, CPT_)                                                                   \
-  if (nt == NT_ && cpt == CPT_) {                                                            \
-    quant_int8_kernel<B, NT_, CPT_><<<grid, NT_, 0, s>>>(x, M, K, rows, scale_div, q, scale, gate); \
-    return hipGetLastError();                                                                \
+                         float scale_div, int8_t* q, float* scale, hipStream_t s, const uint8_t* gate,
+                         int8_t* q_lo) {
+#define TABIT_Q(NT_, CPT_)                                                                      \
+  if (nt == NT_ && cpt == CPT_) {                                                               \
+    quant_int8_kernel<B, NT_, CPT_, HQ><<<grid, NT_, 0, s>>>(x, M, K, rows, scale_div, q, scale, \
+                                                             gate, q_lo);                       \
+    return hipGetLastError();                                                                   \
   }
   TABIT_Q(256, 1) TABIT_Q(512, 1) TABIT_Q(1024, 1) TABIT_Q(1024, 2)
 #undef TABIT_Q
@@ -239,16 +274,20 @@ hipError_t dispatch_int8(int nt, int cpt, int grid, int rows, const uint16_t* x,
 
 }  // namespace
 
-hipError_t launch_quant_int8(const uint16_t* x, int M, int K, int had_block, float scale_div,
-                             int8_t* q, float* scale, hipStream_t stream, const uint8_t* gate) {
+namespace {
+
+// Workgroup shape: one 16-element chunk per thread and as few rows per
+// workgroup as fill it (256 threads for rows of up to 256 chunks, else the
+// next power of two; two chunks per thread past 1024 chunks).  Small
+// workgroups with few registers outnumber the resident slots, so reads of
+// late workgroups overlap the stores of early ones; on MI355X this beat
+// fuller multi-row, multi-chunk shapes by 7-32% at the workloads' sizes.
+template <bool HQ>
+hipError_t launch_int8_rows(const uint16_t* x, int M, int K, int had_block, float scale_div,
+                            int8_t* q, float* scale, hipStream_t stream, const uint8_t* gate,
+                            int8_t* q_lo) {
   if (M <= 0) return hipSuccess;
   const int cr = K / 16;
-  // Workgroup shape: one 16-element chunk per thread and as few rows per
-  // workgroup as fill it (256 threads for rows of up to 256 chunks, else the
-  // next power of two; two chunks per thread past 1024 chunks).  Small
-  // workgroups with few registers outnumber the resident slots, so reads of
-  // late workgroups overlap the stores of early ones; on MI355X this beat
-  // fuller multi-row, multi-chunk shapes by 7-32% at the workloads' sizes.
   int nt = 1024, cpt = 1;
   if (cr <= 256) nt = 256;
   else if (cr <= 512) nt = 512;
@@ -256,11 +295,24 @@ hipError_t launch_quant_int8(const uint16_t* x, int M, int K, int had_block, flo
   const int rows = (nt * cpt) / cr;
   const int grid = (M + rows - 1) / rows;
   switch (had_block) {
-    case 0: return dispatch_int8<0>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream, gate);
-    case 32: return dispatch_int8<32>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream, gate);
-    case 64: return dispatch_int8<64>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream, gate);
-    default: return dispatch_int8<128>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream, gate);
+    case 0: return dispatch_int8<0, HQ>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream, gate, q_lo);
+    case 32: return dispatch_int8<32, HQ>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream, gate, q_lo);
+    case 64: return dispatch_int8<64, HQ>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream, gate, q_lo);
+    default: return dispatch_int8<128, HQ>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream, gate, q_lo);
   }
+}
+
+}  // namespace
+
+hipError_t launch_quant_int8(const uint16_t* x, int M, int K, int had_block, float scale_div,
+                             int8_t* q, float* scale, hipStream_t stream, const uint8_t* gate) {
+  return launch_int8_rows<false>(x, M, K, had_block, scale_div, q, scale, stream, gate, nullptr);
+}
+
+hipError_t launch_quant_hqdm(const uint16_t* x, int M, int K, int had_block, int8_t* q_hi,
+                             int8_t* q_lo, float* scale, hipStream_t stream, const uint8_t* gate) {
+  const float div = (float)(had_block > 0 ? had_block : 1);   // X ~ (s_a / b) Z
+  return launch_int8_rows<true>(x, M, K, had_block, div, q_hi, scale, stream, gate, q_lo);
 }
 
 hipError_t launch_quant_mx(const uint16_t* x, int M, int K, int had_block, uint8_t* q_fp4,

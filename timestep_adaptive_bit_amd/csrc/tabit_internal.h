@@ -24,6 +24,12 @@ hipError_t launch_quant_int8(const uint16_t* x, int M, int K, int had_block, flo
                              int8_t* q, float* scale, hipStream_t stream,
                              const uint8_t* gate = nullptr);
 
+// HQ-DM single Hadamard: codes of the rotated row rotated back, Z = 128 hi + lo
+// as two int8 planes; scale = (a / 127) / max(b, 1).
+hipError_t launch_quant_hqdm(const uint16_t* x, int M, int K, int had_block, int8_t* q_hi,
+                             int8_t* q_lo, float* scale, hipStream_t stream,
+                             const uint8_t* gate = nullptr);
+
 // MXFP4 quantization (block 32, optional FWHT32).
 hipError_t launch_quant_mx(const uint16_t* x, int M, int K, int had_block,
                            uint8_t* q_fp4, uint8_t* e8m0, hipStream_t stream,
@@ -68,6 +74,15 @@ hipError_t launch_gemm_planes(int cfg, const int8_t* xq, const float* sa, const 
                               int32_t* acc, hipStream_t stream, hipEvent_t ev0 = nullptr,
                               hipEvent_t ev1 = nullptr, const uint8_t* gate = nullptr);
 
+// ---------------------------------------------------------------- HQ-DM single-Hadamard GEMM
+int hqdm_config_count();
+GemmConfig hqdm_config(int index);
+int hqdm_config_choose(int M, int N, int K, int num_cus);
+hipError_t launch_gemm_hqdm(int cfg, const int8_t* xh, const int8_t* xl, const float* sa,
+                            const int8_t* wq, const float* sw, int M, int N, int K, int kbits,
+                            uint16_t* y, long long* acc, hipStream_t stream,
+                            hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+
 // ---------------------------------------------------------------- DMPQ selector
 // Gamma = sum |out - in| / sum |in| of a block's hidden states in the fixed
 // fp64 order; fmt[l] = Gamma > theta[l] ? INT8 : MXFP4.  rows: M x 2 doubles.
@@ -90,6 +105,7 @@ struct tabit_ctx {
   int force_gemm_cfg = -1;
   int force_mx_cfg = -1;
   int force_plane_cfg = -1;
+  int force_hqdm_cfg = -1;
   // autotuned tile configuration per (path, M, N, K); path 2 = MXFP4, 3 = plane-major
   std::map<std::tuple<int, int, int, int>, int> tuned;
 
