@@ -434,6 +434,61 @@ def mxfp4_gemm(x_fp4, x_e8m0, w_fp4, w_e8m0, out_scale: float) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# Producer-fused quantization: GELU folded into the MLP-down activation quantizer
+# --------------------------------------------------------------------------
+#
+# The MLP's down projection consumes GELU(up-projection output).  Folding the
+# GELU into the quantizer that feeds the down projection removes a full read and
+# write of the 4H-wide activation.  The pages fix no activation function; the
+# DiT convention is GELU in its tanh form,
+#   gelu(x) = 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))),
+# evaluated here in fp32 from IEEE add, multiply, divide and exact power-of-two
+# scaling only (no library exp/tanh), so that a kernel taking the same steps in
+# the same order gives the same bits.  The result is rounded to bf16 -- the
+# precision an unfused pipeline would store it in -- and then quantized exactly
+# as quantize_act_int8 does.
+#
+# exp(v), |v| <= 40: n = rint(v log2 e); r = (v - n ln2_hi) - n ln2_lo (Cody-Waite
+# reduction, ln2_hi exact in 16 bits); e^r by its Taylor polynomial to degree 7
+# in Horner form; result = e^r * 2^n.
+_F = np.float32
+_LOG2E = _F(1.44269504088896341)
+_LN2_HI = _F(0.693145751953125)          # 16 significant bits: n * _LN2_HI is exact
+_LN2_LO = _F(1.42860682030941723e-06)
+_EXP_C = [_F(1.0 / 5040.0), _F(1.0 / 720.0), _F(1.0 / 120.0), _F(1.0 / 24.0), _F(1.0 / 6.0),
+          _F(0.5), _F(1.0), _F(1.0)]
+_GELU_C = _F(0.7978845608028654)          # sqrt(2 / pi)
+_GELU_A = _F(0.044715)
+
+
+def exp_f32(v: np.ndarray) -> np.ndarray:
+    """exp in fp32 by the steps above (|v| <= 40; the caller clamps)."""
+    v = np.asarray(v, dtype=np.float32)
+    n = np.rint(v * _LOG2E).astype(np.float32)
+    r = (v - n * _LN2_HI) - n * _LN2_LO
+    p = _EXP_C[0]
+    for c in _EXP_C[1:]:
+        p = p * r + c
+    return np.ldexp(p, n.astype(np.int32)).astype(np.float32)
+
+
+def gelu_tanh_f32(x: np.ndarray) -> np.ndarray:
+    """GELU (tanh form) in fp32: tanh(u) = sign(u) (1 - 2 / (exp(2 |u|) + 1)), |u| clamped to 20."""
+    x = np.asarray(x, dtype=np.float32)
+    u = _GELU_C * (x + _GELU_A * (x * x * x))
+    au = np.minimum(np.abs(u), _F(20.0))
+    t = _F(1.0) - _F(2.0) / (exp_f32(_F(2.0) * au) + _F(1.0))
+    t = np.where(u < 0, -t, t).astype(np.float32)
+    return (_F(0.5) * x) * (_F(1.0) + t)
+
+
+def quantize_act_gelu_int8(x_bits: np.ndarray, had_block: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Quantizer of the down projection's input: bf16(gelu(x)), then quantize_act_int8."""
+    g = gelu_tanh_f32(bf16_to_f32(np.asarray(x_bits)))
+    return quantize_act_int8(f32_to_bf16_bits(g), had_block)
+
+
+# --------------------------------------------------------------------------
 # HQ-DM single Hadamard: rotate only the activations, keep the weights as they are
 # --------------------------------------------------------------------------
 #

@@ -298,6 +298,37 @@ def test_plane_gemm_brute_force(k):
     assert O.plane_gemm_i32(X, O.pack_weight_planes(Wq), k).tolist() == _brute_gemm(X, Wt)
 
 
+# ---------------------------------------------------------------- fused GELU quantizer
+def test_exp_f32_within_two_ulp():
+    v = np.linspace(-40, 40, 400001).astype(np.float32)
+    e = O.exp_f32(v).astype(np.float64)
+    ref = np.array([math.exp(float(t)) for t in v[::97]])
+    assert np.all(np.abs(e[::97] - ref) <= 2.0 ** -22 * ref)        # within 2 ulp (relative)
+    assert O.exp_f32(np.float32(0.0)) == 1.0
+
+
+def test_gelu_tanh_against_closed_form():
+    x = np.linspace(-12, 12, 200001).astype(np.float32)
+    g = O.gelu_tanh_f32(x).astype(np.float64)
+    xd = x.astype(np.float64)
+    ref = 0.5 * xd * (1 + np.tanh(math.sqrt(2 / math.pi) * (xd + 0.044715 * xd ** 3)))
+    assert np.all(np.abs(g - ref) <= 1e-6 + 1e-4 * np.abs(ref))
+    assert O.gelu_tanh_f32(np.float32(0.0)) == 0.0
+    big = np.array([10.0, 37.5, 1e4], np.float32)
+    assert np.array_equal(O.gelu_tanh_f32(big), big)                  # tanh = 1 exactly
+    assert np.all(O.gelu_tanh_f32(-big) <= 0) and np.all(O.gelu_tanh_f32(-big) > -1e-6)
+
+
+def test_gelu_quant_is_identity_quant_on_large_inputs():
+    """For x >= 10 the fused GELU is exactly the identity, so the codes equal the plain quantizer's."""
+    x = (torch.rand(7, 128, generator=torch.Generator().manual_seed(3)) * 50 + 10).to(torch.bfloat16)
+    xb = S.bf16_bits(x)
+    for b in (0, 64):
+        q1, s1 = O.quantize_act_gelu_int8(xb, b)
+        q2, s2 = O.quantize_act_int8(xb, b)
+        assert np.array_equal(q1, q2) and np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+
+
 # ---------------------------------------------------------------- HQ-DM single Hadamard
 @pytest.mark.parametrize("b", [32, 64, 128])
 def test_hqdm_codes_unrotate_by_matrix(b):
