@@ -488,6 +488,49 @@ def quant_bandwidth(ctx, T, torch, wl, xs, b, act_ws) -> dict:
     return out
 
 
+def gelu_fusion_bench(T, torch, dev) -> dict:
+    """MLP-down input quantization with the GELU folded in, against the unfused
+    pipeline (a separate GELU pass -- torch's tanh GELU, bf16 in and out -- then
+    the plain quantizer) and the plain quantizer alone, at each workload's
+    down-projection input shape.  HIP events around 20 launches each."""
+    import tabit_synth as S
+    ctx = T.Context()
+    out = {}
+
+    def timed(fn, n=20):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+    for name in ("c2", "c3", "c5"):
+        wl = S.WORKLOADS[name]()
+        layer = [l for l in wl.layers if l.name.endswith("mlp_down")][0]
+        M, K, b = layer.M, layer.K, (wl.had_block if wl.had_block in (0, 32, 64, 128) else 0)
+        pre = (S.gen_activation(M, K, seed=5).float() * 2.0).to(torch.bfloat16).to(dev)
+        q = torch.empty((M, K), dtype=torch.int8, device=dev)
+        sc = torch.empty((M,), dtype=torch.float32, device=dev)
+        g = torch.nn.functional.gelu(pre, approximate="tanh")
+        fused = timed(lambda: ctx.gelu_quant_act(pre, b, q, sc))
+        gelu = timed(lambda: torch.nn.functional.gelu(pre, approximate="tanh"))
+        quant = timed(lambda: ctx.hadamard_quant_act(g, b, T.FMT_INT8, q, sc))
+        fused_bytes = 3 * M * K + 4 * M
+        unfused_bytes = fused_bytes + 4 * M * K
+        out[f"{wl.name} {M}x{K}"] = {
+            "fused_us": round(fused, 2), "quant_alone_us": round(quant, 2),
+            "unfused_gelu_plus_quant_us": round(gelu + quant, 2),
+            "fused_GBps": round(fused_bytes / fused / 1e3, 1),
+            "hbm_bytes_fused": fused_bytes, "hbm_bytes_unfused": unfused_bytes}
+        del pre, q, sc, g
+    ctx.close()
+    return {"mode": "gelu_fusion", "shapes": out}
+
+
 def gemm_tiles(T, wl, tuned, path=0):
     """Tile shape (BM, BN) each distinct GEMM shape runs with."""
     out = {}
@@ -523,6 +566,8 @@ def main() -> int:
                          "calibrated choice, which keeps counter runs on the same kernels)")
     ap.add_argument("--shared-x", action="store_true",
                     help="reuse step 0's activations at every step (same work, faster set-up)")
+    ap.add_argument("--gelu-fusion", action="store_true",
+                    help="only time the MLP-down input quantizer with the GELU folded in vs unfused")
     ap.add_argument("--dmpq", action="store_true",
                     help="only run the CogVideoX-shaped schedule with the online INT8/4-bit selector")
     ap.add_argument("--dmpq-steps", type=int, default=0, help="denoising steps for --dmpq (0 = 50)")
@@ -573,6 +618,9 @@ def main() -> int:
     torch.cuda.set_device(dev)
     if args.dmpq:
         print(json.dumps(dmpq_bench(args, T, torch, dev)), flush=True)
+        return 0
+    if args.gelu_fusion:
+        print(json.dumps(gelu_fusion_bench(T, torch, dev)), flush=True)
         return 0
     wl = S.WORKLOADS[args.workload]() if args.had_block is None else \
         S.WORKLOADS[args.workload](had_block=args.had_block)

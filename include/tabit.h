@@ -206,6 +206,23 @@ int tabit_plane_qgemm(tabit_ctx* ctx, const int8_t* x_q, const float* x_scale,
                       int k_bits, uint16_t* y_bf16, int32_t* acc, void* stream);
 
 /*
+ * Producer-fused quantizer for the MLP down projection: the MLP's activation
+ * (GELU, tanh form -- the pages fix none; the DiT convention) is applied while
+ * the down projection's input is quantized, so the 4H-wide activation is read
+ * once and never written in bf16.  Per element g = bf16_rne(gelu(x)) with
+ *   gelu(x) = 0.5 x (1 + tanh(u)) = x / (1 + exp(-z)),
+ *   u = sqrt(2/pi) (x + 0.044715 x^3),  z = min(max(2u, -40), 40),
+ *   exp(v)  = p(r) 2^n, n = rint(v log2 e), r = (v - n ln2_hi) - n ln2_lo,
+ *             p the degree-6 Taylor polynomial of e^r in Horner form,
+ * all in fp32 with IEEE operations in that order (constants rounded to fp32);
+ * then exactly tabit_hadamard_quant_act (INT8) on g.
+ *   x_bf16 device [M][K] (the up projection's output); x_q int8 [M][K];
+ *   x_scale fp32 [M].  Errors as tabit_hadamard_quant_act.
+ */
+int tabit_gelu_quant_act(tabit_ctx* ctx, const uint16_t* x_bf16, int M, int K, int had_block,
+                         int8_t* x_q, float* x_scale, void* stream);
+
+/*
  * HQ-DM single-Hadamard activation quantizer (HQ-DM section 2.1: only the
  * activations are rotated; inference recovers X_hat = S (XH)_int H, the
  * Hadamard normalization living in the fp scale).  Per token m: codes q of

@@ -143,6 +143,16 @@ def test_gated_linear_validation(lib, ctx):
     assert g(M=0) == T.OK
 
 
+def test_gelu_quant_validation(lib, ctx):
+    def q(M=4, K=64, b=0, xq=FAKE, sc=FAKE):
+        return lib.tabit_gelu_quant_act(ctx.handle, FAKE, M, K, b, xq, sc, None)
+    assert q(xq=None) == T.EINVAL
+    assert q(b=16) == T.ERANGE
+    assert q(K=48) == T.ESHAPE
+    assert q(xq=MISALIGNED) == T.EALIGN
+    assert q(M=0) == T.OK
+
+
 def test_hqdm_validation(lib, ctx):
     def q(M=4, K=64, b=32, hi=FAKE, lo=FAKE, sc=FAKE):
         return lib.tabit_hqdm_quant_act(ctx.handle, FAKE, M, K, b, hi, lo, sc, None)

@@ -96,3 +96,22 @@ def test_hqdm_scheduled_linear_and_full_size(ctx):
     hi, lo, sc = ctx.hqdm_quant_act(x.to(DEV), b)
     _, acc = ctx.hqdm_qgemm(hi, lo, sc, wts["w_q"], wts["w_scale"], 2, want_y=False, want_acc=True)
     np.testing.assert_array_equal(_np(acc)[rows], acc_ref)
+
+
+# ---------------------------------------------------------------- fused GELU quantizer
+@pytest.mark.parametrize("M,K", [(1, 128), (37, 640), (300, 4608), (129, 2560)])
+@pytest.mark.parametrize("b", [0, 64])
+def test_gelu_quant_bit_exact(ctx, M, K, b):
+    """Codes and scales of bf16(gelu(x)) bit-exact: the kernel evaluates GELU with the
+    oracle's fp32 steps.  Inputs span the GELU's range (x from the activation
+    generator scaled by 3, plus rows of large and tiny magnitudes)."""
+    x = S.gen_activation(M, K, seed=M * 3 + K + b).float() * 3.0
+    if M >= 3:
+        x[0] = 0.0
+        x[1] = torch.linspace(-30, 30, K)
+        x[2] *= 1e-4
+    x = x.to(torch.bfloat16)
+    q_ref, s_ref = O.quantize_act_gelu_int8(S.bf16_bits(x), b)
+    q, s = ctx.gelu_quant_act(x.to(DEV), b)
+    np.testing.assert_array_equal(_np(q), q_ref)
+    np.testing.assert_array_equal(_np(s).view(np.uint32), s_ref.view(np.uint32))

@@ -66,6 +66,8 @@ _SIGNATURES = {
     "tabit_plane_config_info": (_c_int, [_c_int, _PINT, _PINT]),
     "tabit_weight_planes_bytes": (_c_size_t, [_c_int, _c_int]),
     "tabit_dmpq_workspace_bytes": (_c_size_t, [_c_int]),
+    "tabit_gelu_quant_act": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p,
+                                      _c_void_p, _c_void_p]),
     "tabit_hqdm_quant_act": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p,
                                       _c_void_p, _c_void_p, _c_void_p]),
     "tabit_hqdm_qgemm": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -352,6 +354,21 @@ class Context:
                         want_acc=False):
         return self._gemm_i8(self._lib.tabit_qgemm_bitserial, x_q, x_scale, w_q, w_scale, k_bits, y,
                              acc, want_y, want_acc)
+
+    def gelu_quant_act(self, x: torch.Tensor, had_block: int, x_q=None, x_scale=None):
+        """Down projection's input codes with the GELU folded in: int8 [M, K] + fp32 [M]."""
+        _dev(x, torch.bfloat16, "x")
+        M, K = x.shape
+        if x_q is None:
+            x_q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        if x_scale is None:
+            x_scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+        _dev(x_q, torch.int8, "x_q", (M, K))
+        _dev(x_scale, torch.float32, "x_scale", (M,))
+        st = self._lib.tabit_gelu_quant_act(self._h, x.data_ptr(), M, K, had_block, x_q.data_ptr(),
+                                            x_scale.data_ptr(), _stream(x.device))
+        self._check(st)
+        return x_q, x_scale
 
     def hqdm_quant_act(self, x: torch.Tensor, had_block: int):
         """HQ-DM single-Hadamard codes: (x_hi int8 [M,K], x_lo int8 [M,K], x_scale fp32 [M])."""

@@ -327,6 +327,24 @@ int tabit_mxfp4_qgemm(tabit_ctx* ctx, const uint8_t* x_fp4, const uint8_t* x_e8m
                     "mxfp4_qgemm launch");
 }
 
+int tabit_gelu_quant_act(tabit_ctx* ctx, const uint16_t* x_bf16, int M, int K, int had_block,
+                         int8_t* x_q, float* x_scale, void* stream) {
+  if (ctx == nullptr) return TABIT_EINVAL;
+  if (x_bf16 == nullptr || x_q == nullptr || x_scale == nullptr)
+    return fail(ctx, TABIT_EINVAL, "null pointer");
+  int st = check_k_shape(ctx, M, K, had_block);
+  if (st != TABIT_OK) return st;
+  if ((size_t)M * (size_t)K > kMaxOperandBytes)
+    return fail(ctx, TABIT_ESHAPE, "activations must stay below 2 GiB");
+  if (!aligned(x_bf16, 16) || !aligned(x_q, 16) || !aligned(x_scale, 4))
+    return fail(ctx, TABIT_EALIGN, "misaligned pointer");
+  if (M == 0) return TABIT_OK;
+  return hip_status(ctx,
+                    tabit::launch_quant_gelu_int8(x_bf16, M, K, had_block, x_q, x_scale,
+                                                  static_cast<hipStream_t>(stream)),
+                    "gelu_quant_act launch");
+}
+
 int tabit_hqdm_quant_act(tabit_ctx* ctx, const uint16_t* x_bf16, int M, int K, int had_block,
                          int8_t* x_hi, int8_t* x_lo, float* x_scale, void* stream) {
   if (ctx == nullptr) return TABIT_EINVAL;

@@ -84,6 +84,13 @@ __device__ __forceinline__ void load_chunk(const uint16_t* p, float (&v)[16]) {
   }
 }
 
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t tile_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
 __device__ __forceinline__ uint32_t pack4_i8(float a, float b, float c, float d, float r) {
   const int qa = (int)__builtin_amdgcn_fmed3f(rintf(a * r), -127.0f, 127.0f);
   const int qb = (int)__builtin_amdgcn_fmed3f(rintf(b * r), -127.0f, 127.0f);
@@ -101,11 +108,42 @@ __device__ __forceinline__ int row_of(int c, int cr, float inv_cr) {
   return r;
 }
 
-// HQ = false: codes of the rotated row.  HQ = true (HQ-DM single Hadamard):
+// exp(v), |v| <= 40, in fp32 from exact operations only: n = rint(v log2 e),
+// r = (v - n ln2_hi) - n ln2_lo (Cody-Waite; n ln2_hi is exact), e^r by its
+// degree-6 Taylor polynomial in Horner form, times 2^n.  The constants are the
+// fp32 values nearest to log2 e, ln 2 (split 16 + 24 bits) and 1/j!.
+__device__ __forceinline__ float exp_f32(float v) {
+  const float n = rintf(v * 0x1.715476p+0f);
+  const float r = (v - n * 0x1.62e4p-1f) - n * 0x1.7f7d1cp-20f;
+  float p = 0x1.6c16c2p-10f;
+  p = p * r + 0x1.111112p-7f;
+  p = p * r + 0x1.555556p-5f;
+  p = p * r + 0x1.555556p-3f;
+  p = p * r + 0.5f;
+  p = p * r + 1.0f;
+  p = p * r + 1.0f;
+  return ldexpf(p, (int)n);
+}
+
+// GELU, tanh form: 0.5 x (1 + tanh(u)) = x / (1 + exp(-2u)) with
+// u = sqrt(2/pi) (x + 0.044715 x^3) and 2u clamped to [-40, 40].  Every
+// operation is an IEEE add, multiply, correctly rounded divide or exact
+// scaling, in a fixed order (no contraction).
+__device__ __forceinline__ float gelu_tanh(float x) {
+  const float u = 0x1.988454p-1f * (x + 0x1.6e4e26p-5f * (x * x * x));
+  const float z = fminf(fmaxf(2.0f * u, -40.0f), 40.0f);
+  return x / (1.0f + exp_f32(-z));
+}
+
+enum QuantMode { Q_PLAIN = 0, Q_HQDM = 1, Q_GELU = 2 };
+
+// MODE = Q_GELU: each input element becomes bf16(gelu(x)) first (the MLP's
+// activation folded into the quantizer of the down projection's input).
+// MODE = Q_PLAIN: codes of the rotated row.  MODE = Q_HQDM (HQ-DM single Hadamard):
 // the codes are rotated back by the same block FWHT -- integers up to 127 b in
 // magnitude, exact in fp32 -- and written as two int8 planes Z = 128 hi + lo
 // (hi = floor(Z / 128) to q, lo in [0, 127] to q_lo).
-template <int B, int NT, int CPT, bool HQ>
+template <int B, int NT, int CPT, int MODE>
 __global__ void __launch_bounds__(NT)
 quant_int8_kernel(const uint16_t* __restrict__ x, int M, int K, int rows_per_wg, float scale_div,
                   int8_t* __restrict__ q, float* __restrict__ scale, const uint8_t* __restrict__ gate,
@@ -128,6 +166,10 @@ quant_int8_kernel(const uint16_t* __restrict__ x, int M, int K, int rows_per_wg,
     const int c = i * NT + tid;
     if (c < nchunks) {
       load_chunk(x + base + (size_t)c * 16, v[i]);
+      if constexpr (MODE == Q_GELU) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[i][e] = __uint_as_float((uint32_t)tile_bf16(gelu_tanh(v[i][e])) << 16);
+      }
     } else {
 #pragma unroll
       for (int e = 0; e < 16; ++e) v[i][e] = 0.0f;
@@ -157,7 +199,7 @@ quant_int8_kernel(const uint16_t* __restrict__ x, int M, int K, int rows_per_wg,
   }
   __syncthreads();
 
-  if constexpr (!HQ) {
+  if constexpr (MODE != Q_HQDM) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = i * NT + tid;
@@ -257,13 +299,13 @@ quant_mx_kernel(const uint16_t* __restrict__ x, long long nchunks, uint8_t* __re
   }
 }
 
-template <int B, bool HQ>
+template <int B, int MODE>
 hipError_t dispatch_int8(int nt, int cpt, int grid, int rows, const uint16_t* x, int M, int K,
                          float scale_div, int8_t* q, float* scale, hipStream_t s, const uint8_t* gate,
                          int8_t* q_lo) {
 #define TABIT_Q(NT_, CPT_)                                                                      \
   if (nt == NT_ && cpt == CPT_) {                                                               \
-    quant_int8_kernel<B, NT_, CPT_, HQ><<<grid, NT_, 0, s>>>(x, M, K, rows, scale_div, q, scale, \
+    quant_int8_kernel<B, NT_, CPT_, MODE><<<grid, NT_, 0, s>>>(x, M, K, rows, scale_div, q, scale, \
                                                              gate, q_lo);                       \
     return hipGetLastError();                                                                   \
   }
@@ -282,7 +324,7 @@ namespace {
 // workgroups with few registers outnumber the resident slots, so reads of
 // late workgroups overlap the stores of early ones; on MI355X this beat
 // fuller multi-row, multi-chunk shapes by 7-32% at the workloads' sizes.
-template <bool HQ>
+template <int MODE>
 hipError_t launch_int8_rows(const uint16_t* x, int M, int K, int had_block, float scale_div,
                             int8_t* q, float* scale, hipStream_t stream, const uint8_t* gate,
                             int8_t* q_lo) {
@@ -295,10 +337,10 @@ hipError_t launch_int8_rows(const uint16_t* x, int M, int K, int had_block, floa
   const int rows = (nt * cpt) / cr;
   const int grid = (M + rows - 1) / rows;
   switch (had_block) {
-    case 0: return dispatch_int8<0, HQ>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream, gate, q_lo);
-    case 32: return dispatch_int8<32, HQ>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream, gate, q_lo);
-    case 64: return dispatch_int8<64, HQ>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream, gate, q_lo);
-    default: return dispatch_int8<128, HQ>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream, gate, q_lo);
+    case 0: return dispatch_int8<0, MODE>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream, gate, q_lo);
+    case 32: return dispatch_int8<32, MODE>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream, gate, q_lo);
+    case 64: return dispatch_int8<64, MODE>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream, gate, q_lo);
+    default: return dispatch_int8<128, MODE>(nt, cpt, grid, rows, x, M, K, scale_div, q, scale, stream, gate, q_lo);
   }
 }
 
@@ -306,13 +348,18 @@ hipError_t launch_int8_rows(const uint16_t* x, int M, int K, int had_block, floa
 
 hipError_t launch_quant_int8(const uint16_t* x, int M, int K, int had_block, float scale_div,
                              int8_t* q, float* scale, hipStream_t stream, const uint8_t* gate) {
-  return launch_int8_rows<false>(x, M, K, had_block, scale_div, q, scale, stream, gate, nullptr);
+  return launch_int8_rows<Q_PLAIN>(x, M, K, had_block, scale_div, q, scale, stream, gate, nullptr);
+}
+
+hipError_t launch_quant_gelu_int8(const uint16_t* x, int M, int K, int had_block, int8_t* q,
+                                  float* scale, hipStream_t stream, const uint8_t* gate) {
+  return launch_int8_rows<Q_GELU>(x, M, K, had_block, 1.0f, q, scale, stream, gate, nullptr);
 }
 
 hipError_t launch_quant_hqdm(const uint16_t* x, int M, int K, int had_block, int8_t* q_hi,
                              int8_t* q_lo, float* scale, hipStream_t stream, const uint8_t* gate) {
   const float div = (float)(had_block > 0 ? had_block : 1);   // X ~ (s_a / b) Z
-  return launch_int8_rows<true>(x, M, K, had_block, div, q_hi, scale, stream, gate, q_lo);
+  return launch_int8_rows<Q_HQDM>(x, M, K, had_block, div, q_hi, scale, stream, gate, q_lo);
 }
 
 hipError_t launch_quant_mx(const uint16_t* x, int M, int K, int had_block, uint8_t* q_fp4,

@@ -24,6 +24,11 @@ hipError_t launch_quant_int8(const uint16_t* x, int M, int K, int had_block, flo
                              int8_t* q, float* scale, hipStream_t stream,
                              const uint8_t* gate = nullptr);
 
+// Quantizer of the MLP down projection's input with the GELU (tanh form)
+// folded in: codes of blockFWHT_b(bf16(gelu(x))).
+hipError_t launch_quant_gelu_int8(const uint16_t* x, int M, int K, int had_block, int8_t* q,
+                                  float* scale, hipStream_t stream, const uint8_t* gate = nullptr);
+
 // HQ-DM single Hadamard: codes of the rotated row rotated back, Z = 128 hi + lo
 // as two int8 planes; scale = (a / 127) / max(b, 1).
 hipError_t launch_quant_hqdm(const uint16_t* x, int M, int K, int had_block, int8_t* q_hi,
