@@ -187,6 +187,72 @@ def record_traffic(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_bytes
     print(json.dumps(rec))
 
 
+def single_gemm(shape, reps: int) -> None:
+    """`reps` launches of one masked INT8 GEMM (M, N, K, tile config) on seeded
+    synthetic codes, for counter passes over a single kernel."""
+    import torch
+    import tabit_synth as S
+    import timestep_adaptive_bit_amd as T
+    M, N, K, cfg = shape
+    ctx = T.Context()
+    xq = torch.from_numpy(S.gen_int8((M, K), seed=1)).cuda()
+    wq = torch.from_numpy(S.gen_int8((N, K), seed=2)).cuda()
+    sa = torch.from_numpy(S.gen_scales(M, seed=3)).cuda()
+    sw = torch.from_numpy(S.gen_scales(N, seed=4)).cuda()
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    ctx.set_option(T.OPT_GEMM_CONFIG, cfg)
+    for _ in range(reps):
+        ctx.masked_qgemm(xq, sa, wq, sw, 2, y=y)
+    torch.cuda.synchronize()
+    ctx.close()
+    print(json.dumps({"single_gemm": [M, N, K], "config": cfg, "launches": reps}))
+
+
+def summarize_pmc(dirs) -> None:
+    """Mean of every collected counter per kernel over the rocprofv3 --pmc
+    databases under `dirs` (one pass per directory), with the mean duration."""
+    import sqlite3
+    acc, dur = {}, {}
+    for root in dirs:
+        for db in sorted(glob.glob(os.path.join(root, "**", "*.db"), recursive=True)):
+            c = sqlite3.connect(db)
+            per = {}
+            for d, name, cn, v, du in c.execute(
+                    "select dispatch_id, kernel_name, counter_name, value, duration "
+                    "from counters_collection"):
+                k = name.replace("void ", "").replace("tabit::(anonymous namespace)::", "").split("(")[0]
+                per.setdefault((k, d), {}).setdefault(cn, 0.0)
+                per[(k, d)][cn] += v
+                dur.setdefault(k, {})[(db, d)] = du
+            for (k, _), cs in per.items():
+                for cn, v in cs.items():
+                    acc.setdefault(k, {}).setdefault(cn, []).append(v)
+    simds, xcds = 1024, 8   # 256 CUs x 4 SIMDs; GRBM_GUI_ACTIVE arrives summed over the 8 XCDs
+    for k in sorted(acc):
+        if k.startswith("__amd"):
+            continue            # runtime copies of the inputs
+        ds = list(dur[k].values())
+        print(f"{k}  dispatches {len(ds)}  mean duration {sum(ds) / len(ds) / 1e3:.2f} us")
+        m = {cn: sum(v) / len(v) for cn, v in acc[k].items()}
+        for cn in sorted(m):
+            print(f"  {cn:32s} {m[cn]:14.6g}")
+        gui = m.get("GRBM_GUI_ACTIVE", 0.0) / xcds
+        if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+            print(f"  -> MFMA busy {100 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui * simds):.1f}% of SIMD cycles"
+                  " (of GRBM_GUI_ACTIVE per XCD)")
+        if "SQ_WAVE_CYCLES" in m and m["SQ_WAVE_CYCLES"]:
+            w = m["SQ_WAVE_CYCLES"]
+            print(f"  -> of wave time: waiting on memory/barriers {100 * m.get('SQ_WAIT_ANY', 0) / w:.1f}%,"
+                  f" waiting for issue {100 * m.get('SQ_WAIT_INST_ANY', 0) / w:.1f}%,"
+                  f" waiting for LDS issue {100 * m.get('SQ_WAIT_INST_LDS', 0) / w:.1f}%")
+        if "SQ_LDS_IDX_ACTIVE" in m and m["SQ_LDS_IDX_ACTIVE"]:
+            print(f"  -> LDS bank-conflict cycles per LDS-active cycle "
+                  f"{m.get('SQ_LDS_BANK_CONFLICT', 0) / m['SQ_LDS_IDX_ACTIVE']:.4f}")
+        if "SQ_INSTS_VALU_MFMA_MOPS_I8" in m:
+            print(f"  -> INT8 MFMA ops executed {m['SQ_INSTS_VALU_MFMA_MOPS_I8'] * 512 / 1e9:.2f} G; "
+                  f"LDS bytes read {m.get('SQ_INSTS_LDS_LOAD_BANDWIDTH', 0) * 64 / 1e9:.2f} GB")
+
+
 def copy_calibration(mib: int) -> None:
     """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
     import torch
@@ -587,7 +653,18 @@ def main() -> int:
     ap.add_argument("--summarize-counters", nargs=5, metavar=("MFMA_DIR", "FETCH_DIR", "WRITE_DIR",
                                                              "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
                     default=None, help="only print MFMA and quantizer HBM counter evidence")
+    ap.add_argument("--single-gemm", nargs=4, type=int, metavar=("M", "N", "K", "CFG"),
+                    default=None, help="only launch one masked GEMM --reps times (counter passes)")
+    ap.add_argument("--reps", type=int, default=3, help="launches for --single-gemm")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR", default=None,
+                    help="only print per-kernel means of the counters under the given directories")
     args = ap.parse_args()
+    if args.single_gemm:
+        single_gemm(args.single_gemm, args.reps)
+        return 0
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return 0
     if args.record_traffic:
         fd, wd, cfd, cwd, n = args.record_traffic
         import tabit_synth as S
