@@ -5,9 +5,13 @@ configurations bench.py times), and the kernels run in the launch
 configuration bench.py uses (the library's automatic tile choice).
 Activation and weight codes and scales are compared with the oracle in full,
 bit-exact; GEMM outputs on a seeded sample of rows (first and last row
-included): int32 accumulators bit-exact, bf16 within 1e-2 relative, MXFP4
-outputs within the MXFP4 bound of test_gpu_parity.
+included) at every k the shape's layer-steps use: int32 accumulators
+bit-exact, bf16 within 1e-2 relative, MXFP4 outputs within the MXFP4 bound of
+test_gpu_parity.  One denoising step of the PixArt-shaped stack also runs
+through the native schedule driver, every layer checked.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -34,14 +38,18 @@ def _np(t):
 
 
 def _distinct(wl):
+    """(M, N, K) -> (first layer of that shape, formats used, k values its INT8 steps use)."""
     seen = {}
     for li, layer in enumerate(wl.layers):
         key = (layer.M, layer.N, layer.K)
+        fmts = set(int(f) for f in wl.fmt[:, li])
+        ks = set(int(k) for k, f in zip(wl.k_bits[:, li], wl.fmt[:, li]) if f == 0)
         if key not in seen:
-            fmts = sorted(set(int(f) for f in wl.fmt[:, li]))
-            kmax = int(wl.k_bits[:, li].max())
-            seen[key] = (li, fmts, kmax)
-    return seen
+            seen[key] = (li, fmts, ks)
+        else:
+            seen[key][1].update(fmts)
+            seen[key][2].update(ks)
+    return {k: (li, sorted(f), sorted(ks)) for k, (li, f, ks) in seen.items()}
 
 
 def _sample_rows(M, seed):
@@ -54,8 +62,8 @@ def _sample_rows(M, seed):
 def test_workload_shapes(ctx, name):
     wl = S.WORKLOADS[name]()
     b = wl.had_block
-    for (M, N, K), (li, fmts, kmax) in _distinct(wl).items():
-        print(f"[{name}] {M}x{N}x{K} layer {li} fmts {fmts} k {kmax}", flush=True)
+    for (M, N, K), (li, fmts, ks) in _distinct(wl).items():
+        print(f"[{name}] {M}x{N}x{K} layer {li} fmts {fmts} k {ks}", flush=True)
         x = S.gen_activation(M, K, seed=S.activation_seed(0, K))
         w = S.gen_weight(N, K, seed=li)
         xb, wb = S.bf16_bits(x), S.bf16_bits(w)
@@ -70,12 +78,14 @@ def test_workload_shapes(ctx, name):
             xq_ref, sa_ref = O.quantize_act_int8(xb, b)
             np.testing.assert_array_equal(_np(xq), xq_ref)
             np.testing.assert_array_equal(_np(sa).view(np.uint32), sa_ref.view(np.uint32))
-            y, acc = ctx.masked_qgemm(xq, sa, wts["w_q"], wts["w_scale"], kmax, want_acc=True)
-            acc_ref = O.masked_gemm_i32(xq_ref[rows], wq_ref, kmax)
-            np.testing.assert_array_equal(_np(acc)[rows], acc_ref)
-            y_ref = O.dequant(acc_ref, sa_ref[rows], sw_ref)
-            yy = y.float().cpu().numpy().astype(np.float64)[rows]
-            assert np.all(np.abs(yy - y_ref) <= 1e-2 * np.abs(y_ref) + 1e-30)
+            for i, k in enumerate(ks):       # every k this shape's INT8 layer-steps use
+                r = rows if i == 0 else np.concatenate([rows[:8], rows[-8:]])
+                y, acc = ctx.masked_qgemm(xq, sa, wts["w_q"], wts["w_scale"], k, want_acc=True)
+                acc_ref = O.masked_gemm_i32(xq_ref[r], wq_ref, k)
+                np.testing.assert_array_equal(_np(acc)[r], acc_ref, err_msg=f"k {k}")
+                y_ref = O.dequant(acc_ref, sa_ref[r], sw_ref)
+                yy = y.float().cpu().numpy().astype(np.float64)[r]
+                assert np.all(np.abs(yy - y_ref) <= 1e-2 * np.abs(y_ref) + 1e-30), f"k {k}"
         if 1 in fmts:
             wf_ref, we_ref = O.mx_quantize_rows(O.bf16_to_f32(wb), b)
             np.testing.assert_array_equal(_np(wts["w_fp4"]), wf_ref)
@@ -108,3 +118,46 @@ def test_c3_bitplane_every_k_sampled(ctx):
             _, acc = ctx.qgemm_bitserial(xq, sa, wts["w_q"], wts["w_scale"], k, want_y=False,
                                          want_acc=True)
             np.testing.assert_array_equal(_np(acc)[rows], O.bitplane_gemm_i32(xq_np[rows], wq_np, k))
+
+
+@pytest.mark.parametrize("step", [0, 19])
+def test_pixart_schedule_step_every_layer(ctx, step):
+    """One denoising step of the PixArt-Sigma-shaped stack through the native
+    driver (tabit_run_schedule, as bench.py runs it): all 112 linears, each with
+    its own weights and its (layer, step) k from the installed table; every
+    layer's output checked on sampled rows against the oracle's linear."""
+    wl = S.c2_pixart_sigma()
+    L, b = len(wl.layers), wl.had_block
+    ctx.set_step_schedule(wl.k_bits, wl.fmt)
+    layers = (T.Layer * L)()
+    keep, w_refs = [], []
+    for li, layer in enumerate(wl.layers):
+        w = S.gen_weight(layer.N, layer.K, seed=li)
+        wts = ctx.quantize_weights(w.to(DEV), b)
+        y = torch.empty((layer.M, layer.N), dtype=torch.bfloat16, device=DEV)
+        layers[li].M, layers[li].N, layers[li].K = layer.M, layer.N, layer.K
+        layers[li].w_q, layers[li].w_scale = wts["w_q"].data_ptr(), wts["w_scale"].data_ptr()
+        layers[li].y_bf16 = y.data_ptr()
+        keep.append((wts, y))
+        w_refs.append(O.quantize_weights_int8(S.bf16_bits(w), b))
+    xs = {}
+    for layer in wl.layers:
+        if (layer.M, layer.K) not in xs:
+            xs[(layer.M, layer.K)] = S.gen_activation(layer.M, layer.K,
+                                                      seed=S.activation_seed(step, layer.K))
+    dxs = {key: x.to(DEV) for key, x in xs.items()}
+    x_ptrs = (ctypes.c_void_p * L)(*[dxs[(l.M, l.K)].data_ptr() for l in wl.layers])
+    ws = torch.empty(max(T.act_workspace_bytes(l.M, l.K) for l in wl.layers), dtype=torch.uint8,
+                     device=DEV)
+    print(f"pixart step {step}: run_schedule over {L} layers", flush=True)
+    ctx.run_schedule(step, 1, layers, x_ptrs, b, ws)
+    torch.cuda.synchronize()
+    rows = _sample_rows(wl.layers[0].M, seed=100 + step)[:12]
+    acts = {key: O.quantize_act_int8(S.bf16_bits(x[rows]), b) for key, x in xs.items()}
+    for li, layer in enumerate(wl.layers):
+        k = int(wl.k_bits[step, li])
+        xq_ref, sa_ref = acts[(layer.M, layer.K)]
+        wq_ref, sw_ref = w_refs[li]
+        y_ref = O.dequant(O.masked_gemm_i32(xq_ref, wq_ref, k), sa_ref, sw_ref)
+        yy = keep[li][1].float().cpu().numpy().astype(np.float64)[rows]
+        assert np.all(np.abs(yy - y_ref) <= 1e-2 * np.abs(y_ref) + 1e-30), f"layer {li} k {k}"
