@@ -14,9 +14,10 @@
 // the INT8 GEMM's: packed operand stages of 128 bytes (256 elements) copied
 // global->LDS by buffer loads into a double-buffered ring, one barrier per
 // stage; each wave reads the next K-step's fragments and scale bytes from LDS
-// while the matrix cores work on the current one.  The 8 scale bytes per row and stage go through registers into a
-// small LDS table next to the data (their loads are issued before the stage's
-// copies so waiting for them never waits for the copies).
+// while the matrix cores work on the current one.  The 8 scale bytes per row
+// and stage go through registers (two words per row) into a small LDS table
+// next to the data (their loads are issued before the stage's copies so
+// waiting for them never waits for the copies).
 #include "tabit_internal.h"
 #include "tile_common.h"
 
@@ -43,11 +44,10 @@ gemm_mxfp4_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ AE,
   constexpr int KS = RB / 32;                     // 32-byte (64-element) K-steps per stage
   constexpr int DATA = (BM + BN) * RB;
   constexpr int SCL = (BM + BN) * SPR;
-  constexpr int SL = (SCL + NT - 1) / NT;         // scale bytes per thread per stage
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold whole 32x32 blocks");
   static_assert(2 * DATA >= BM * BN * 2, "epilogue tile must fit in the LDS stages");
   __shared__ __attribute__((aligned(1024))) int8_t smem[2 * DATA];
-  __shared__ uint8_t sscale[2][SCL];
+  __shared__ __attribute__((aligned(16))) uint8_t sscale[2][SCL];
 
   int tm, tn;
   tile::tile_coords<4>(tiles_m, tiles_n, tm, tn);
@@ -60,30 +60,50 @@ gemm_mxfp4_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ AE,
   const auto rsa = tile::make_rsrc(A, (unsigned)M * (unsigned)KB);
   const auto rsb = tile::make_rsrc(B, (unsigned)N * (unsigned)KB);
 
-  // scale byte q of the stage table: rows 0..BM-1 from AE, then BN rows from BE
-  uint8_t sreg[SL];
+  // Scale table of a stage: row r (0..BM-1 from AE, then BN rows from BE)
+  // holds its 8 scale bytes; a thread moves whole rows, as two words when the
+  // row's bytes are 4-byte aligned and all inside K (else byte by byte, 127 =
+  // 2^0 past the end or past the last row).
+  constexpr int RPT = (BM + BN + NT - 1) / NT;   // scale rows per thread
+  static_assert(SPR == 8, "two words per row and stage");
+  const bool words = (KSB & 3) == 0;
+  uint32_t sreg[RPT][2];
   auto load_scales = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < SL; ++i) {
-      const int q = i * NT + tid;
-      const int r = q / SPR, j = q % SPR;
-      const int gs = kt * SPR + j;
-      uint8_t v = 127;
-      if (q < SCL && gs < KSB) {
-        if (r < BM) {
-          if (r < rows_a) v = AE[(size_t)(m0 + r) * KSB + gs];
-        } else if (r - BM < rows_b) {
-          v = BE[(size_t)(n0 + r - BM) * KSB + gs];
+    for (int i = 0; i < RPT; ++i) {
+      const int r = i * NT + tid;
+      const uint8_t* src = nullptr;
+      if (r < BM) {
+        if (r < rows_a) src = AE + (size_t)(m0 + r) * KSB;
+      } else if (r < BM + BN && r - BM < rows_b) {
+        src = BE + (size_t)(n0 + r - BM) * KSB;
+      }
+      const int g0 = kt * SPR;
+      uint32_t lo = 0x7F7F7F7Fu, hi = 0x7F7F7F7Fu;
+      if (src != nullptr) {
+        if (words && g0 + SPR <= KSB) {
+          lo = *reinterpret_cast<const uint32_t*>(src + g0);
+          hi = *reinterpret_cast<const uint32_t*>(src + g0 + 4);
+        } else {
+          lo = hi = 0u;
+#pragma unroll
+          for (int j = 0; j < SPR; ++j) {
+            const uint32_t v = g0 + j < KSB ? src[g0 + j] : 127u;
+            if (j < 4) lo |= v << (8 * j);
+            else hi |= v << (8 * (j - 4));
+          }
         }
       }
-      sreg[i] = v;
+      sreg[i][0] = lo;
+      sreg[i][1] = hi;
     }
   };
   auto store_scales = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < SL; ++i) {
-      const int q = i * NT + tid;
-      if (q < SCL) sscale[buf][q] = sreg[i];
+    for (int i = 0; i < RPT; ++i) {
+      const int r = i * NT + tid;
+      if (r < BM + BN)
+        *reinterpret_cast<uint2*>(&sscale[buf][r * SPR]) = make_uint2(sreg[i][0], sreg[i][1]);
     }
   };
   auto issue = [&](int kt) {
@@ -183,11 +203,11 @@ struct CfgDesc {
 };
 // index, BM, BN, WM, WN, rate
 #define TABIT_MX_CONFIGS(X)       \
-  X(0, 256, 128, 2, 2, 0.815f)    \
-  X(1, 128, 128, 2, 2, 0.958f)    \
-  X(2, 128, 64, 2, 2, 0.853f)     \
-  X(3, 64, 64, 2, 2, 0.713f)      \
-  X(4, 256, 128, 2, 4, 0.972f)    \
+  X(0, 256, 128, 2, 2, 0.821f)    \
+  X(1, 128, 128, 2, 2, 0.976f)    \
+  X(2, 128, 64, 2, 2, 0.835f)     \
+  X(3, 64, 64, 2, 2, 0.724f)      \
+  X(4, 256, 128, 2, 4, 0.935f)    \
   X(5, 128, 256, 2, 4, 1.00f)
 #define TABIT_DESC(I, BM, BN, WM, WN, RATE) {BM, BN, WM, WN, RATE},
 constexpr CfgDesc kCfgs[] = {TABIT_MX_CONFIGS(TABIT_DESC)};
