@@ -100,6 +100,26 @@ def test_quant_act_mxfp4_bit_exact(ctx, M, K, b):
     np.testing.assert_array_equal(_np(f), f_ref)
 
 
+def test_quant_mxfp4_ties_and_negative_zero(ctx):
+    """Blocks whose scale is 2^0 (amax 6, X = floor(log2 6) - 2 = 0), so the
+    values reach the E2M1 rounding unscaled: every rounding tie of the format
+    (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5) with both signs, saturation above 6,
+    and small negative values that round to zero (codes must be +0)."""
+    ties = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0]
+    row = [6.0] + ties + [-t for t in ties] + [-0.125, -0.0625, -0.25, -0.0, 0.0, 0.125, 7.0,
+                                                -7.0, 4.0, -4.0, 0.5, -0.5, 3.0, -3.0, 1.0]
+    assert len(row) == 32
+    rows = [row, row[::-1], [-v for v in row]]
+    x = torch.tensor(rows * 4, dtype=torch.float32).reshape(12, 32).repeat(1, 4).to(torch.bfloat16)
+    assert torch.equal(x.float(), torch.tensor(rows * 4).reshape(12, 32).repeat(1, 4))  # exact in bf16
+    f_ref, e_ref = O.mx_quantize_rows(O.bf16_to_f32(_bits(x)), 0)
+    assert (e_ref == 127).all()                                  # scale 2^0 in every block
+    f, e = ctx.hadamard_quant_act(x.to(DEV), 0, T.FMT_MXFP4)
+    np.testing.assert_array_equal(_np(e), e_ref)
+    np.testing.assert_array_equal(_np(f), f_ref)
+    assert not ((f_ref & 0x0F) == 0x08).any() and not ((f_ref & 0xF0) == 0x80).any()   # no -0
+
+
 # ------------------------------------------------------------ INT8 GEMMs
 GEMM_SHAPES = [(1, 32, 32), (17, 96, 96), (64, 640, 1152), (129, 96, 1120), (300, 416, 2240),
                (513, 288, 160)]

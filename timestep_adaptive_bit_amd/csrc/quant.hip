@@ -242,15 +242,23 @@ quant_int8_kernel(const uint16_t* __restrict__ x, int M, int K, int rows_per_wg,
   }
 }
 
-// E2M1 code of t (already scaled by 2^-X): nearest of {0,.5,1,1.5,2,3,4,6},
-// ties to the even mantissa bit, saturating at 6; -0 encodes as +0.
-__device__ __forceinline__ uint32_t e2m1_code(float t) {
-  const float m = fabsf(t);
-  uint32_t c = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) +
-               (uint32_t)(m >= 1.75f) + (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) +
-               (uint32_t)(m > 5.0f);
-  if (t < 0.0f && c != 0u) c |= 8u;
-  return c;
+// E2M1 codes of a and b (already scaled by 2^-X) in the low and high nibble of
+// a byte: nearest of {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even mantissa
+// bit, saturating at 6.  gfx950's packed FP4 conversion rounds and saturates
+// exactly so (checked on the device against the comparison-chain definition
+// over [-10, 10] in steps of 1/400, every tie, +-0 and subnormals; its scale
+// operand divides, and 1.0 leaves the values as they are).
+__device__ __forceinline__ uint32_t e2m1_pair(float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0) & 0xFFu;
+}
+
+// The conversion keeps the sign of a value that rounds to zero (code 8); the
+// format's convention here encodes -0 as +0: clear bit 3 of every nibble whose
+// magnitude bits are zero (adding 7 to 3 magnitude bits carries into bit 3
+// exactly when they are nonzero, and never out of the nibble).
+__device__ __forceinline__ uint32_t drop_negative_zero(uint32_t x) {
+  const uint32_t mag = x & 0x77777777u;
+  return mag | (x & ((mag + 0x77777777u) & 0x88888888u));
 }
 
 template <int B, int CPT>
@@ -289,9 +297,12 @@ quant_mx_kernel(const uint16_t* __restrict__ x, long long nchunks, uint8_t* __re
     const float inv = __uint_as_float((uint32_t)(127 - X) << 23);  // 2^-X, exact
     uint32_t lo = 0u, hi = 0u;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) lo |= e2m1_code(v[e] * inv) << (4 * e);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) hi |= e2m1_code(v[8 + e] * inv) << (4 * e);
+    for (int e = 0; e < 4; ++e) {
+      lo |= e2m1_pair(v[2 * e] * inv, v[2 * e + 1] * inv) << (8 * e);
+      hi |= e2m1_pair(v[8 + 2 * e] * inv, v[8 + 2 * e + 1] * inv) << (8 * e);
+    }
+    lo = drop_negative_zero(lo);
+    hi = drop_negative_zero(hi);
     if (valid) {
       *reinterpret_cast<uint2*>(qf + c * 8) = make_uint2(lo, hi);
       if ((c & 1) == 0) e8[c >> 1] = (uint8_t)(X + 127);
