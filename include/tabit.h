@@ -401,8 +401,19 @@ int tabit_gemm_config_info(int index, int* bm, int* bn, int* split_k);
 /* As tabit_gemm_config_info, for the MXFP4 GEMM's tile configurations. */
 int tabit_mxfp4_config_info(int index, int* bm, int* bn);
 
-/* As tabit_mxfp4_config_info, for the plane-major GEMM's tile configurations. */
-int tabit_plane_config_info(int index, int* bm, int* bn);
+/* As tabit_mxfp4_config_info, for the plane-major GEMM's tile configurations;
+ * *k_groups (may be NULL) receives the number of wave groups that split the K
+ * stages of one tile inside its workgroup (1 = no split; the groups' int32
+ * sums are added exactly, so every configuration gives the same result). */
+int tabit_plane_config_info(int index, int* bm, int* bn, int* k_groups);
+
+/* The plane-major GEMM configuration the library picks for M x N x K on a
+ * device with num_cus compute units (<= 0: 256) when neither an option nor
+ * tuning forces one: the busiest-CU model over one-group tiles, then, when
+ * that tile leaves at least half of the CUs idle, its K-split variant with the
+ * fewest stages per group.  EINVAL for negative sizes or K < 1.  Makes no HIP
+ * call. */
+int tabit_plane_config_choose(int M, int N, int K, int num_cus);
 
 /* As tabit_mxfp4_config_info, for the HQ-DM GEMM's tile configurations. */
 int tabit_hqdm_config_info(int index, int* bm, int* bn);

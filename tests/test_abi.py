@@ -251,9 +251,14 @@ def test_options_and_configs(ctx):
     npl = T.plane_config_info()
     assert npl >= 1
     for i in range(npl):
-        bm, bn = T.plane_config_info(i)
-        assert bm % 32 == 0 and bn % 32 == 0
+        bm, bn, kg = T.plane_config_info(i)
+        assert bm % 32 == 0 and bn % 32 == 0 and kg >= 1
         ctx.set_option(T.OPT_PLANE_CONFIG, i)
+    # few tiles (64 tokens): a K-split tile; a full chip of tiles: none
+    assert T.plane_config_info(T.plane_config_choose(64, 1152, 1152, 256))[2] > 1
+    assert T.plane_config_info(T.plane_config_choose(4096, 4608, 1152, 256))[2] == 1
+    with pytest.raises(T.TabitError):
+        T.plane_config_choose(64, 1152, 0)
     ctx.set_option(T.OPT_PLANE_CONFIG, -1)
     with pytest.raises(T.TabitError):
         ctx.set_option(T.OPT_PLANE_CONFIG, npl)

@@ -7,7 +7,8 @@ raises if the library has not been built.
 """
 from ._lib import (  # noqa: F401
     Context, Layer, TabitError, load, version, act_workspace_bytes, gemm_config_info,
-    gemm_config_choose, mxfp4_config_info, plane_config_info, weight_planes_bytes,
+    gemm_config_choose, mxfp4_config_info, plane_config_info, plane_config_choose,
+    weight_planes_bytes,
     dmpq_workspace_bytes,
     header_functions, LIB_PATH,
     OK, EINVAL, ESHAPE, EALIGN, ERANGE, ENOSCHED, EHIP, ENOMEM,
@@ -19,6 +20,6 @@ __all__ = [
     "Context", "TabitError", "load", "version", "act_workspace_bytes", "gemm_config_info",
     "gemm_config_choose", "header_functions", "FMT_INT8", "FMT_MXFP4", "PATH_MASKED",
     "PATH_BITSERIAL", "PATH_PLANES", "OPT_GEMM_CONFIG", "OPT_MXFP4_CONFIG", "OPT_PLANE_CONFIG",
-    "plane_config_info", "weight_planes_bytes", "dmpq_workspace_bytes",
+    "plane_config_info", "plane_config_choose", "weight_planes_bytes", "dmpq_workspace_bytes",
     "PATH_HQDM", "OPT_HQDM_CONFIG", "hqdm_config_info",
 ]

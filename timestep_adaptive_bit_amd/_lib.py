@@ -63,7 +63,8 @@ _SIGNATURES = {
                                           _c_void_p]),
     "tabit_plane_qgemm": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
                                    _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
-    "tabit_plane_config_info": (_c_int, [_c_int, _PINT, _PINT]),
+    "tabit_plane_config_info": (_c_int, [_c_int, _PINT, _PINT, _PINT]),
+    "tabit_plane_config_choose": (_c_int, [_c_int, _c_int, _c_int, _c_int]),
     "tabit_weight_planes_bytes": (_c_size_t, [_c_int, _c_int]),
     "tabit_dmpq_workspace_bytes": (_c_size_t, [_c_int]),
     "tabit_gelu_quant_act": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p,
@@ -198,15 +199,23 @@ def weight_planes_bytes(N: int, K: int) -> int:
 
 
 def plane_config_info(index: int = -1):
-    """Number of plane-major GEMM configs (index < 0) or (bm, bn) of one."""
+    """Number of plane-major GEMM configs (index < 0) or (bm, bn, k_groups) of one."""
     lib = load()
     if index < 0:
-        return int(lib.tabit_plane_config_info(-1, None, None))
-    bm, bn = ctypes.c_int(), ctypes.c_int()
-    st = lib.tabit_plane_config_info(index, ctypes.byref(bm), ctypes.byref(bn))
+        return int(lib.tabit_plane_config_info(-1, None, None, None))
+    bm, bn, kg = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    st = lib.tabit_plane_config_info(index, ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(kg))
     if st != OK:
         raise TabitError(st, "bad config index")
-    return bm.value, bn.value
+    return bm.value, bn.value, kg.value
+
+
+def plane_config_choose(M: int, N: int, K: int, num_cus: int = 0) -> int:
+    """Index of the plane-major GEMM configuration the library picks for M x N x K."""
+    st = int(load().tabit_plane_config_choose(M, N, K, num_cus))
+    if st < 0:
+        raise TabitError(st, "bad shape")
+    return st
 
 
 def gemm_config_choose(M: int, N: int, K: int, num_cus: int = 0) -> int:

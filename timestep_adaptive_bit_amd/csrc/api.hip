@@ -742,13 +742,19 @@ int tabit_mxfp4_config_info(int index, int* bm, int* bn) {
   return TABIT_OK;
 }
 
-int tabit_plane_config_info(int index, int* bm, int* bn) {
+int tabit_plane_config_info(int index, int* bm, int* bn, int* k_groups) {
   if (index < 0) return tabit::plane_config_count();
   if (index >= tabit::plane_config_count() || bm == nullptr || bn == nullptr) return TABIT_EINVAL;
   const tabit::GemmConfig c = tabit::plane_config(index);
   *bm = c.bm;
   *bn = c.bn;
+  if (k_groups != nullptr) *k_groups = c.split_k;
   return TABIT_OK;
+}
+
+int tabit_plane_config_choose(int M, int N, int K, int num_cus) {
+  if (M < 0 || N < 0 || K < 1) return TABIT_EINVAL;
+  return tabit::plane_config_choose(M, N, K, num_cus);
 }
 
 int tabit_gemm_config_choose(int M, int N, int K, int num_cus) {

@@ -28,6 +28,13 @@
 // The rebuilt byte is sum_{b >= k} c_b * bit_b = (w >> k) << k exactly
 // (c_7 = -128 is the two's-complement sign bit), so the product equals the
 // masked GEMM bit for bit with one MFMA per K-step.
+//
+// K split inside the workgroup (KW > 1), for few-token shapes whose tiles
+// leave most CUs idle: KW groups of WM x WN waves each walk a contiguous range
+// of the K stages through their own LDS ring, then groups 1..KW-1 hand their
+// int32 accumulators to group 0 through LDS (integer sums: the result is the
+// unsplit one bit for bit) and group 0 runs the epilogue.  Every wave takes
+// part in every barrier.
 #include "tabit_internal.h"
 #include "tile_common.h"
 
@@ -91,8 +98,8 @@ __device__ __forceinline__ void dma_planes(__amdgpu_buffer_rsrc_t rs, int8_t* ld
   }
 }
 
-template <int BM, int BN, int WM, int WN, int NST>
-__global__ void __launch_bounds__(WM* WN * 64)
+template <int BM, int BN, int WM, int WN, int NST, int KW>
+__global__ void __launch_bounds__(WM* WN * KW * 64)
 gemm_planes_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
                    const uint32_t* __restrict__ P, const float* __restrict__ SB, int M, int N,
                    int K, int kbits, uint16_t* __restrict__ Y, int32_t* __restrict__ ACC,
@@ -111,14 +118,18 @@ gemm_planes_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
   static_assert(SP_BYTES % 1024 == 0 && NI % NW == 0, "plane copies split evenly over the waves");
   static_assert(NST >= 2 && NST <= 4, "2 to 4 LDS stages");
   static_assert(NST * STAGE >= BM * BN * 2, "epilogue tile must fit in the LDS stages");
-  __shared__ __attribute__((aligned(1024))) int8_t smem[NST * STAGE];
+  static_assert(KW >= 1 && (KW - 1) * BM * BN * 4 <= KW * NST * STAGE,
+                "the K groups' partial accumulators must fit in the LDS stages");
+  __shared__ __attribute__((aligned(1024))) int8_t smem[KW * NST * STAGE];
 
   int tm, tn;
   tile::tile_coords<4>(tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int group = (tid >> 6) / NW;             // K group
+  const int wave = (tid >> 6) % NW, lane = tid & 63;   // wave within the group
   const int wm = wave / WN, wn = wave % WN;
+  int8_t* ring = smem + group * NST * STAGE;
   const int rows_a = min(BM, M - m0);
   const int S = (K + RB - 1) / RB;
   const auto rsa = tile::make_rsrc(A, (unsigned)M * (unsigned)K);
@@ -132,29 +143,33 @@ gemm_planes_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
 
   const int ra0 = wm * WTM + (lane & 31), rb0 = wn * WTN + (lane & 31);
   const int khalf = lane >> 5;
-  const int nk = S;
+  // this group's stages [kt0, kt0 + nk); every group runs `trips` iterations
+  const int trips = (S + KW - 1) / KW;
+  const int kt0 = group * trips;
+  const int nk = max(0, min(S - kt0, trips));
   // rotate amounts (t - b + 4*khalf) mod 32 for t - b = -7..3: bit 8q + 4*khalf + t
   // of a word (this lane's weight 4t + q) moves to bit 8q + b
   int rot[11];
 #pragma unroll
   for (int d = 0; d < 11; ++d) rot[d] = (d - 7 + 4 * khalf) & 31;
-  auto issue = [&](int kt) {
-    int8_t* dst = smem + (kt % NST) * STAGE;
-    tile::dma_stage<BM, NW, RB>(rsa, dst, m0, rows_a, K, kt * RB, wave, lane);
-    dma_planes<BN, NW>(rsp, dst + SA_BYTES, n0, N, S, kt, kbits, wave, lane);
+  auto issue = [&](int it) {
+    int8_t* dst = ring + (it % NST) * STAGE;
+    tile::dma_stage<BM, NW, RB>(rsa, dst, m0, rows_a, K, (kt0 + it) * RB, wave, lane);
+    dma_planes<BN, NW>(rsp, dst + SA_BYTES, n0, N, S, kt0 + it, kbits, wave, lane);
   };
 #pragma unroll
   for (int st = 0; st < NST - 1; ++st)
     if (st < nk) issue(st);
-  for (int kt = 0; kt < nk; ++kt) {
+  for (int kt = 0; kt < trips; ++kt) {
     // stage kt has landed once at most (stages issued after it) x DPW copies are pending
     const int ahead = min(NST - 2, nk - 1 - kt);
     if (NST >= 4 && ahead >= 2) tile::wait_vmcnt<(NST >= 4 ? 2 : 0) * DPW>();
     else if (NST >= 3 && ahead >= 1) tile::wait_vmcnt<(NST >= 3 ? 1 : 0) * DPW>();
     else tile::wait_vmcnt<0>();
     __syncthreads();   // stage kt visible to all; stage kt-1's buffer is free
+    if (kt >= nk) continue;   // this group's range is done (the barrier above still counts it)
     if (kt + NST - 1 < nk) issue(kt + NST - 1);
-    const int8_t* sa = smem + (kt % NST) * STAGE;
+    const int8_t* sa = ring + (kt % NST) * STAGE;
     const int8_t* sp = sa + SA_BYTES;
     // this lane's row of every retained plane: 4 words = the stage's 4 K-steps
     uint4 pw[FN][8];
@@ -194,9 +209,44 @@ gemm_planes_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
     }
   }
 
+  if constexpr (KW > 1) {
+    // groups 1..KW-1 hand their partial sums to group 0: v4i q of lane t of
+    // wave w in group g at part[((g - 1) * NQ + q) * NW * 64 + w * 64 + t]
+    constexpr int NQ = FM * FN * 4, GT = NW * 64;
+    v4i* part = reinterpret_cast<v4i*>(smem);
+    const int t = wave * 64 + lane;
+    __syncthreads();   // every group is done reading its ring
+    if (group > 0) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            part[((group - 1) * NQ + (i * FN + j) * 4 + g4) * GT + t] =
+                v4i{acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
+                    acc[i][j][4 * g4 + 3]};
+    }
+    __syncthreads();
+    if (group == 0) {
+      for (int g = 1; g < KW; ++g)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const v4i v = part[((g - 1) * NQ + (i * FN + j) * 4 + g4) * GT + t];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[i][j][4 * g4 + e] += v[e];
+            }
+    }
+  }
+  const bool out = group == 0;   // the waves that hold the tile's sums
+
   // 32x32 output layout: lane l, register r holds row (r/4)*8 + (l/32)*4 + r%4, col l%32.
   const int row_w = m0 + wm * WTM, col_w = n0 + wn * WTN;
-  if (ACC != nullptr) {
+  if (ACC != nullptr && out) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -222,37 +272,40 @@ gemm_planes_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
       const int gn = col_w + j * 32 + (lane & 31);
       sb_c[j] = gn < N ? SB[gn] : 0.0f;
     }
-    __syncthreads();   // every wave is done reading the last stage
+    __syncthreads();   // every wave is done reading the last stage (or the partial sums)
     uint16_t* st = reinterpret_cast<uint16_t*>(smem) + wave * WTM * WTN;
     tile::store_tile32_bf16<WTM, WTN>(st, lane, Y, row_w, col_w, M, N, [&](int i, int j, int r) {
       return tile::bf16_rne(((float)acc[i][j][r] * sa_r[i][r]) * sb_c[j]);
-    });
+    }, out);
   }
 }
 
 struct PlaneCfg {
-  int bm, bn, wm, wn, nst;
+  int bm, bn, wm, wn, nst, kw;
   float rate;   // relative per-CU throughput when busy
 };
-// index, BM, BN, WM, WN, LDS stages, rate
-#define TABIT_PLANE_CONFIGS(X)   \
-  X(0, 64, 32, 1, 1, 4, 0.30f)   \
-  X(1, 64, 64, 1, 2, 2, 0.45f)   \
-  X(2, 128, 64, 1, 2, 2, 0.70f)  \
-  X(3, 128, 128, 2, 2, 2, 1.00f)
-#define TABIT_PDESC(I, BM, BN, WM, WN, NST, RATE) {BM, BN, WM, WN, NST, RATE},
+// index, BM, BN, WM, WN, LDS stages, K groups, rate
+#define TABIT_PLANE_CONFIGS(X)      \
+  X(0, 64, 32, 1, 1, 4, 1, 0.30f)   \
+  X(1, 64, 64, 1, 2, 2, 1, 0.45f)   \
+  X(2, 128, 64, 1, 2, 2, 1, 0.70f)  \
+  X(3, 128, 128, 2, 2, 2, 1, 1.00f) \
+  X(4, 64, 32, 1, 1, 2, 3, 0.30f)   \
+  X(5, 64, 32, 1, 1, 2, 5, 0.30f)   \
+  X(6, 64, 64, 1, 2, 2, 3, 0.45f)
+#define TABIT_PDESC(I, BM, BN, WM, WN, NST, KW, RATE) {BM, BN, WM, WN, NST, KW, RATE},
 constexpr PlaneCfg kPlaneCfgs[] = {TABIT_PLANE_CONFIGS(TABIT_PDESC)};
 #undef TABIT_PDESC
 constexpr int kNumPlaneCfgs = sizeof(kPlaneCfgs) / sizeof(kPlaneCfgs[0]);
 
-template <int BM, int BN, int WM, int WN, int NST>
+template <int BM, int BN, int WM, int WN, int NST, int KW>
 hipError_t launch_planes_cfg(const int8_t* xq, const float* sa, const uint32_t* wp,
                              const float* sw, int M, int N, int K, int kbits, uint16_t* y,
                              int32_t* acc, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
                              const uint8_t* gate) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const dim3 grid(tiles_m * tiles_n), block(WM * WN * 64);
-  auto kern = gemm_planes_kernel<BM, BN, WM, WN, NST>;
+  const dim3 grid(tiles_m * tiles_n), block(WM * WN * KW * 64);
+  auto kern = gemm_planes_kernel<BM, BN, WM, WN, NST, KW>;
   if (ev0 != nullptr || ev1 != nullptr)
     hipExtLaunchKernelGGL(kern, grid, block, 0, s, ev0, ev1, 0, xq, sa, wp, sw, M, N, K, kbits, y,
                           acc, tiles_m, tiles_n, gate);
@@ -275,37 +328,57 @@ hipError_t launch_pack_planes(const int8_t* wq, int N, int K, uint32_t* planes, 
 int plane_config_count() { return kNumPlaneCfgs; }
 
 GemmConfig plane_config(int index) {
-  return GemmConfig{kPlaneCfgs[index].bm, kPlaneCfgs[index].bn, 1};
+  return GemmConfig{kPlaneCfgs[index].bm, kPlaneCfgs[index].bn, kPlaneCfgs[index].kw};
 }
 
 // Tiles land round-robin on the CUs, so the busiest CU runs ceil(tiles / CUs)
-// of them; its time is that count times the tile's work over the tile's rate.
+// of them; its time is that count times the tile's work over the tile's rate
+// (one K group per workgroup).  When the chosen tile leaves at least half of
+// the CUs idle, the variant of the same tile with the most K groups that cuts
+// the stages each group walks (fewest trips, then fewest groups) replaces it:
+// at 64 x 1152 x 1152 five groups take 17.3 us down to 7.9 (k = 0).
 int plane_config_choose(int M, int N, int K, int num_cus) {
-  (void)K;
   if (num_cus <= 0) num_cus = 256;
+  auto tiles_of = [&](const PlaneCfg& c) {
+    return (long long)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+  };
   int best = 0;
   double best_cost = 1e300;
   for (int i = 0; i < kNumPlaneCfgs; ++i) {
     const PlaneCfg& c = kPlaneCfgs[i];
-    const long long tiles = (long long)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
-    const long long per_cu = (tiles + num_cus - 1) / num_cus;
+    if (c.kw != 1) continue;
+    const long long per_cu = (tiles_of(c) + num_cus - 1) / num_cus;
     const double cost = (double)per_cu * c.bm * c.bn / c.rate;
     if (cost < best_cost * 0.999) {
       best_cost = cost;
       best = i;
     }
   }
-  return best;
+  const PlaneCfg& b = kPlaneCfgs[best];
+  if (2 * tiles_of(b) > num_cus) return best;
+  const int S = (K + RB - 1) / RB;
+  int pick = best, pick_trips = S, pick_kw = 1;
+  for (int i = 0; i < kNumPlaneCfgs; ++i) {
+    const PlaneCfg& c = kPlaneCfgs[i];
+    if (c.kw == 1 || c.bm != b.bm || c.bn != b.bn) continue;
+    const int trips = (S + c.kw - 1) / c.kw;
+    if (trips < pick_trips || (trips == pick_trips && c.kw < pick_kw)) {
+      pick = i;
+      pick_trips = trips;
+      pick_kw = c.kw;
+    }
+  }
+  return pick;
 }
 
 hipError_t launch_gemm_planes(int cfg, const int8_t* xq, const float* sa, const uint32_t* wp,
                               const float* sw, int M, int N, int K, int kbits, uint16_t* y,
                               int32_t* acc, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1,
                               const uint8_t* gate) {
-#define TABIT_PCASE(I, BM, BN, WM, WN, NST, RATE) \
-  case I:                                        \
-    return launch_planes_cfg<BM, BN, WM, WN, NST>(xq, sa, wp, sw, M, N, K, kbits, y, acc, stream, \
-                                                  ev0, ev1, gate);
+#define TABIT_PCASE(I, BM, BN, WM, WN, NST, KW, RATE) \
+  case I:                                            \
+    return launch_planes_cfg<BM, BN, WM, WN, NST, KW>(xq, sa, wp, sw, M, N, K, kbits, y, acc,   \
+                                                      stream, ev0, ev1, gate);
   switch (cfg) {
     TABIT_PLANE_CONFIGS(TABIT_PCASE)
     default: return hipErrorInvalidValue;

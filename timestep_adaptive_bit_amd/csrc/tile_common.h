@@ -132,22 +132,28 @@ __device__ __forceinline__ void store_tile_bf16(uint16_t* st, int lane, uint16_t
 // l%32.  `val(i, j, r)` gives the bf16 of fragment (i, j), register r.  The
 // global stores are nontemporal (1.6-5% faster on MI355X than plain stores for
 // the 128 x 64 and 256 x 256 tiles).
+// `active` = false: the wave only takes part in the barrier (for workgroups
+// where some waves hold no output).
 template <int WTM, int WTN, typename F>
 __device__ __forceinline__ void store_tile32_bf16(uint16_t* st, int lane, uint16_t* __restrict__ Y,
-                                                  int row0, int col0, int M, int N, F val) {
+                                                  int row0, int col0, int M, int N, F val,
+                                                  bool active = true) {
   constexpr int FM = WTM / 32, FN = WTN / 32, CH = WTN / 8;
+  if (active) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int lr = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const int lc = j * 32 + (lane & 31);
-        const int ch = (lc >> 3) ^ (lr & (CH - 1));
-        st[lr * WTN + ch * 8 + (lc & 7)] = val(i, j, r);
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int lr = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const int lc = j * 32 + (lane & 31);
+          const int ch = (lc >> 3) ^ (lr & (CH - 1));
+          st[lr * WTN + ch * 8 + (lc & 7)] = val(i, j, r);
+        }
+  }
   __syncthreads();
+  if (!active) return;
 #pragma unroll
   for (int it = 0; it < WTM * CH / 64; ++it) {
     const int idx = it * 64 + lane;
