@@ -26,6 +26,13 @@
 // rate with a few independent accumulators per wave).  The
 // epilogue scales in fp32, rounds to bf16 and transposes through LDS for
 // 16-byte row-contiguous stores.
+//
+// K split inside the workgroup (KW > 1), for few-token shapes whose tiles
+// leave most CUs idle: KW groups of WM x WN waves each walk a contiguous range
+// of the K stages through their own LDS ring; groups 1..KW-1 then hand their
+// int32 accumulators to group 0 through LDS (integer sums: the result equals
+// the unsplit one bit for bit) and group 0 runs the epilogue.  Every wave
+// takes part in every barrier.
 #include "tabit_internal.h"
 #include "tile_common.h"
 
@@ -36,8 +43,8 @@ using tile::v4i;
 typedef int v16i __attribute__((ext_vector_type(16)));
 using tile::BKB;
 
-template <int BM, int BN, int WM, int WN, int RB, int NST, bool BITSERIAL>
-__global__ void __launch_bounds__(WM* WN * 64)
+template <int BM, int BN, int WM, int WN, int RB, int NST, int KW, bool BITSERIAL>
+__global__ void __launch_bounds__(WM* WN * KW * 64)
 gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
                const int8_t* __restrict__ B, const float* __restrict__ SB, int M, int N, int K,
                int kbits, uint16_t* __restrict__ Y, int32_t* __restrict__ ACC, int tiles_m,
@@ -52,14 +59,20 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold whole 32x32 blocks");
   static_assert(NST >= 2 && NST <= 4, "2 to 4 LDS stages");
   static_assert(NST * STAGE >= BM * BN * 2, "epilogue tile must fit in the LDS stages");
-  __shared__ __attribute__((aligned(1024))) int8_t smem[NST * STAGE];
+  static_assert(KW >= 1 && (KW - 1) * BM * BN * 4 <= KW * NST * STAGE,
+                "the K groups' partial accumulators must fit in the LDS stages");
+  static_assert(NW * KW * 64 <= 1024, "at most 1024 threads per workgroup");
+  __shared__ __attribute__((aligned(1024))) int8_t smem[KW * NST * STAGE];
 
   int tm, tn;
   tile::tile_coords<4>(tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // K group and wave within it (compile-time 0 and the wave id without a split)
+  const int group = KW > 1 ? (tid >> 6) / NW : 0;
+  const int wave = KW > 1 ? (tid >> 6) % NW : (tid >> 6), lane = tid & 63;
   const int wm = wave / WN, wn = wave % WN;
+  int8_t* ring = smem + group * NST * STAGE;
   const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
   const auto rsa = tile::make_rsrc(A, (unsigned)M * (unsigned)K);
   const auto rsb = tile::make_rsrc(B, (unsigned)N * (unsigned)K);
@@ -77,24 +90,32 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
   const int ra0 = wm * WTM + (lane & 31), rb0 = wn * WTN + (lane & 31);
   const int khalf = lane >> 5;   // which 16-byte half of the 32-byte K-step
 
-  const int nk = (K + RB - 1) / RB;
-  auto issue = [&](int kt) {
-    int8_t* dst = smem + (kt % NST) * STAGE;
-    tile::dma_stage<BM, NW, RB>(rsa, dst, m0, rows_a, K, kt * RB, wave, lane);
-    tile::dma_stage<BN, NW, RB>(rsb, dst + BM * RB, n0, rows_b, K, kt * RB, wave, lane);
+  // this group's stages [kt0, kt0 + nk); every group runs `trips` iterations
+  const int S = (K + RB - 1) / RB;
+  const int trips = KW > 1 ? (S + KW - 1) / KW : S;
+  const int kt0 = KW > 1 ? group * trips : 0;
+  const int nk = KW > 1 ? max(0, min(S - kt0, trips)) : S;
+  auto issue = [&](int it) {
+    int8_t* dst = ring + (it % NST) * STAGE;
+    const int kb = (kt0 + it) * RB;
+    tile::dma_stage<BM, NW, RB>(rsa, dst, m0, rows_a, K, kb, wave, lane);
+    tile::dma_stage<BN, NW, RB>(rsb, dst + BM * RB, n0, rows_b, K, kb, wave, lane);
   };
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
     if (s < nk) issue(s);
-  for (int kt = 0; kt < nk; ++kt) {
+  for (int kt = 0; kt < trips; ++kt) {
     // stage kt has landed once at most (stages issued after it) x DPW copies are pending
     const int ahead = min(NST - 2, nk - 1 - kt);
     if (NST >= 4 && ahead >= 2) tile::wait_vmcnt<(NST >= 4 ? 2 : 0) * DPW>();
     else if (NST >= 3 && ahead >= 1) tile::wait_vmcnt<(NST >= 3 ? 1 : 0) * DPW>();
     else tile::wait_vmcnt<0>();
     __syncthreads();   // stage kt visible to all; stage kt-1's buffer free for reuse
+    if constexpr (KW > 1) {
+      if (kt >= nk) continue;   // this group's range is done (the barrier above still counts it)
+    }
     if (kt + NST - 1 < nk) issue(kt + NST - 1);
-    const int8_t* sa = smem + (kt % NST) * STAGE;
+    const int8_t* sa = ring + (kt % NST) * STAGE;
     const int8_t* sb = sa + BM * RB;
     v4i a[2][FM], b[2][FN];
     auto load = [&](int ks, int buf) {
@@ -134,10 +155,45 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
     }
   }
 
+  if constexpr (KW > 1) {
+    // groups 1..KW-1 hand their partial sums to group 0: v4i q of lane t of
+    // wave w in group g at part[((g - 1) * NQ + q) * NW * 64 + w * 64 + t]
+    constexpr int NQ = FM * FN * 4, GT = NW * 64;
+    v4i* part = reinterpret_cast<v4i*>(smem);
+    const int t = wave * 64 + lane;
+    __syncthreads();   // every group is done reading its ring
+    if (group > 0) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            part[((group - 1) * NQ + (i * FN + j) * 4 + g4) * GT + t] =
+                v4i{acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
+                    acc[i][j][4 * g4 + 3]};
+    }
+    __syncthreads();
+    if (group == 0) {
+      for (int g = 1; g < KW; ++g)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const v4i v = part[((g - 1) * NQ + (i * FN + j) * 4 + g4) * GT + t];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[i][j][4 * g4 + e] += v[e];
+            }
+    }
+  }
+  const bool out = KW == 1 || group == 0;   // the waves that hold the tile's sums
+
   // ------------------------------------------------------------ epilogue
   // 32x32 output layout: lane l, register r holds row (r/4)*8 + (l/32)*4 + r%4, col l%32.
   const int row_w = m0 + wm * WTM, col_w = n0 + wn * WTN;
-  if (ACC != nullptr) {
+  if (ACC != nullptr && out) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -174,40 +230,42 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
       const int gn = col_w + j * 32 + (lane & 31);
       sb_c[j] = gn < N ? SB[gn] : 0.0f;
     }
-    __syncthreads();  // every wave is done reading the last stage
+    __syncthreads();  // every wave is done reading the last stage (or the partial sums)
     uint16_t* st = reinterpret_cast<uint16_t*>(smem) + wave * WTM * WTN;
     tile::store_tile32_bf16<WTM, WTN>(st, lane, Y, row_w, col_w, M, N, [&](int i, int j, int r) {
       return tile::bf16_rne(((float)acc[i][j][r] * sa_r[i][r]) * sb_c[j]);
-    });
+    }, out);
   }
 }
 
 struct CfgDesc {
-  int bm, bn, wm, wn, rb, nst;
+  int bm, bn, wm, wn, rb, nst, kw;
   float rate;   // relative throughput per CU on its tiles (fitted to MI355X sweeps)
 };
-// index, BM, BN, WM, WN, stage row bytes, LDS stages, rate
-#define TABIT_I8_CONFIGS(X)             \
-  X(0, 256, 256, 2, 4, 128, 2, 1.00f)    \
-  X(1, 192, 192, 2, 3, 128, 3, 0.71f)    \
-  X(2, 128, 128, 2, 2, 128, 2, 0.79f)    \
-  X(3, 256, 128, 2, 2, 128, 3, 0.68f)    \
-  X(4, 128, 64, 2, 2, 128, 2, 0.665f)    \
-  X(5, 64, 64, 2, 2, 128, 2, 0.52f)      \
-  X(6, 192, 128, 2, 2, 128, 2, 0.66f)
-#define TABIT_DESC(I, BM, BN, WM, WN, RB, NST, RATE) {BM, BN, WM, WN, RB, NST, RATE},
+// index, BM, BN, WM, WN, stage row bytes, LDS stages, K groups, rate
+#define TABIT_I8_CONFIGS(X)                \
+  X(0, 256, 256, 2, 4, 128, 2, 1, 1.00f)    \
+  X(1, 192, 192, 2, 3, 128, 3, 1, 0.71f)    \
+  X(2, 128, 128, 2, 2, 128, 2, 1, 0.79f)    \
+  X(3, 256, 128, 2, 2, 128, 3, 1, 0.68f)    \
+  X(4, 128, 64, 2, 2, 128, 2, 1, 0.665f)    \
+  X(5, 64, 64, 2, 2, 128, 2, 1, 0.52f)      \
+  X(6, 192, 128, 2, 2, 128, 2, 1, 0.66f)    \
+  X(7, 64, 64, 2, 2, 128, 2, 3, 0.52f)      \
+  X(8, 128, 64, 2, 2, 128, 2, 3, 0.665f)
+#define TABIT_DESC(I, BM, BN, WM, WN, RB, NST, KW, RATE) {BM, BN, WM, WN, RB, NST, KW, RATE},
 constexpr CfgDesc kCfgs[] = {TABIT_I8_CONFIGS(TABIT_DESC)};
 #undef TABIT_DESC
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
-template <int BM, int BN, int WM, int WN, int RB, int NST>
+template <int BM, int BN, int WM, int WN, int RB, int NST, int KW>
 hipError_t launch_cfg(bool bitserial, const int8_t* xq, const float* sa, const int8_t* wq,
                       const float* sw, int M, int N, int K, int kbits, uint16_t* y, int32_t* acc,
                       hipStream_t s, hipEvent_t ev0, hipEvent_t ev1, const uint8_t* gate) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const dim3 grid(tiles_m * tiles_n), block(WM * WN * 64);
-  auto kern = bitserial ? gemm_i8_kernel<BM, BN, WM, WN, RB, NST, true>
-                        : gemm_i8_kernel<BM, BN, WM, WN, RB, NST, false>;
+  const dim3 grid(tiles_m * tiles_n), block(WM * WN * KW * 64);
+  auto kern = bitserial ? gemm_i8_kernel<BM, BN, WM, WN, RB, NST, KW, true>
+                        : gemm_i8_kernel<BM, BN, WM, WN, RB, NST, KW, false>;
   if (ev0 != nullptr || ev1 != nullptr)   // timestamps of this dispatch itself
     hipExtLaunchKernelGGL(kern, grid, block, 0, s, ev0, ev1, 0, xq, sa, wq, sw, M, N, K, kbits, y,
                           acc, tiles_m, tiles_n, gate);
@@ -220,7 +278,9 @@ hipError_t launch_cfg(bool bitserial, const int8_t* xq, const float* sa, const i
 
 int gemm_config_count() { return kNumCfgs; }
 
-GemmConfig gemm_config(int index) { return GemmConfig{kCfgs[index].bm, kCfgs[index].bn, 1}; }
+GemmConfig gemm_config(int index) {
+  return GemmConfig{kCfgs[index].bm, kCfgs[index].bn, kCfgs[index].kw};
+}
 
 // Estimated time of a configuration: tiles land round-robin on the CUs, so
 // the busiest CU runs ceil(tiles / CUs) of them (several at once when they
@@ -229,31 +289,52 @@ GemmConfig gemm_config(int index) { return GemmConfig{kCfgs[index].bm, kCfgs[ind
 // shapes on MI355X; callers that want the measured best use
 // tabit_autotune_gemm.
 int gemm_config_choose(int M, int N, int K, int num_cus) {
-  (void)K;
   if (num_cus <= 0) num_cus = 256;
+  auto tiles_of = [&](const CfgDesc& c) {
+    return (long long)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+  };
   int best = 0;
   double best_cost = 1e300;
   for (int i = 0; i < kNumCfgs; ++i) {
     const CfgDesc& c = kCfgs[i];
-    const long long tiles = (long long)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
-    const long long per_cu = (tiles + num_cus - 1) / num_cus;
+    if (c.kw != 1) continue;
+    const long long per_cu = (tiles_of(c) + num_cus - 1) / num_cus;
     const double cost = (double)per_cu * c.bm * c.bn / c.rate;
     if (cost < best_cost * 0.999) {
       best_cost = cost;
       best = i;
     }
   }
-  return best;
+  // a tile that leaves at least half of the CUs idle gives way to its K-split
+  // variant with the fewest stages per group (then the fewest groups): at
+  // 64 x 1152 x 1152 three groups of 2 x 2 waves take the masked GEMM from 8.5
+  // to 6.7 us with the weights cold and the bit-plane form from 13.7 to 8.9 us
+  // (k = 0); one-wave groups, even five of them, were slower
+  const CfgDesc& b = kCfgs[best];
+  if (2 * tiles_of(b) > num_cus) return best;
+  const int S = (K + b.rb - 1) / b.rb;
+  int pick = best, pick_trips = S, pick_kw = 1;
+  for (int i = 0; i < kNumCfgs; ++i) {
+    const CfgDesc& c = kCfgs[i];
+    if (c.kw == 1 || c.bm != b.bm || c.bn != b.bn || c.rb != b.rb) continue;
+    const int trips = (S + c.kw - 1) / c.kw;
+    if (trips < pick_trips || (trips == pick_trips && c.kw < pick_kw)) {
+      pick = i;
+      pick_trips = trips;
+      pick_kw = c.kw;
+    }
+  }
+  return pick;
 }
 
 hipError_t launch_gemm_i8(int cfg, bool bitserial, const int8_t* xq, const float* sa,
                           const int8_t* wq, const float* sw, int M, int N, int K, int kbits,
                           uint16_t* y, int32_t* acc, hipStream_t stream, hipEvent_t ev0,
                           hipEvent_t ev1, const uint8_t* gate) {
-#define TABIT_CASE(I, BM, BN, WM, WN, RB, NST, RATE) \
-  case I:                                            \
-    return launch_cfg<BM, BN, WM, WN, RB, NST>(bitserial, xq, sa, wq, sw, M, N, K, kbits, y, acc, \
-                                               stream, ev0, ev1, gate);
+#define TABIT_CASE(I, BM, BN, WM, WN, RB, NST, KW, RATE)                                        \
+  case I:                                                                                       \
+    return launch_cfg<BM, BN, WM, WN, RB, NST, KW>(bitserial, xq, sa, wq, sw, M, N, K, kbits, y, \
+                                                   acc, stream, ev0, ev1, gate);
   switch (cfg) {
     TABIT_I8_CONFIGS(TABIT_CASE)
     default: return hipErrorInvalidValue;

@@ -120,14 +120,16 @@ gemm_planes_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
   static_assert(NST * STAGE >= BM * BN * 2, "epilogue tile must fit in the LDS stages");
   static_assert(KW >= 1 && (KW - 1) * BM * BN * 4 <= KW * NST * STAGE,
                 "the K groups' partial accumulators must fit in the LDS stages");
+  static_assert(NW * KW * 64 <= 1024, "at most 1024 threads per workgroup");
   __shared__ __attribute__((aligned(1024))) int8_t smem[KW * NST * STAGE];
 
   int tm, tn;
   tile::tile_coords<4>(tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x;
-  const int group = (tid >> 6) / NW;             // K group
-  const int wave = (tid >> 6) % NW, lane = tid & 63;   // wave within the group
+  // K group and wave within it (compile-time 0 and the wave id without a split)
+  const int group = KW > 1 ? (tid >> 6) / NW : 0;
+  const int wave = KW > 1 ? (tid >> 6) % NW : (tid >> 6), lane = tid & 63;
   const int wm = wave / WN, wn = wave % WN;
   int8_t* ring = smem + group * NST * STAGE;
   const int rows_a = min(BM, M - m0);
@@ -144,9 +146,9 @@ gemm_planes_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
   const int ra0 = wm * WTM + (lane & 31), rb0 = wn * WTN + (lane & 31);
   const int khalf = lane >> 5;
   // this group's stages [kt0, kt0 + nk); every group runs `trips` iterations
-  const int trips = (S + KW - 1) / KW;
-  const int kt0 = group * trips;
-  const int nk = max(0, min(S - kt0, trips));
+  const int trips = KW > 1 ? (S + KW - 1) / KW : S;
+  const int kt0 = KW > 1 ? group * trips : 0;
+  const int nk = KW > 1 ? max(0, min(S - kt0, trips)) : S;
   // rotate amounts (t - b + 4*khalf) mod 32 for t - b = -7..3: bit 8q + 4*khalf + t
   // of a word (this lane's weight 4t + q) moves to bit 8q + b
   int rot[11];
@@ -167,7 +169,9 @@ gemm_planes_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
     else if (NST >= 3 && ahead >= 1) tile::wait_vmcnt<(NST >= 3 ? 1 : 0) * DPW>();
     else tile::wait_vmcnt<0>();
     __syncthreads();   // stage kt visible to all; stage kt-1's buffer is free
-    if (kt >= nk) continue;   // this group's range is done (the barrier above still counts it)
+    if constexpr (KW > 1) {
+      if (kt >= nk) continue;   // this group's range is done (the barrier above still counts it)
+    }
     if (kt + NST - 1 < nk) issue(kt + NST - 1);
     const int8_t* sa = ring + (kt % NST) * STAGE;
     const int8_t* sp = sa + SA_BYTES;
@@ -242,7 +246,7 @@ gemm_planes_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
             }
     }
   }
-  const bool out = group == 0;   // the waves that hold the tile's sums
+  const bool out = KW == 1 || group == 0;   // the waves that hold the tile's sums
 
   // 32x32 output layout: lane l, register r holds row (r/4)*8 + (l/32)*4 + r%4, col l%32.
   const int row_w = m0 + wm * WTM, col_w = n0 + wn * WTN;
