@@ -394,9 +394,13 @@ enum tabit_option {
 int tabit_set_option(tabit_ctx* ctx, int option, int value);
 
 /* Describe INT8 GEMM tile configuration `index` (0 <= index < count): block
- * tile BM x BN, split-K factor.  Returns the number of configurations when
- * index < 0.  Makes no HIP call. */
-int tabit_gemm_config_info(int index, int* bm, int* bn, int* split_k);
+ * tile BM x BN and, in *k_groups, the number of wave groups that split the K
+ * stages of one tile inside its workgroup (1 = no split; the groups' int32
+ * sums are added exactly, so every configuration gives the same result; the
+ * automatic choice, tabit_gemm_config_choose, takes a split tile only when the
+ * one-group tile leaves at least half of the CUs idle).  Returns the number of
+ * configurations when index < 0.  Makes no HIP call. */
+int tabit_gemm_config_info(int index, int* bm, int* bn, int* k_groups);
 
 /* As tabit_gemm_config_info, for the MXFP4 GEMM's tile configurations. */
 int tabit_mxfp4_config_info(int index, int* bm, int* bn);

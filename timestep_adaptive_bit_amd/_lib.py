@@ -155,7 +155,7 @@ def act_workspace_bytes(M: int, K: int) -> int:
 
 
 def gemm_config_info(index: int = -1):
-    """Number of INT8 GEMM configs (index < 0) or (bm, bn, split_k) of one."""
+    """Number of INT8 GEMM configs (index < 0) or (bm, bn, k_groups) of one."""
     lib = load()
     if index < 0:
         return int(lib.tabit_gemm_config_info(-1, None, None, None))

@@ -722,14 +722,14 @@ int tabit_set_option(tabit_ctx* ctx, int option, int value) {
   }
 }
 
-int tabit_gemm_config_info(int index, int* bm, int* bn, int* split_k) {
+int tabit_gemm_config_info(int index, int* bm, int* bn, int* k_groups) {
   if (index < 0) return tabit::gemm_config_count();
-  if (index >= tabit::gemm_config_count() || bm == nullptr || bn == nullptr || split_k == nullptr)
+  if (index >= tabit::gemm_config_count() || bm == nullptr || bn == nullptr || k_groups == nullptr)
     return TABIT_EINVAL;
   const tabit::GemmConfig c = tabit::gemm_config(index);
   *bm = c.bm;
   *bn = c.bn;
-  *split_k = c.split_k;
+  *k_groups = c.split_k;
   return TABIT_OK;
 }
 
