@@ -187,6 +187,20 @@ def record_traffic(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_bytes
     print(json.dumps(rec))
 
 
+def read_sclk():
+    """The GPU's current shader clock level as the driver reports it (sysfs
+    pp_dpm_sclk, the line marked '*'), or None where it cannot be read."""
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if "*" in line:
+                        return line.split(":", 1)[-1].replace("*", "").strip()
+        except OSError:
+            continue
+    return None
+
+
 def single_gemm(shape, reps: int) -> None:
     """`reps` launches of one masked INT8 GEMM (M, N, K, tile config) on seeded
     synthetic codes, for counter passes over a single kernel."""
@@ -619,8 +633,8 @@ def gemm_tiles(T, wl, tuned, path=0):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5, help="timed schedule passes")
-    ap.add_argument("--warmup", type=int, default=2, help="untimed schedule passes")
+    ap.add_argument("--steps", type=int, default=10, help="timed schedule passes")
+    ap.add_argument("--warmup", type=int, default=3, help="untimed schedule passes")
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--path", default="masked", choices=["masked", "bitserial", "planes", "hqdm"])
     ap.add_argument("--had-block", type=int, default=None, help="override the workload's block")
@@ -797,6 +811,18 @@ def main() -> int:
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
+    # ---- per-pass times: the same K passes again, an event pair around each (median and
+    # spread reported beside `value`, which comes from the uninstrumented region above)
+    pass_ms = []
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        one_pass()
+        e1.record()
+        pass_ms.append((e0, e1))
+    torch.cuda.synchronize()
+    pass_ms = sorted(a.elapsed_time(b) for a, b in pass_ms)
+
     # ---- instrumented region: the same K passes with a start/stop event pair attached
     # to every GEMM dispatch (the runtime stamps them with that kernel's own start and
     # end); kept out of the region that gives `value`
@@ -819,7 +845,9 @@ def main() -> int:
     value = total_ops / (ms_per_step / 1e3) / 1e12
 
     roofline = None
-    detail = {}
+    detail = {"pass_ms_median": round(pass_ms[len(pass_ms) // 2], 3),
+              "pass_ms_min": round(pass_ms[0], 3), "pass_ms_max": round(pass_ms[-1], 3),
+              "sclk": read_sclk()}
     if not args.no_events:
         gemm_ms_i8 = gemm_ms_mx = 0.0
         n_i8 = n_mx = 0
