@@ -1,0 +1,61 @@
+"""GPU parity of the K-split tiles (few tokens, long K) under the automatic choice.
+
+The library's chooser replaces a tile that leaves half of the CUs idle with a
+variant whose K stages are split over wave groups inside the workgroup; the
+groups' int32 sums are added exactly, so the bars are the unsplit ones:
+accumulators bit-exact against the oracle (masked, bit-plane and plane-major
+forms), bf16 within 1e-2 relative and identical across the three forms.
+Shapes: one token; K with a ragged last stage; more groups than stages (some
+groups walk none); a stage count the groups do not divide.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import tabit_oracle as O
+import tabit_synth as S
+import timestep_adaptive_bit_amd as T
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    c = T.Context()
+    yield c
+    c.close()
+
+
+SHAPES = [(1, 32, 8192), (3, 64, 4160), (64, 1152, 4608), (17, 96, 160), (40, 320, 1120)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_auto_ksplit_bit_exact(ctx, M, N, K):
+    cfg = T.gemm_config_choose(M, N, K)
+    pcfg = T.plane_config_choose(M, N, K)
+    print(f"ksplit {M}x{N}x{K}: int8 cfg {cfg} {T.gemm_config_info(cfg)}, "
+          f"plane cfg {pcfg} {T.plane_config_info(pcfg)}", flush=True)
+    if (K + 127) // 128 > 1:                    # more than one stage: a split tile is chosen
+        assert T.gemm_config_info(cfg)[2] > 1
+        assert T.plane_config_info(pcfg)[2] > 1
+    xq = S.gen_int8((M, K), seed=M + K)
+    wq = S.gen_int8((N, K), seed=N + K, lo=-128, hi=127)
+    xq[0, :] = -127
+    wq[0, :] = -128
+    sa, sw = S.gen_scales(M, seed=5), S.gen_scales(N, seed=6)
+    dx, dw = torch.from_numpy(xq).to(DEV), torch.from_numpy(wq).to(DEV)
+    dsa, dsw = torch.from_numpy(sa).to(DEV), torch.from_numpy(sw).to(DEV)
+    dp = ctx.pack_weight_planes(dw)
+    for k in (0, 3, 7):
+        ref = O.masked_gemm_i32(xq, wq, k)
+        y_ref = O.dequant(ref, sa, sw)
+        ym, am = ctx.masked_qgemm(dx, dsa, dw, dsw, k, want_acc=True)
+        yb, ab = ctx.qgemm_bitserial(dx, dsa, dw, dsw, k, want_acc=True)
+        yp, ap = ctx.plane_qgemm(dx, dsa, dp, dsw, k, want_acc=True)
+        torch.cuda.synchronize()
+        for name, acc in (("masked", am), ("bit-plane", ab), ("plane-major", ap)):
+            np.testing.assert_array_equal(acc.cpu().numpy(), ref, err_msg=f"{name} k {k}")
+        yy = ym.float().cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(yy - y_ref) <= 1e-2 * np.abs(y_ref) + 1e-30), f"k {k}"
+        assert torch.equal(ym, yb) and torch.equal(ym, yp), f"k {k}: bf16 differs between forms"
