@@ -131,18 +131,21 @@ def summarize_counters(mfma_dir: str, fetch_dir: str, write_dir: str, cal_fetch_
 
     def short(name):
         return name.replace("void ", "").replace("tabit::(anonymous namespace)::", "").split("(")[0]
-    print("# GEMM (per dispatch, grouped by tile config): MFMA ops executed = MOPS_I8 x 512;")
-    print("# MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs), rocprof's MfmaUtil")
-    print(f"{'kernel':58s} {'n':>5s} {'MFMA Gop':>9s} {'util%':>6s} {'us':>7s} {'TOPS':>7s}")
-    groups = {}
-    for r in _pmc_rows(mfma_dir, "gemm_i8"):
-        groups.setdefault(short(r["_name"]), []).append(r)
-    for k, rs in sorted(groups.items()):
-        ops = sum(r.get("SQ_INSTS_VALU_MFMA_MOPS_I8", 0) * 512 for r in rs) / len(rs)
-        busy = sum(r.get("SQ_VALU_MFMA_BUSY_CYCLES", 0)
-                   / max(1.0, r.get("GRBM_GUI_ACTIVE", 1) / xcds * simds) for r in rs) / len(rs)
-        us = sum(r["_dur_ns"] for r in rs) / len(rs) / 1e3
-        print(f"{k:58s} {len(rs):5d} {ops / 1e9:9.2f} {100 * busy:6.1f} {us:7.2f} {ops / us / 1e6:7.1f}")
+    print("# GEMM (per dispatch, grouped by tile config): MFMA ops executed = MOPS x 512 (MOPS_I8 for")
+    print("# the INT8 kernels, MOPS_F6F4 for the MXFP4 one); MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /")
+    print("# (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs), rocprof's MfmaUtil; rate in T ops (or flops) per s")
+    print(f"{'kernel':58s} {'n':>5s} {'MFMA Gop':>9s} {'util%':>6s} {'us':>7s} {'T/s':>7s}")
+    for family, counter in (("gemm_i8", "SQ_INSTS_VALU_MFMA_MOPS_I8"),
+                            ("gemm_mxfp4", "SQ_INSTS_VALU_MFMA_MOPS_F6F4")):
+        groups = {}
+        for r in _pmc_rows(mfma_dir, family):
+            groups.setdefault(short(r["_name"]), []).append(r)
+        for k, rs in sorted(groups.items()):
+            ops = sum(r.get(counter, 0) * 512 for r in rs) / len(rs)
+            busy = sum(r.get("SQ_VALU_MFMA_BUSY_CYCLES", 0)
+                       / max(1.0, r.get("GRBM_GUI_ACTIVE", 1) / xcds * simds) for r in rs) / len(rs)
+            us = sum(r["_dur_ns"] for r in rs) / len(rs) / 1e3
+            print(f"{k:58s} {len(rs):5d} {ops / 1e9:9.2f} {100 * busy:6.1f} {us:7.2f} {ops / us / 1e6:7.1f}")
     shapes = sorted({(l.M, l.N, l.K) for l in wl.layers})
     print("# algorithmic 2MNK per shape (Gop): " +
           ", ".join(f"{m}x{n}x{k} {2 * m * n * k / 1e9:.2f}" for m, n, k in shapes))
@@ -157,6 +160,8 @@ def summarize_counters(mfma_dir: str, fetch_dir: str, write_dir: str, cal_fetch_
         rd = sum(r["FETCH_SIZE"] for r in fr) / len(fr) * 1024 / cf
         wb = sum(r["WRITE_SIZE"] for r in wr) / len(wr) * 1024 / cw
         us = sum(r["_dur_ns"] for r in fr + wr) / len(fr + wr) / 1e3
+        if not wr:
+            continue
         print(f"{short(k):58s} {len(fr):5d} {rd / 1e6:8.2f} {wb / 1e6:9.2f} {us:7.2f} "
               f"{(rd + wb) / us / 1e3:8.0f} {100 * (rd + wb) / us / 8e6:7.1f}")
 
@@ -652,6 +657,8 @@ def main() -> int:
                     help="only run the CogVideoX-shaped schedule with the online INT8/4-bit selector")
     ap.add_argument("--dmpq-steps", type=int, default=0, help="denoising steps for --dmpq (0 = 50)")
     ap.add_argument("--dmpq-theta", type=float, default=0.2, help="selector threshold on Gamma")
+    ap.add_argument("--denoise-steps", type=int, default=0,
+                    help="run only the schedule's first N denoising steps (profiling runs)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one schedule pass captured in a HIP graph")
     ap.add_argument("--cold", action="store_true",
@@ -717,6 +724,12 @@ def main() -> int:
         return 0
     wl = S.WORKLOADS[args.workload]() if args.had_block is None else \
         S.WORKLOADS[args.workload](had_block=args.had_block)
+    if args.denoise_steps:
+        # the schedule's first N steps only (profiling runs: per-dispatch counters do not
+        # depend on how many steps run)
+        import dataclasses
+        n = min(args.denoise_steps, wl.steps)
+        wl = dataclasses.replace(wl, steps=n, k_bits=wl.k_bits[:n], fmt=wl.fmt[:n])
     b = wl.had_block
     L, Tn = wl.num_layers, wl.steps
     ctx = T.Context()
