@@ -729,7 +729,7 @@ int tabit_gemm_config_info(int index, int* bm, int* bn, int* k_groups) {
   const tabit::GemmConfig c = tabit::gemm_config(index);
   *bm = c.bm;
   *bn = c.bn;
-  *k_groups = c.split_k;
+  *k_groups = c.k_groups;
   return TABIT_OK;
 }
 
@@ -748,7 +748,7 @@ int tabit_plane_config_info(int index, int* bm, int* bn, int* k_groups) {
   const tabit::GemmConfig c = tabit::plane_config(index);
   *bm = c.bm;
   *bn = c.bn;
-  if (k_groups != nullptr) *k_groups = c.split_k;
+  if (k_groups != nullptr) *k_groups = c.k_groups;
   return TABIT_OK;
 }
 

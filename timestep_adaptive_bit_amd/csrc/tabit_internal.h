@@ -42,7 +42,7 @@ hipError_t launch_quant_mx(const uint16_t* x, int M, int K, int had_block,
 
 // ---------------------------------------------------------------- INT8 GEMM
 struct GemmConfig {
-  int bm, bn, split_k;   // split_k: K groups per tile (1 = none)
+  int bm, bn, k_groups;   // wave groups splitting one tile's K stages (1 = none)
 };
 int gemm_config_count();
 GemmConfig gemm_config(int index);
