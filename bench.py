@@ -921,8 +921,13 @@ def main() -> int:
             hip.destroy(e)
         if n_i8:
             achieved = (int8_ops * args.steps) / (gemm_ms_i8 / 1e3) / 1e12
+            sustained = ctx.mfma_peak_probe(0, 20000) / 1e12
             roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS,
                         "unit": "TOPS", "frac": round(achieved / INT8_PEAK_TOPS, 4),
+                        "peak_measured": round(sustained, 1),
+                        "frac_of_measured": round(achieved / sustained, 4),
+                        "peak_measured_how": "register-only INT8 MFMA chains on every SIMD "
+                                             "(tabit_mfma_peak_probe), after the timed passes",
                         "traffic": recorded_traffic(wl.name, args.path),
                         "kernel": {T.PATH_MASKED: "gemm_i8_kernel (masked)",
                                    T.PATH_BITSERIAL: "gemm_i8_kernel (bitserial)",
@@ -935,6 +940,9 @@ def main() -> int:
             mx_tops = (mx_ops * args.steps) / (gemm_ms_mx / 1e3) / 1e12
             detail["gemm_mxfp4_tops"] = round(mx_tops, 2)
             detail["gemm_mxfp4_frac_of_peak"] = round(mx_tops / MXFP4_PEAK_TOPS, 4)
+            mx_sustained = ctx.mfma_peak_probe(1, 20000) / 1e12
+            detail["mxfp4_peak_measured_tflops"] = round(mx_sustained, 1)
+            detail["gemm_mxfp4_frac_of_measured"] = round(mx_tops / mx_sustained, 4)
             detail["gemm_mxfp4_ms_per_step"] = round(gemm_ms_mx / args.steps, 3)
             if roofline is None:
                 roofline = {"bound": "mfma", "achieved": round(mx_tops, 2), "peak": MXFP4_PEAK_TOPS,

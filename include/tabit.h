@@ -422,6 +422,26 @@ int tabit_plane_config_choose(int M, int N, int K, int num_cus);
 /* As tabit_mxfp4_config_info, for the HQ-DM GEMM's tile configurations. */
 int tabit_hqdm_config_info(int index, int* bm, int* bn);
 
+/*
+ * Sustained matrix-core rate of the current device at its running clock (the
+ * measured side of the roofline beside the published peak): every CU runs four
+ * workgroups of four waves, each wave `iters` rounds of independent MFMA
+ * chains on register operands, with no memory traffic in the loop.
+ *   kind   0: v_mfma_i32_32x32x32_i8 (INT8 ops), 1: the FP4 block-scaled
+ *          32x32x64 MFMA (FP4 flops).
+ *   iters  rounds per wave, 1 .. 2^24 (20000 runs for about 2 ms).
+ *   sink   device int32 [tabit_mfma_probe_sink_ints(number of CUs)]: one word per
+ *          thread keeps the chains live; its contents mean nothing.
+ *   ops_per_s  host: operations per second of the launch, timed by its own
+ *          start/stop events.
+ * Enqueues on `stream` and synchronizes on the stop event: call it outside
+ * graph capture.  EINVAL / ERANGE / ESHAPE for bad arguments, EHIP for a launch
+ * error.
+ */
+int tabit_mfma_peak_probe(tabit_ctx* ctx, int kind, int iters, int32_t* sink, size_t sink_ints,
+                          double* ops_per_s, void* stream);
+size_t tabit_mfma_probe_sink_ints(int num_cus);
+
 /* The configuration the automatic choice would take for (M, N, K) on a device
  * with num_cus compute units (num_cus <= 0: 256).  Makes no HIP call. */
 int tabit_gemm_config_choose(int M, int N, int K, int num_cus);

@@ -234,6 +234,18 @@ def test_workspace_bytes():
     assert T.act_workspace_bytes(0, 64) == 0
 
 
+def test_mfma_probe_validation(ctx, lib):
+    """Argument errors come back before any HIP call."""
+    out = ctypes.c_double()
+    fake = ctypes.c_void_p(4096)
+    assert lib.tabit_mfma_peak_probe(ctx._h, 2, 10, fake, 1 << 20, ctypes.byref(out), None) == T.EINVAL
+    assert lib.tabit_mfma_peak_probe(ctx._h, 0, 0, fake, 1 << 20, ctypes.byref(out), None) == T.ERANGE
+    assert lib.tabit_mfma_peak_probe(ctx._h, 0, 10, None, 1 << 20, ctypes.byref(out), None) == T.EINVAL
+    assert lib.tabit_mfma_peak_probe(ctx._h, 0, 10, fake, 1 << 20, None, None) == T.EINVAL
+    assert lib.tabit_mfma_peak_probe(None, 0, 10, fake, 1 << 20, ctypes.byref(out), None) == T.EINVAL
+    assert lib.tabit_mfma_probe_sink_ints(256) >= 256 * 64
+
+
 def test_options_and_configs(ctx):
     n = T.gemm_config_info()
     assert n >= 1

@@ -65,6 +65,9 @@ _SIGNATURES = {
                                    _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
     "tabit_plane_config_info": (_c_int, [_c_int, _PINT, _PINT, _PINT]),
     "tabit_plane_config_choose": (_c_int, [_c_int, _c_int, _c_int, _c_int]),
+    "tabit_mfma_peak_probe": (_c_int, [_c_void_p, _c_int, _c_int, _c_void_p, _c_size_t,
+                                       ctypes.POINTER(ctypes.c_double), _c_void_p]),
+    "tabit_mfma_probe_sink_ints": (_c_size_t, [_c_int]),
     "tabit_weight_planes_bytes": (_c_size_t, [_c_int, _c_int]),
     "tabit_dmpq_workspace_bytes": (_c_size_t, [_c_int]),
     "tabit_gelu_quant_act": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p,
@@ -534,6 +537,19 @@ class Context:
             act_ws.numel() * act_ws.element_size(),
             None if gemm_events is None else ctypes.cast(gemm_events, ctypes.c_void_p), stream)
         self._check(st)
+
+    def mfma_peak_probe(self, kind: int = 0, iters: int = 20000, device="cuda:0") -> float:
+        """Sustained matrix-core rate (ops or flops per second) of the device at its
+        running clock: kind 0 INT8 MFMA, 1 FP4 scaled MFMA.  Synchronizes."""
+        dev = torch.device(device)
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        n = int(self._lib.tabit_mfma_probe_sink_ints(cus))
+        sink = torch.empty(n, dtype=torch.int32, device=dev)
+        out = ctypes.c_double()
+        st = self._lib.tabit_mfma_peak_probe(self._h, kind, iters, sink.data_ptr(), n,
+                                             ctypes.byref(out), _stream(dev))
+        self._check(st)
+        return out.value
 
     def autotune_gemm(self, path: int, x_q, x_scale, w_q, w_scale, M: int, N: int, K: int,
                       k_bits: int, y: torch.Tensor, reps: int = 3) -> int:

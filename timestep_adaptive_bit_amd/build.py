@@ -18,7 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libtabit.so")
-SOURCES = ["api.hip", "quant.hip", "gemm_i8.hip", "gemm_mxfp4.hip", "gemm_planes.hip", "dmpq.hip", "gemm_hqdm.hip"]
+SOURCES = ["api.hip", "quant.hip", "gemm_i8.hip", "gemm_mxfp4.hip", "gemm_planes.hip", "dmpq.hip",
+           "gemm_hqdm.hip", "probe.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

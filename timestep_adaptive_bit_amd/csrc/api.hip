@@ -757,6 +757,37 @@ int tabit_plane_config_choose(int M, int N, int K, int num_cus) {
   return tabit::plane_config_choose(M, N, K, num_cus);
 }
 
+size_t tabit_mfma_probe_sink_ints(int num_cus) {
+  return tabit::mfma_probe_sink_ints(num_cus > 0 ? num_cus : 256);
+}
+
+int tabit_mfma_peak_probe(tabit_ctx* ctx, int kind, int iters, int32_t* sink, size_t sink_ints,
+                          double* ops_per_s, void* stream) {
+  if (ctx == nullptr) return TABIT_EINVAL;
+  if (kind != 0 && kind != 1) return fail(ctx, TABIT_EINVAL, "probe kind must be 0 or 1 (got %d)", kind);
+  if (iters < 1 || iters > (1 << 24))
+    return fail(ctx, TABIT_ERANGE, "iters must be in [1, 2^24] (got %d)", iters);
+  if (sink == nullptr || ops_per_s == nullptr) return fail(ctx, TABIT_EINVAL, "null pointer");
+  const int num_cus = tabit::device_num_cus();
+  if (sink_ints < tabit::mfma_probe_sink_ints(num_cus))
+    return fail(ctx, TABIT_ESHAPE, "sink holds %zu ints, %zu needed", sink_ints,
+                tabit::mfma_probe_sink_ints(num_cus));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  double ops = 0.0;
+  if (e == hipSuccess) ops = tabit::launch_mfma_probe(kind, iters, num_cus, sink, s, e0, e1, &e);
+  if (e == hipSuccess) e = hipEventSynchronize(e1);
+  float ms = 0.0f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (e != hipSuccess) return hip_status(ctx, e, "mfma probe");
+  *ops_per_s = ms > 0.0f ? ops / (ms * 1e-3) : 0.0;
+  return TABIT_OK;
+}
+
 int tabit_gemm_config_choose(int M, int N, int K, int num_cus) {
   return tabit::gemm_config_choose(M, N, K, num_cus);
 }

@@ -96,6 +96,13 @@ hipError_t launch_dmpq_select(const uint16_t* xin, const uint16_t* xout, int M, 
                               const float* theta, int n_layers, uint8_t* fmt, double* gamma,
                               hipStream_t s);
 
+// ---------------------------------------------------------------- matrix-core rate probe
+// kind 0: INT8 32x32x32 MFMA; kind 1: FP4 32x32x64 scaled MFMA.  sink holds
+// mfma_probe_sink_ints(num_cus) ints.  Returns the operations the launch performs.
+size_t mfma_probe_sink_ints(int num_cus);
+double launch_mfma_probe(int kind, int iters, int num_cus, int* sink, hipStream_t s,
+                         hipEvent_t ev0, hipEvent_t ev1, hipError_t* err);
+
 // Compute units of the current device (cached per device id).
 int device_num_cus();
 
