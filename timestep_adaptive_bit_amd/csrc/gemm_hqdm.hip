@@ -152,8 +152,10 @@ struct HqCfg {
 // index, BM, BN, WM, WN, rate
 #define TABIT_HQ_CONFIGS(X)     \
   X(0, 128, 128, 2, 2, 1.00f)   \
-  X(1, 128, 64, 2, 2, 0.80f)    \
-  X(2, 64, 64, 2, 2, 0.55f)
+  X(1, 128, 64, 2, 2, 0.94f)    \
+  X(2, 64, 64, 2, 2, 0.86f)     \
+  X(3, 256, 128, 2, 4, 1.19f)   \
+  X(4, 128, 256, 2, 4, 1.33f)
 #define TABIT_HDESC(I, BM, BN, WM, WN, RATE) {BM, BN, WM, WN, RATE},
 constexpr HqCfg kHqCfgs[] = {TABIT_HQ_CONFIGS(TABIT_HDESC)};
 #undef TABIT_HDESC
