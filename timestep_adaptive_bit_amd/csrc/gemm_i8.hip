@@ -58,11 +58,14 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
   constexpr int DPW = STAGE / 1024 / NW;        // DMA instructions per wave per stage
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold whole 32x32 blocks");
   static_assert(NST >= 2 && NST <= 4, "2 to 4 LDS stages");
-  static_assert(NST * STAGE >= BM * BN * 2, "epilogue tile must fit in the LDS stages");
   static_assert(KW >= 1 && (KW - 1) * BM * BN * 4 <= KW * NST * STAGE,
                 "the K groups' partial accumulators must fit in the LDS stages");
   static_assert(NW * KW * 64 <= 1024, "at most 1024 threads per workgroup");
-  __shared__ __attribute__((aligned(1024))) int8_t smem[KW * NST * STAGE];
+  static_assert(NST == 2 || (BM % (8 * NW) == 0 && BN % (8 * NW) == 0),
+                "deeper rings count copies per wave: every wave copies the same share");
+  // the ring, or the bf16 staging of the epilogue when that is larger
+  constexpr int SMEM = KW * NST * STAGE > BM * BN * 2 ? KW * NST * STAGE : BM * BN * 2;
+  __shared__ __attribute__((aligned(1024))) int8_t smem[SMEM];
 
   int tm, tn;
   tile::tile_coords<4>(tiles_m, tiles_n, tm, tn);
@@ -242,17 +245,23 @@ struct CfgDesc {
   int bm, bn, wm, wn, rb, nst, kw;
   float rate;   // relative throughput per CU on its tiles (fitted to MI355X sweeps)
 };
+// Twelve or sixteen waves per large tile (wave tiles of 64 x 64 or 64 x 96):
+// on MI355X these beat the same tiles with eight waves of 128 x 64 by 3-15%
+// at every DiT shape (more waves per SIMD keep the matrix cores fed between
+// barriers), and the 288- and 192-wide tiles split N = 1152, 1920, 4608, 7680
+// into whole rounds of tiles over the CUs.  Rates are the median per-tile
+// rates of a graph-replayed sweep of every tile over 22 DiT shapes (the
+// chooser then loses 1.1% on average, at most 6%, to the best tile).
 // index, BM, BN, WM, WN, stage row bytes, LDS stages, K groups, rate
 #define TABIT_I8_CONFIGS(X)                \
-  X(0, 256, 256, 2, 4, 128, 2, 1, 1.00f)    \
-  X(1, 192, 192, 2, 3, 128, 3, 1, 0.71f)    \
-  X(2, 128, 128, 2, 2, 128, 2, 1, 0.79f)    \
-  X(3, 256, 128, 2, 2, 128, 3, 1, 0.68f)    \
-  X(4, 128, 64, 2, 2, 128, 2, 1, 0.665f)    \
-  X(5, 64, 64, 2, 2, 128, 2, 1, 0.52f)      \
-  X(6, 192, 128, 2, 2, 128, 2, 1, 0.66f)    \
-  X(7, 64, 64, 2, 2, 128, 2, 3, 0.52f)      \
-  X(8, 128, 64, 2, 2, 128, 2, 3, 0.665f)
+  X(0, 256, 256, 4, 4, 128, 2, 1, 1.00f)    \
+  X(1, 256, 288, 4, 3, 128, 2, 1, 1.04f)    \
+  X(2, 256, 192, 4, 3, 128, 2, 1, 0.88f)    \
+  X(3, 128, 128, 4, 2, 128, 2, 1, 0.65f)    \
+  X(4, 128, 96, 4, 3, 128, 2, 1, 0.58f)     \
+  X(5, 64, 64, 2, 2, 128, 2, 1, 0.48f)      \
+  X(6, 128, 192, 4, 3, 128, 2, 1, 0.71f)    \
+  X(7, 64, 64, 2, 2, 128, 2, 3, 0.48f)
 #define TABIT_DESC(I, BM, BN, WM, WN, RB, NST, KW, RATE) {BM, BN, WM, WN, RB, NST, KW, RATE},
 constexpr CfgDesc kCfgs[] = {TABIT_I8_CONFIGS(TABIT_DESC)};
 #undef TABIT_DESC

@@ -39,17 +39,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, unsig
 // kb0 of each row.  Each wave instruction fills one 1 KB LDS block (1024/RB
 // rows); lane l writes slot l % (RB/16) of row l / (RB/16) of that block, so it
 // fetches the logical chunk the swizzle places there.  Rows past rows_valid and
-// chunks past row_bytes read out of range and land as zeros.
+// chunks past row_bytes read out of range and land as zeros.  Block j goes to
+// wave j % NWAVES; when the blocks do not split evenly, the first waves take
+// one more (callers then wait for all of a stage's copies at once).
 template <int ROWS, int NWAVES, int RB = 128>
 __device__ __forceinline__ void dma_stage(__amdgpu_buffer_rsrc_t rs, int8_t* lds, int row0,
                                           int rows_valid, int row_bytes, int kb0, int wave,
                                           int lane) {
   constexpr int CPR = RB / 16;           // chunks per row
   constexpr int RPB = 1024 / RB;         // rows per 1 KB block
-  static_assert(ROWS % (RPB * NWAVES) == 0, "tile rows must split evenly over the waves");
+  constexpr int BLOCKS = ROWS / RPB;
+  static_assert(ROWS % RPB == 0, "tile rows must fill whole 1 KB blocks");
 #pragma unroll
-  for (int i = 0; i < ROWS / RPB / NWAVES; ++i) {
+  for (int i = 0; i < (BLOCKS + NWAVES - 1) / NWAVES; ++i) {
     const int j = i * NWAVES + wave;
+    if (BLOCKS % NWAVES != 0 && j >= BLOCKS) break;   // wave-uniform
     const int r = RPB * j + lane / CPR;
     const int c = (lane % CPR) ^ swz<RB>(r);
     const int gk = kb0 + c * 16;
@@ -130,6 +134,8 @@ __device__ __forceinline__ void store_tile_bf16(uint16_t* st, int lane, uint16_t
 // As store_tile_bf16, for the 32x32 MFMA output layout: fragment (i, j) is a
 // 32 x 32 block; lane l, register r holds row (r/4)*8 + (l/32)*4 + r%4, column
 // l%32.  `val(i, j, r)` gives the bf16 of fragment (i, j), register r.  The
+// chunk swizzle XORs within aligned groups of SW chunks, SW the largest power
+// of two dividing the row's chunk count (12 chunks of a 96-wide tile: 4).  The
 // global stores are nontemporal (1.6-5% faster on MI355X than plain stores for
 // the 128 x 64 and 256 x 256 tiles).
 // `active` = false: the wave only takes part in the barrier (for workgroups
@@ -138,7 +144,7 @@ template <int WTM, int WTN, typename F>
 __device__ __forceinline__ void store_tile32_bf16(uint16_t* st, int lane, uint16_t* __restrict__ Y,
                                                   int row0, int col0, int M, int N, F val,
                                                   bool active = true) {
-  constexpr int FM = WTM / 32, FN = WTN / 32, CH = WTN / 8;
+  constexpr int FM = WTM / 32, FN = WTN / 32, CH = WTN / 8, SW = CH & -CH;
   if (active) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -148,7 +154,7 @@ __device__ __forceinline__ void store_tile32_bf16(uint16_t* st, int lane, uint16
         for (int r = 0; r < 16; ++r) {
           const int lr = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
           const int lc = j * 32 + (lane & 31);
-          const int ch = (lc >> 3) ^ (lr & (CH - 1));
+          const int ch = (lc >> 3) ^ (lr & (SW - 1));
           st[lr * WTN + ch * 8 + (lc & 7)] = val(i, j, r);
         }
   }
@@ -159,7 +165,7 @@ __device__ __forceinline__ void store_tile32_bf16(uint16_t* st, int lane, uint16
     const int idx = it * 64 + lane;
     const int lr = idx / CH, ch = idx % CH;
     const int gm = row0 + lr, gn = col0 + ch * 8;
-    const v4u v = *reinterpret_cast<const v4u*>(st + lr * WTN + ((ch ^ (lr & (CH - 1))) * 8));
+    const v4u v = *reinterpret_cast<const v4u*>(st + lr * WTN + ((ch ^ (lr & (SW - 1))) * 8));
     // streaming store: the tile is written once and read by the next kernel
     if (gm < M && gn < N) __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(Y + (size_t)gm * N + gn));
   }
