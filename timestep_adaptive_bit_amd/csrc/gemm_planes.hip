@@ -288,11 +288,15 @@ struct PlaneCfg {
   int bm, bn, wm, wn, nst, kw;
   float rate;   // relative per-CU throughput when busy
 };
+// Rates fitted to a graph-replayed sweep (k = 0 and 4, 64 to 4096 tokens):
+// the 128 x 64 tile is as fast per tile element as 128 x 128 on MI355X (the
+// byte rebuild, not the fill, bounds both); 8- and 16-wave tiles were slower
+// (more waves compete for the rebuild's VALU slots).
 // index, BM, BN, WM, WN, LDS stages, K groups, rate
 #define TABIT_PLANE_CONFIGS(X)      \
-  X(0, 64, 32, 1, 1, 4, 1, 0.30f)   \
-  X(1, 64, 64, 1, 2, 2, 1, 0.45f)   \
-  X(2, 128, 64, 1, 2, 2, 1, 0.70f)  \
+  X(0, 64, 32, 1, 1, 4, 1, 0.40f)   \
+  X(1, 64, 64, 1, 2, 2, 1, 0.80f)   \
+  X(2, 128, 64, 1, 2, 2, 1, 1.00f)  \
   X(3, 128, 128, 2, 2, 2, 1, 1.00f) \
   X(4, 64, 32, 1, 1, 2, 3, 0.30f)   \
   X(5, 64, 32, 1, 1, 2, 5, 0.30f)   \
@@ -337,10 +341,11 @@ GemmConfig plane_config(int index) {
 
 // Tiles land round-robin on the CUs, so the busiest CU runs ceil(tiles / CUs)
 // of them; its time is that count times the tile's work over the tile's rate
-// (one K group per workgroup).  When the chosen tile leaves at least half of
-// the CUs idle, the variant of the same tile with the most K groups that cuts
-// the stages each group walks (fewest trips, then fewest groups) replaces it:
-// at 64 x 1152 x 1152 five groups take 17.3 us down to 7.9 (k = 0).
+// (one K group per workgroup).  When the chosen tile's workgroups fit in one
+// round over the CUs, the variant of the same tile with the most K groups that
+// cuts the stages each group walks (fewest trips, then fewest groups) replaces
+// it: at 64 x 1152 x 1152 five groups take 17.3 us down to 7.9 (k = 0), at
+// 256 x 1152 x 1152 (144 tiles) 16.9 down to 8.2.
 int plane_config_choose(int M, int N, int K, int num_cus) {
   if (num_cus <= 0) num_cus = 256;
   auto tiles_of = [&](const PlaneCfg& c) {
@@ -359,7 +364,7 @@ int plane_config_choose(int M, int N, int K, int num_cus) {
     }
   }
   const PlaneCfg& b = kPlaneCfgs[best];
-  if (2 * tiles_of(b) > num_cus) return best;
+  if (tiles_of(b) > num_cus) return best;
   const int S = (K + RB - 1) / RB;
   int pick = best, pick_trips = S, pick_kw = 1;
   for (int i = 0; i < kNumPlaneCfgs; ++i) {
