@@ -6,7 +6,8 @@ groups' int32 sums are added exactly, so the bars are the unsplit ones:
 accumulators bit-exact against the oracle (masked, bit-plane and plane-major
 forms), bf16 within 1e-2 relative and identical across the three forms.
 Shapes: one token; K with a ragged last stage; more groups than stages (some
-groups walk none); a stage count the groups do not divide.
+groups walk none); a stage count the groups do not divide; 216 tiles of 64 x 64
+(most of one round over 256 CUs, where the split still pays).
 """
 import numpy as np
 import pytest
@@ -27,7 +28,8 @@ def ctx():
     c.close()
 
 
-SHAPES = [(1, 32, 8192), (3, 64, 4160), (64, 1152, 4608), (17, 96, 160), (40, 320, 1120)]
+SHAPES = [(1, 32, 8192), (3, 64, 4160), (64, 1152, 4608), (17, 96, 160), (40, 320, 1120),
+          (768, 1152, 1152)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)

@@ -314,13 +314,15 @@ int gemm_config_choose(int M, int N, int K, int num_cus) {
       best = i;
     }
   }
-  // a tile that leaves at least half of the CUs idle gives way to its K-split
-  // variant with the fewest stages per group (then the fewest groups): at
-  // 64 x 1152 x 1152 three groups of 2 x 2 waves take the masked GEMM from 8.5
-  // to 6.7 us with the weights cold and the bit-plane form from 13.7 to 8.9 us
-  // (k = 0); one-wave groups, even five of them, were slower
+  // a tile whose workgroups fit in one round over the CUs gives way to its
+  // K-split variant with the fewest stages per group (then the fewest groups):
+  // at 64 x 1152 x 1152 three groups of 2 x 2 waves take the masked GEMM from
+  // 8.5 to 6.7 us with the weights cold and the bit-plane form from 13.7 to
+  // 8.9 us (k = 0), at 512 x 1152 x 4608 (144 tiles) from 22.2 to 15.2 us and at
+  // 512 x 1920 x 1920 (240 tiles) from 12.3 to 9.2 us; one-wave groups, even
+  // five of them, were slower
   const CfgDesc& b = kCfgs[best];
-  if (2 * tiles_of(b) > num_cus) return best;
+  if (tiles_of(b) > num_cus) return best;
   const int S = (K + b.rb - 1) / b.rb;
   int pick = best, pick_trips = S, pick_kw = 1;
   for (int i = 0; i < kNumCfgs; ++i) {
