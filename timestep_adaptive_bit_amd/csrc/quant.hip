@@ -320,7 +320,8 @@ hipError_t dispatch_int8(int nt, int cpt, int grid, int rows, const uint16_t* x,
                                                              gate, q_lo);                       \
     return hipGetLastError();                                                                   \
   }
-  TABIT_Q(256, 1) TABIT_Q(512, 1) TABIT_Q(1024, 1) TABIT_Q(1024, 2)
+  TABIT_Q(192, 1) TABIT_Q(256, 1) TABIT_Q(320, 1) TABIT_Q(384, 1) TABIT_Q(448, 1) TABIT_Q(512, 1)
+  TABIT_Q(1024, 1) TABIT_Q(1024, 2)
 #undef TABIT_Q
   return hipErrorInvalidValue;
 }
@@ -329,12 +330,14 @@ hipError_t dispatch_int8(int nt, int cpt, int grid, int rows, const uint16_t* x,
 
 namespace {
 
-// Workgroup shape: one 16-element chunk per thread and as few rows per
-// workgroup as fill it (256 threads for rows of up to 256 chunks, else the
-// next power of two; two chunks per thread past 1024 chunks).  Small
-// workgroups with few registers outnumber the resident slots, so reads of
-// late workgroups overlap the stores of early ones; on MI355X this beat
-// fuller multi-row, multi-chunk shapes by 7-32% at the workloads' sizes.
+// Workgroup shape: one 16-element chunk per thread.  Rows of up to 128
+// chunks share 256-thread workgroups; a longer row gets a workgroup of its own
+// sized to the next multiple of 64 threads up to 512 (320 threads for the 288
+// chunks of K = 4608: 13.1 vs 14.0 us at 4096 rows with 512, 13.6 with two
+// rows in 576), then 1024 threads, then two chunks per thread past 1024
+// chunks.  Small workgroups with few registers outnumber the resident slots,
+// so reads of late workgroups overlap the stores of early ones; on MI355X this
+// beat fuller multi-row, multi-chunk shapes by 7-32% at the workloads' sizes.
 template <int MODE>
 hipError_t launch_int8_rows(const uint16_t* x, int M, int K, int had_block, float scale_div,
                             int8_t* q, float* scale, hipStream_t stream, const uint8_t* gate,
@@ -342,8 +345,8 @@ hipError_t launch_int8_rows(const uint16_t* x, int M, int K, int had_block, floa
   if (M <= 0) return hipSuccess;
   const int cr = K / 16;
   int nt = 1024, cpt = 1;
-  if (cr <= 256) nt = 256;
-  else if (cr <= 512) nt = 512;
+  if (cr <= 128) nt = 256;
+  else if (cr <= 512) nt = (cr + 63) / 64 * 64;
   else if (cr > 1024) cpt = 2;
   const int rows = (nt * cpt) / cr;
   const int grid = (M + rows - 1) / rows;
