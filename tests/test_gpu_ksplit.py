@@ -61,3 +61,32 @@ def test_auto_ksplit_bit_exact(ctx, M, N, K):
         yy = ym.float().cpu().numpy().astype(np.float64)
         assert np.all(np.abs(yy - y_ref) <= 1e-2 * np.abs(y_ref) + 1e-30), f"k {k}"
         assert torch.equal(ym, yb) and torch.equal(ym, yp), f"k {k}: bf16 differs between forms"
+
+
+def test_long_k_split_of_the_128x192_tile(ctx):
+    """Two six-wave groups on the 128 x 192 tile, chosen from 32 K stages on:
+    ragged M, N and K; int32 equal to the one-group tile's everywhere and to
+    the oracle on sampled rows (the full oracle product is too slow here)."""
+    M, N, K = 3900, 1120, 4192
+    cfg = T.gemm_config_choose(M, N, K)
+    assert T.gemm_config_info(cfg) == (128, 192, 2)
+    one = next(i for i in range(T.gemm_config_info()) if T.gemm_config_info(i) == (128, 192, 1))
+    xq = S.gen_int8((M, K), seed=11)
+    wq = S.gen_int8((N, K), seed=12, lo=-128, hi=127)
+    sa, sw = S.gen_scales(M, seed=13), S.gen_scales(N, seed=14)
+    dx, dw = torch.from_numpy(xq).to(DEV), torch.from_numpy(wq).to(DEV)
+    dsa, dsw = torch.from_numpy(sa).to(DEV), torch.from_numpy(sw).to(DEV)
+    rows = np.array([0, 1, 127, 128, 1919, 3840, 3899])
+    try:
+        for k in (0, 5):
+            ys, accs = ctx.masked_qgemm(dx, dsa, dw, dsw, k, want_acc=True)
+            ctx.set_option(T.OPT_GEMM_CONFIG, one)
+            y1, acc1 = ctx.masked_qgemm(dx, dsa, dw, dsw, k, want_acc=True)
+            ctx.set_option(T.OPT_GEMM_CONFIG, -1)
+            torch.cuda.synchronize()
+            assert torch.equal(accs, acc1), f"k {k}: split and one-group sums differ"
+            assert torch.equal(ys, y1), f"k {k}: split and one-group bf16 differ"
+            ref = O.masked_gemm_i32(xq[rows], wq, k)
+            np.testing.assert_array_equal(accs.cpu().numpy()[rows], ref, err_msg=f"k {k}")
+    finally:
+        ctx.set_option(T.OPT_GEMM_CONFIG, -1)

@@ -243,7 +243,8 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
 
 struct CfgDesc {
   int bm, bn, wm, wn, rb, nst, kw;
-  float rate;   // relative throughput per CU on its tiles (fitted to MI355X sweeps)
+  float rate;       // relative throughput per CU on its tiles (fitted to MI355X sweeps)
+  int min_stages;   // K-split variants: taken only from this many K stages on
 };
 // Twelve or sixteen waves per large tile (wave tiles of 64 x 64 or 64 x 96):
 // on MI355X these beat the same tiles with eight waves of 128 x 64 by 3-15%
@@ -252,17 +253,21 @@ struct CfgDesc {
 // into whole rounds of tiles over the CUs.  Rates are the median per-tile
 // rates of a graph-replayed sweep of every tile over 22 DiT shapes (the
 // chooser then loses 1.1% on average, at most 6%, to the best tile).
-// index, BM, BN, WM, WN, stage row bytes, LDS stages, K groups, rate
-#define TABIT_I8_CONFIGS(X)                \
-  X(0, 256, 256, 4, 4, 128, 2, 1, 1.00f)    \
-  X(1, 256, 288, 4, 3, 128, 2, 1, 1.04f)    \
-  X(2, 256, 192, 4, 3, 128, 2, 1, 0.88f)    \
-  X(3, 128, 128, 4, 2, 128, 2, 1, 0.65f)    \
-  X(4, 128, 96, 4, 3, 128, 2, 1, 0.58f)     \
-  X(5, 64, 64, 2, 2, 128, 2, 1, 0.48f)      \
-  X(6, 128, 192, 4, 3, 128, 2, 1, 0.71f)    \
-  X(7, 64, 64, 2, 2, 128, 2, 3, 0.48f)
-#define TABIT_DESC(I, BM, BN, WM, WN, RB, NST, KW, RATE) {BM, BN, WM, WN, RB, NST, KW, RATE},
+// The K-split 128 x 192 tile (two groups of six waves, each with its own
+// 80 KB ring) pays only on long K: PixArt MLP-down 4096 x 1152 x 4608 31.8 ->
+// 29.3 us, 4096 x 1280 x 5120 35.7 -> 33.9 us, but 11.8 -> 12.8 us at K = 1152.
+// index, BM, BN, WM, WN, stage row bytes, LDS stages, K groups, rate, min stages
+#define TABIT_I8_CONFIGS(X)                    \
+  X(0, 256, 256, 4, 4, 128, 2, 1, 1.00f, 0)     \
+  X(1, 256, 288, 4, 3, 128, 2, 1, 1.04f, 0)     \
+  X(2, 256, 192, 4, 3, 128, 2, 1, 0.88f, 0)     \
+  X(3, 128, 128, 4, 2, 128, 2, 1, 0.65f, 0)     \
+  X(4, 128, 96, 4, 3, 128, 2, 1, 0.58f, 0)      \
+  X(5, 64, 64, 2, 2, 128, 2, 1, 0.48f, 0)       \
+  X(6, 128, 192, 4, 3, 128, 2, 1, 0.71f, 0)     \
+  X(7, 64, 64, 2, 2, 128, 2, 3, 0.48f, 2)       \
+  X(8, 128, 192, 2, 3, 128, 2, 2, 0.71f, 32)
+#define TABIT_DESC(I, BM, BN, WM, WN, RB, NST, KW, RATE, MS) {BM, BN, WM, WN, RB, NST, KW, RATE, MS},
 constexpr CfgDesc kCfgs[] = {TABIT_I8_CONFIGS(TABIT_DESC)};
 #undef TABIT_DESC
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
@@ -315,7 +320,8 @@ int gemm_config_choose(int M, int N, int K, int num_cus) {
     }
   }
   // a tile whose workgroups fit in one round over the CUs gives way to its
-  // K-split variant with the fewest stages per group (then the fewest groups):
+  // K-split variant (among those whose minimum stage count K reaches) with the
+  // fewest stages per group (then the fewest groups):
   // at 64 x 1152 x 1152 three groups of 2 x 2 waves take the masked GEMM from
   // 8.5 to 6.7 us with the weights cold and the bit-plane form from 13.7 to
   // 8.9 us (k = 0), at 512 x 1152 x 4608 (144 tiles) from 22.2 to 15.2 us and at
@@ -327,7 +333,7 @@ int gemm_config_choose(int M, int N, int K, int num_cus) {
   int pick = best, pick_trips = S, pick_kw = 1;
   for (int i = 0; i < kNumCfgs; ++i) {
     const CfgDesc& c = kCfgs[i];
-    if (c.kw == 1 || c.bm != b.bm || c.bn != b.bn || c.rb != b.rb) continue;
+    if (c.kw == 1 || c.bm != b.bm || c.bn != b.bn || c.rb != b.rb || S < c.min_stages) continue;
     const int trips = (S + c.kw - 1) / c.kw;
     if (trips < pick_trips || (trips == pick_trips && c.kw < pick_kw)) {
       pick = i;
@@ -342,7 +348,7 @@ hipError_t launch_gemm_i8(int cfg, bool bitserial, const int8_t* xq, const float
                           const int8_t* wq, const float* sw, int M, int N, int K, int kbits,
                           uint16_t* y, int32_t* acc, hipStream_t stream, hipEvent_t ev0,
                           hipEvent_t ev1, const uint8_t* gate) {
-#define TABIT_CASE(I, BM, BN, WM, WN, RB, NST, KW, RATE)                                        \
+#define TABIT_CASE(I, BM, BN, WM, WN, RB, NST, KW, RATE, MS)                                    \
   case I:                                                                                       \
     return launch_cfg<BM, BN, WM, WN, RB, NST, KW>(bitserial, xq, sa, wq, sw, M, N, K, kbits, y, \
                                                    acc, stream, ev0, ev1, gate);
