@@ -253,9 +253,10 @@ struct CfgDesc {
 // into whole rounds of tiles over the CUs.  Rates are the median per-tile
 // rates of a graph-replayed sweep of every tile over 22 DiT shapes (the
 // chooser then loses 1.1% on average, at most 6%, to the best tile).
-// The K-split 128 x 192 tile (two groups of six waves, each with its own
-// 80 KB ring) pays only on long K: PixArt MLP-down 4096 x 1152 x 4608 31.8 ->
-// 29.3 us, 4096 x 1280 x 5120 35.7 -> 33.9 us, but 11.8 -> 12.8 us at K = 1152.
+// The K-split 128 x 192 and 128 x 96 tiles (two groups of six waves, each
+// with its own ring) pay only on long K: PixArt MLP-down 4096 x 1152 x 4608
+// 31.8 -> 29.3 us, 4096 x 1280 x 5120 35.7 -> 33.9 us, SANA MLP-down
+// 1024 x 2240 x 5600 42.7 -> 38.9 us, but 11.8 -> 12.8 us at K = 1152.
 // index, BM, BN, WM, WN, stage row bytes, LDS stages, K groups, rate, min stages
 #define TABIT_I8_CONFIGS(X)                    \
   X(0, 256, 256, 4, 4, 128, 2, 1, 1.00f, 0)     \
@@ -266,7 +267,8 @@ struct CfgDesc {
   X(5, 64, 64, 2, 2, 128, 2, 1, 0.48f, 0)       \
   X(6, 128, 192, 4, 3, 128, 2, 1, 0.71f, 0)     \
   X(7, 64, 64, 2, 2, 128, 2, 3, 0.48f, 2)       \
-  X(8, 128, 192, 2, 3, 128, 2, 2, 0.71f, 32)
+  X(8, 128, 192, 2, 3, 128, 2, 2, 0.71f, 32)   \
+  X(9, 128, 96, 2, 3, 128, 2, 2, 0.58f, 32)
 #define TABIT_DESC(I, BM, BN, WM, WN, RB, NST, KW, RATE, MS) {BM, BN, WM, WN, RB, NST, KW, RATE, MS},
 constexpr CfgDesc kCfgs[] = {TABIT_I8_CONFIGS(TABIT_DESC)};
 #undef TABIT_DESC
