@@ -267,3 +267,52 @@ def test_mfma_peak_probe(ctx):
     print(f"mfma probe: INT8 {i8 / 1e12:.0f} TOPS, FP4 {fp4 / 1e12:.0f} TFLOP/s", flush=True)
     assert 2.5e15 < i8 < 6.0e15
     assert 5.0e15 < fp4 < 12.1e15
+
+
+@pytest.mark.parametrize("path", [T.PATH_MASKED, T.PATH_BITSERIAL])
+def test_autotune_keeps_a_valid_tile_and_the_result(ctx, path):
+    """Autotune times every tile (K-split ones included) for one ragged shape,
+    returns a valid index, and later calls for that shape, which run the tuned
+    tile, still match the oracle bit for bit."""
+    M, N, K = 200, 416, 1120
+    xq, wq, sa, sw = _gemm_inputs(M, N, K, seed=77)
+    dx, dw = torch.from_numpy(xq).to(DEV), torch.from_numpy(wq).to(DEV)
+    dsa, dsw = torch.from_numpy(sa).to(DEV), torch.from_numpy(sw).to(DEV)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    c = T.Context()
+    try:
+        best = c.autotune_gemm(path, dx, dsa, dw, dsw, M, N, K, 3, y, reps=2)
+        assert 0 <= best < T.gemm_config_info()
+        fn = c.masked_qgemm if path == T.PATH_MASKED else c.qgemm_bitserial
+        for k in (0, 3, 7):
+            _, acc = fn(dx, dsa, dw, dsw, k, want_acc=True)
+            ref = O.masked_gemm_i32(xq, wq, k) if path == T.PATH_MASKED else O.bitplane_gemm_i32(xq, wq, k)
+            np.testing.assert_array_equal(_np(acc), ref, err_msg=f"tuned cfg {best} k {k}")
+    finally:
+        c.close()
+
+
+def test_autotune_mxfp4(ctx):
+    """The MXFP4 path's autotune returns a valid tile and the tuned GEMM keeps
+    the exact fp64 product's bound."""
+    M, N, K = 130, 192, 512
+    rng = np.random.default_rng(9)
+    xf = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    wf = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    xe = rng.integers(120, 132, size=(M, K // 32), dtype=np.uint8)
+    we = rng.integers(120, 132, size=(N, K // 32), dtype=np.uint8)
+    d = [torch.from_numpy(a).to(DEV) for a in (xf, xe, wf, we)]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    c = T.Context()
+    try:
+        best = c.autotune_gemm(T.PATH_MXFP4_GEMM, d[0], d[1], d[2], d[3], M, N, K, 0, y, reps=2)
+        assert 0 <= best < T.mxfp4_config_info()
+        yt, acc = c.mxfp4_qgemm(d[0], d[1], d[2], d[3], 1 / 32, want_acc=True)
+        ctx.set_option(T.OPT_MXFP4_CONFIG, best)
+        _, acc_forced = ctx.mxfp4_qgemm(d[0], d[1], d[2], d[3], 1 / 32, want_acc=True)
+        torch.cuda.synchronize()
+        assert torch.equal(acc, acc_forced), "the tuned call did not run the tuned tile"
+        _check_mx(_bf16_np(yt), _np(acc).astype(np.float64), xf, xe, wf, we, 1 / 32)
+    finally:
+        ctx.set_option(T.OPT_MXFP4_CONFIG, -1)
+        c.close()
