@@ -161,3 +161,50 @@ def test_pixart_schedule_step_every_layer(ctx, step):
         y_ref = O.dequant(O.masked_gemm_i32(xq_ref, wq_ref, k), sa_ref, sw_ref)
         yy = keep[li][1].float().cpu().numpy().astype(np.float64)[rows]
         assert np.all(np.abs(yy - y_ref) <= 1e-2 * np.abs(y_ref) + 1e-30), f"layer {li} k {k}"
+
+
+# ------------------------------------------------------------ the library's size limits
+MAX_M, MAX_K = 65535, 32768      # an operand of 2^31 - 32768 bytes: the largest the ABI accepts
+MAX_ROWS = np.array([0, 1, 30001, MAX_M - 2, MAX_M - 1])
+
+
+def _device_int8(shape, seed):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    return torch.randint(-127, 128, shape, dtype=torch.int8, device=DEV, generator=g)
+
+
+def test_gemm_at_the_size_limits(ctx):
+    """K = 32768 (256 stages) and an activation operand just under 2 GiB, so
+    every byte offset the kernels form is near the top of the 31-bit range:
+    sampled rows (the last ones included) bit-exact against the oracle."""
+    N = 96
+    xq = _device_int8((MAX_M, MAX_K), seed=21)
+    wq_h = S.gen_int8((N, MAX_K), seed=22, lo=-128, hi=127)
+    wq = torch.from_numpy(wq_h).to(DEV)
+    sa = torch.from_numpy(S.gen_scales(MAX_M, seed=23)).to(DEV)
+    sw = torch.from_numpy(S.gen_scales(N, seed=24)).to(DEV)
+    x_rows = xq[torch.from_numpy(MAX_ROWS).to(DEV)].cpu().numpy()
+    for k in (0, 5):
+        _, acc = ctx.masked_qgemm(xq, sa, wq, sw, k, want_y=False, want_acc=True)
+        got = acc[torch.from_numpy(MAX_ROWS).to(DEV)].cpu().numpy()
+        np.testing.assert_array_equal(got, O.masked_gemm_i32(x_rows, wq_h, k), err_msg=f"k {k}")
+        del acc
+    del xq
+    torch.cuda.empty_cache()
+
+
+def test_int8_quantizer_at_the_size_limits(ctx):
+    """Rows of 32768 elements (two 16-element chunks per thread) over an input
+    of 2^31 - 32768 elements: codes and scales of sampled rows bit-exact."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(31)
+    x = torch.randn((MAX_M, MAX_K), dtype=torch.float32, device=DEV, generator=g).to(torch.bfloat16)
+    q, s = ctx.hadamard_quant_act(x, 32)
+    rows = torch.from_numpy(MAX_ROWS).to(DEV)
+    x_bits = x[rows].view(torch.int16).cpu().numpy().view(np.uint16)
+    q_ref, s_ref = O.quantize_act_int8(x_bits, 32)
+    np.testing.assert_array_equal(q[rows].cpu().numpy(), q_ref)
+    np.testing.assert_array_equal(s[rows].cpu().numpy(), s_ref)
+    del x, q, s
+    torch.cuda.empty_cache()
