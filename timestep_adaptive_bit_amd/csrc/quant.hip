@@ -143,14 +143,18 @@ enum QuantMode { Q_PLAIN = 0, Q_HQDM = 1, Q_GELU = 2 };
 // the codes are rotated back by the same block FWHT -- integers up to 127 b in
 // magnitude, exact in fp32 -- and written as two int8 planes Z = 128 hi + lo
 // (hi = floor(Z / 128) to q, lo in [0, 127] to q_lo).
-template <int B, int NT, int CPT, int MODE>
+// ONE: the workgroup holds a single row; its absmax is then a butterfly over
+// each wave's lanes and one value per wave in LDS (one barrier), instead of
+// LDS atomics per row (max is exact in any order, so the codes are the same).
+template <int B, int NT, int CPT, int MODE, bool ONE>
 __global__ void __launch_bounds__(NT)
 quant_int8_kernel(const uint16_t* __restrict__ x, int M, int K, int rows_per_wg, float scale_div,
                   int8_t* __restrict__ q, float* __restrict__ scale, const uint8_t* __restrict__ gate,
                   int8_t* __restrict__ q_lo) {
   if (gate != nullptr && *gate != 0) return;   // device-selected format is not INT8
-  __shared__ unsigned s_amax[NT * CPT / 2];
-  __shared__ float s_r[NT * CPT / 2];
+  __shared__ unsigned s_amax[ONE ? 1 : NT * CPT / 2];
+  __shared__ float s_r[ONE ? 1 : NT * CPT / 2];
+  __shared__ float s_wmax[NT / 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int r0 = blockIdx.x * rows_per_wg;
@@ -175,36 +179,57 @@ quant_int8_kernel(const uint16_t* __restrict__ x, int M, int K, int rows_per_wg,
       for (int e = 0; e < 16; ++e) v[i][e] = 0.0f;
     }
   }
-  for (int t = tid; t < rows; t += NT) s_amax[t] = 0u;
+  if constexpr (!ONE)
+    for (int t = tid; t < rows; t += NT) s_amax[t] = 0u;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) fwht_chunk<B>(v[i], lane);
-  __syncthreads();
 
+  float r_one = 0.0f;   // 127 / absmax of the row (ONE)
+  if constexpr (ONE) {
+    float m = 0.0f;
 #pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int c = i * NT + tid;
-    if (c < nchunks) {
-      float m = 0.0f;
+    for (int i = 0; i < CPT; ++i)
+      if (i * NT + tid < nchunks)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(v[i][e]));
-      // non-negative floats order like their bit patterns
-      atomicMax(&s_amax[row_of(c, cr, inv_cr)], __float_as_uint(m));
+        for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(v[i][e]));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if (lane == 0) s_wmax[tid >> 6] = m;
+    __syncthreads();
+    float a = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) a = fmaxf(a, s_wmax[w]);
+    r_one = a > 0.0f ? 127.0f / a : 0.0f;
+    if (tid == 0) scale[r0] = (a / 127.0f) / scale_div;
+  } else {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = i * NT + tid;
+      if (c < nchunks) {
+        float m = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(v[i][e]));
+        // non-negative floats order like their bit patterns
+        atomicMax(&s_amax[row_of(c, cr, inv_cr)], __float_as_uint(m));
+      }
     }
+    __syncthreads();
+    for (int t = tid; t < rows; t += NT) {
+      const float a = __uint_as_float(s_amax[t]);
+      s_r[t] = a > 0.0f ? 127.0f / a : 0.0f;
+      scale[r0 + t] = (a / 127.0f) / scale_div;
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  for (int t = tid; t < rows; t += NT) {
-    const float a = __uint_as_float(s_amax[t]);
-    s_r[t] = a > 0.0f ? 127.0f / a : 0.0f;
-    scale[r0 + t] = (a / 127.0f) / scale_div;
-  }
-  __syncthreads();
+  auto r_of = [&](int c) { return ONE ? r_one : s_r[row_of(c, cr, inv_cr)]; };
 
   if constexpr (MODE != Q_HQDM) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = i * NT + tid;
       if (c < nchunks) {
-        const float r = s_r[row_of(c, cr, inv_cr)];
+        const float r = r_of(c);
         uint4 o;
         o.x = pack4_i8(v[i][0], v[i][1], v[i][2], v[i][3], r);
         o.y = pack4_i8(v[i][4], v[i][5], v[i][6], v[i][7], r);
@@ -217,7 +242,7 @@ quant_int8_kernel(const uint16_t* __restrict__ x, int M, int K, int rows_per_wg,
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = i * NT + tid;
-      const float r = c < nchunks ? s_r[row_of(c, cr, inv_cr)] : 0.0f;
+      const float r = c < nchunks ? r_of(c) : 0.0f;
 #pragma unroll
       for (int e = 0; e < 16; ++e)   // the codes, as pack4_i8 forms them
         v[i][e] = __builtin_amdgcn_fmed3f(rintf(v[i][e] * r), -127.0f, 127.0f);
@@ -314,14 +339,15 @@ template <int B, int MODE>
 hipError_t dispatch_int8(int nt, int cpt, int grid, int rows, const uint16_t* x, int M, int K,
                          float scale_div, int8_t* q, float* scale, hipStream_t s, const uint8_t* gate,
                          int8_t* q_lo) {
-#define TABIT_Q(NT_, CPT_)                                                                      \
-  if (nt == NT_ && cpt == CPT_) {                                                               \
-    quant_int8_kernel<B, NT_, CPT_, MODE><<<grid, NT_, 0, s>>>(x, M, K, rows, scale_div, q, scale, \
-                                                             gate, q_lo);                       \
+#define TABIT_Q(NT_, CPT_, ONE_)                                                                \
+  if (nt == NT_ && cpt == CPT_ && (rows == 1) == ONE_) {                                        \
+    quant_int8_kernel<B, NT_, CPT_, MODE, ONE_><<<grid, NT_, 0, s>>>(x, M, K, rows, scale_div, q, \
+                                                                   scale, gate, q_lo);          \
     return hipGetLastError();                                                                   \
   }
-  TABIT_Q(192, 1) TABIT_Q(256, 1) TABIT_Q(320, 1) TABIT_Q(384, 1) TABIT_Q(448, 1) TABIT_Q(512, 1)
-  TABIT_Q(1024, 1) TABIT_Q(1024, 2)
+  TABIT_Q(256, 1, false) TABIT_Q(64, 1, true) TABIT_Q(128, 1, true) TABIT_Q(192, 1, true) TABIT_Q(256, 1, true) TABIT_Q(320, 1, true)
+  TABIT_Q(384, 1, true) TABIT_Q(448, 1, true) TABIT_Q(512, 1, true) TABIT_Q(1024, 1, true)
+  TABIT_Q(1024, 2, true)
 #undef TABIT_Q
   return hipErrorInvalidValue;
 }
@@ -330,12 +356,15 @@ hipError_t dispatch_int8(int nt, int cpt, int grid, int rows, const uint16_t* x,
 
 namespace {
 
-// Workgroup shape: one 16-element chunk per thread.  Rows of up to 128
-// chunks share 256-thread workgroups; a longer row gets a workgroup of its own
-// sized to the next multiple of 64 threads up to 512 (320 threads for the 288
-// chunks of K = 4608: 13.1 vs 14.0 us at 4096 rows with 512, 13.6 with two
-// rows in 576), then 1024 threads, then two chunks per thread past 1024
-// chunks.  Small workgroups with few registers outnumber the resident slots,
+// Workgroup shape: one 16-element chunk per thread.  A row of up to 512
+// chunks gets a workgroup of its own sized to the next multiple of 64 threads
+// when that keeps at least as large a share of the threads busy as packing
+// whole rows into 256 threads, else it shares a 256-thread workgroup (rows of
+// up to 32 chunks always do): 320 threads for the 288 chunks of K = 4608
+// (13.1 vs 14.0 us at 4096 rows with 512, 13.6 with two rows in 576), 128 for
+// the 120 of K = 1920 (17.9 vs 19.0 us at 17776 rows), three rows in 256 for
+// the 72 of K = 1152 (4.5 vs 4.8 us hot with one row in 128).  Longer rows
+// take 1024 threads, two chunks per thread past 1024 chunks.  Small workgroups with few registers outnumber the resident slots,
 // so reads of late workgroups overlap the stores of early ones; on MI355X this
 // beat fuller multi-row, multi-chunk shapes by 7-32% at the workloads' sizes.
 template <int MODE>
@@ -345,8 +374,11 @@ hipError_t launch_int8_rows(const uint16_t* x, int M, int K, int had_block, floa
   if (M <= 0) return hipSuccess;
   const int cr = K / 16;
   int nt = 1024, cpt = 1;
-  if (cr <= 128) nt = 256;
-  else if (cr <= 512) nt = (cr + 63) / 64 * 64;
+  if (cr <= 512) {
+    const int one = (cr + 63) / 64 * 64;   // a workgroup of its own, next multiple of 64 threads
+    const int multi = 256 / cr * cr;       // chunks of whole rows a 256-thread workgroup holds
+    nt = cr > 32 && cr * 256 >= multi * one ? one : 256;   // the shape that keeps more threads busy
+  }
   else if (cr > 1024) cpt = 2;
   const int rows = (nt * cpt) / cr;
   const int grid = (M + rows - 1) / rows;
