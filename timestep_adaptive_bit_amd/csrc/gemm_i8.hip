@@ -253,6 +253,10 @@ struct CfgDesc {
 // into whole rounds of tiles over the CUs.  Rates are the median per-tile
 // rates of a graph-replayed sweep of every tile over 22 DiT shapes (the
 // chooser then loses 1.1% on average, at most 6%, to the best tile).
+// The 64 x 64 tile splits K over three or four groups of 2 x 2 waves, whichever
+// walks fewer stages per group (then fewer groups): four groups take
+// 64 x 1152 x 4608 from 13.4 to 12.4 us and 16 x 2240 x 5600 from 21.7 to
+// 20.5 us; at K = 1152 both walk three stages and three groups are faster.
 // The K-split 128 x 192 and 128 x 96 tiles (two groups of six waves, each
 // with its own ring) pay only on long K: PixArt MLP-down 4096 x 1152 x 4608
 // 31.8 -> 29.3 us, 4096 x 1280 x 5120 35.7 -> 33.9 us, SANA MLP-down
@@ -268,7 +272,8 @@ struct CfgDesc {
   X(6, 128, 192, 4, 3, 128, 2, 1, 0.71f, 0)     \
   X(7, 64, 64, 2, 2, 128, 2, 3, 0.48f, 2)       \
   X(8, 128, 192, 2, 3, 128, 2, 2, 0.71f, 32)   \
-  X(9, 128, 96, 2, 3, 128, 2, 2, 0.58f, 32)
+  X(9, 128, 96, 2, 3, 128, 2, 2, 0.58f, 32)    \
+  X(10, 64, 64, 2, 2, 128, 2, 4, 0.48f, 2)
 #define TABIT_DESC(I, BM, BN, WM, WN, RB, NST, KW, RATE, MS) {BM, BN, WM, WN, RB, NST, KW, RATE, MS},
 constexpr CfgDesc kCfgs[] = {TABIT_I8_CONFIGS(TABIT_DESC)};
 #undef TABIT_DESC
