@@ -706,7 +706,7 @@ def main() -> int:
 
     if args.gpus != 1:
         print("bench.py measures one GPU: the linear shards by tokens with no communication, "
-              "so this build runs and reports the single-GPU share only (--gpus 1).",
+              "so it runs and reports one GPU's share only (--gpus 1).",
               file=sys.stderr)
         return 2
 
