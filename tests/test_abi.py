@@ -281,3 +281,30 @@ def test_product_path_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(T._lib, "_lib", None)
     with pytest.raises(RuntimeError, match="no fallback"):
         T._lib.load()
+
+
+def test_int8_chooser_split_rules():
+    """Over seeded random shapes: a K-split tile only when the same tile's
+    workgroups fit in one round over the CUs, two-group tiles only from 32 K
+    stages on, and whenever a split is taken it walks fewer stages per group
+    than the unsplit tile would."""
+    import random
+    rng = random.Random(5)
+    n = T.gemm_config_info()
+    info = [T.gemm_config_info(i) for i in range(n)]
+    for _ in range(2000):
+        M = rng.choice([1, 3, 17, 64, 100, 256, 512, 768, 1024, 2048, 4096, 17776]) + rng.randrange(0, 64)
+        N = 32 * rng.randrange(1, 320)
+        K = 32 * rng.randrange(1, 1024)
+        cus = rng.choice([0, 80, 256, 304])
+        c = T.gemm_config_choose(M, N, K, cus)
+        assert 0 <= c < n
+        bm, bn, kg = info[c]
+        if kg == 1:
+            continue
+        tiles = -(-M // bm) * -(-N // bn)
+        assert tiles <= (cus or 256), (M, N, K, cus, info[c])
+        stages = -(-K // 128)
+        assert -(-stages // kg) < stages or stages == 1, (M, N, K, info[c])
+        if kg == 2:
+            assert stages >= 32, (M, N, K, info[c])
