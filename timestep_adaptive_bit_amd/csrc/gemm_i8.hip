@@ -27,8 +27,9 @@
 // epilogue scales in fp32, rounds to bf16 and transposes through LDS for
 // 16-byte row-contiguous stores.
 //
-// K split inside the workgroup (KW > 1), for few-token shapes whose tiles
-// leave most CUs idle: KW groups of WM x WN waves each walk a contiguous range
+// K split inside the workgroup (KW > 1), for shapes whose tiles fit in one
+// round over the CUs (a few tokens, or a long K): KW groups of WM x WN waves
+// each walk a contiguous range
 // of the K stages through their own LDS ring; groups 1..KW-1 then hand their
 // int32 accumulators to group 0 through LDS (integer sums: the result equals
 // the unsplit one bit for bit) and group 0 runs the epilogue.  Every wave
