@@ -9,6 +9,10 @@ Plain, slow, obviously-correct numpy.  Integer work is exact (int64).  The
 quantizers take their rounding decisions in IEEE fp32, the precision the
 kernels decide codes in, so codes and scales are expected bit-exact; the
 dequantized outputs are evaluated in fp64 and compared within a tolerance.
+Two next-row steps are plain definitions evaluated more precisely than any
+kernel does: the GELU folded into the down projection's quantizer (fp64,
+rounded once to bf16) and DMPQ's relative L1 change (exactly rounded sums);
+the tests compare the kernels with them within stated error bounds.
 
 Sources (web pages; section names as the pages print them):
   * TASQ: Temporal-Adaptive Bit Sparsification Quantization for Diffusion
@@ -30,6 +34,7 @@ silent or garbled are stated inline.
 """
 from __future__ import annotations
 
+import math
 from typing import Dict, Tuple
 
 import numpy as np
@@ -441,50 +446,50 @@ def mxfp4_gemm(x_fp4, x_e8m0, w_fp4, w_e8m0, out_scale: float) -> np.ndarray:
 # GELU into the quantizer that feeds the down projection removes a full read and
 # write of the 4H-wide activation.  The pages fix no activation function; the
 # DiT convention is GELU in its tanh form,
-#   gelu(x) = 0.5 x (1 + tanh(u)),  u = sqrt(2/pi) (x + 0.044715 x^3),
-# and since 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)) exactly, gelu(x) = x / (1 + exp(-2u)).
-# It is evaluated in fp32 from IEEE add, multiply, divide and exact power-of-two
-# scaling only (no library exp/tanh), so that a kernel taking the same steps in
-# the same order gives the same bits.  The result is rounded to bf16 -- the
-# precision an unfused pipeline would store it in -- and then quantized exactly
-# as quantize_act_int8 does.
+#   gelu(x) = 0.5 x (1 + tanh(u)),  u = sqrt(2/pi) (x + 0.044715 x^3).
+# Reading: the down projection's input is that value rounded to bf16 (round to
+# nearest, ties to even) -- what an unfused pipeline stores -- and values of
+# magnitude below 2^-100 are taken as zero (GELU is that small only for
+# x < -9.2, where no fp32 evaluation keeps relative accuracy).  It is then
+# quantized exactly as quantize_act_int8 does.
 #
-# exp(v), |v| <= 40: n = rint(v log2 e); r = (v - n ln2_hi) - n ln2_lo (Cody-Waite
-# reduction, ln2_hi exact in 16 bits); e^r by its Taylor polynomial to degree 6
-# in Horner form (|r| <= ln2/2: truncation below 1.2e-7 relative); result = e^r * 2^n.
-_F = np.float32
-_LOG2E = _F(1.44269504088896341)
-_LN2_HI = _F(0.693145751953125)          # 16 significant bits: n * _LN2_HI is exact
-_LN2_LO = _F(1.42860682030941723e-06)
-_EXP_C = [_F(1.0 / 720.0), _F(1.0 / 120.0), _F(1.0 / 24.0), _F(1.0 / 6.0), _F(0.5), _F(1.0),
-          _F(1.0)]
-_GELU_C = _F(0.7978845608028654)          # sqrt(2 / pi)
-_GELU_A = _F(0.044715)
+# The oracle evaluates the definition in fp64 through the identity
+# 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)), which avoids the cancellation of
+# 1 + tanh(u) for negative u (exp is numpy's fp64 exp, a library primitive),
+# and rounds the fp64 value to bf16 directly (no intermediate fp32 rounding).
+
+GELU_FLUSH = 2.0 ** -100
 
 
-def exp_f32(v: np.ndarray) -> np.ndarray:
-    """exp in fp32 by the steps above (|v| <= 40; the caller clamps)."""
-    v = np.asarray(v, dtype=np.float32)
-    n = np.rint(v * _LOG2E).astype(np.float32)
-    r = (v - n * _LN2_HI) - n * _LN2_LO
-    p = _EXP_C[0]
-    for c in _EXP_C[1:]:
-        p = p * r + c
-    return np.ldexp(p, n.astype(np.int32)).astype(np.float32)
+def gelu_tanh_f64(x: np.ndarray) -> np.ndarray:
+    """GELU (tanh form) of x in fp64, x / (1 + exp(-2u)); |result| < 2^-100 -> 0."""
+    x = np.asarray(x, dtype=np.float64)
+    u = np.sqrt(2.0 / np.pi) * (x + 0.044715 * x ** 3)
+    with np.errstate(over="ignore"):
+        g = x / (1.0 + np.exp(-2.0 * u))      # exp overflow -> inf -> g = -0 (flushed anyway)
+    return np.where(np.abs(g) < GELU_FLUSH, 0.0, g)
 
 
-def gelu_tanh_f32(x: np.ndarray) -> np.ndarray:
-    """GELU (tanh form) in fp32: x / (1 + exp(-2u)), with 2u clamped to [-40, 40]."""
-    x = np.asarray(x, dtype=np.float32)
-    u = _GELU_C * (x + _GELU_A * (x * x * x))
-    z = np.minimum(np.maximum(_F(2.0) * u, _F(-40.0)), _F(40.0))
-    return (x / (_F(1.0) + exp_f32(-z))).astype(np.float32)
+def f64_to_bf16_bits(v: np.ndarray) -> np.ndarray:
+    """fp64 -> bf16 bit patterns, round to nearest, ties to even, in one rounding.
+
+    bf16 keeps 8 significant bits and fp32's exponent range: a normal value
+    m 2^e (m in [0.5, 1)) becomes rint(m 2^8) 2^(e-8); below 2^-126 the step
+    is the subnormal quantum 2^-133.  Finite inputs within the bf16 range.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)
+    normal = np.abs(v) >= 2.0 ** -126
+    q = np.where(normal, np.ldexp(np.rint(np.ldexp(m, 8)), e - 8),
+                 np.ldexp(np.rint(np.ldexp(v, 133)), -133))
+    q = np.where(q == 0, np.copysign(0.0, v), q)
+    return (q.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
 def quantize_act_gelu_int8(x_bits: np.ndarray, had_block: int) -> Tuple[np.ndarray, np.ndarray]:
     """Quantizer of the down projection's input: bf16(gelu(x)), then quantize_act_int8."""
-    g = gelu_tanh_f32(bf16_to_f32(np.asarray(x_bits)))
-    return quantize_act_int8(f32_to_bf16_bits(g), had_block)
+    g = gelu_tanh_f64(bf16_to_f32(np.asarray(x_bits)))
+    return quantize_act_int8(f64_to_bf16_bits(g), had_block)
 
 
 # --------------------------------------------------------------------------
@@ -530,47 +535,25 @@ def hqdm_gemm_i64(z: np.ndarray, w_q: np.ndarray, k: int) -> np.ndarray:
 # threshold, so a linear predictor compared with a threshold is a threshold
 # theta_l on Gamma per layer: INT8 when Gamma > theta_l, else 4-bit.
 #
-# Gamma = sum |out - in| / sum |in| over the block's hidden states.  Its
-# summation order is part of this library's contract so that the device
-# decision can be reproduced exactly: terms in fp64 (|in| exact, out - in one
-# fp64 subtraction), each 16-element chunk summed left to right, the chunk
-# sums of a row by a pairwise tree, the row sums by a pairwise tree (trees
-# padded with zeros to a power of two; x + 0 = x, so padding changes nothing).
-
-
-def _pairwise_tree(v: np.ndarray) -> np.ndarray:
-    """Pairwise sums along the last axis: ((v0 + v1) + (v2 + v3)) + ..., zero-padded."""
-    v = np.asarray(v, dtype=np.float64)
-    n = v.shape[-1]
-    p = 1
-    while p < n:
-        p *= 2
-    if p != n:
-        pad = np.zeros(v.shape[:-1] + (p - n,), dtype=np.float64)
-        v = np.concatenate([v, pad], axis=-1)
-    while v.shape[-1] > 1:
-        v = v[..., 0::2] + v[..., 1::2]
-    return v[..., 0]
+# Gamma = sum |out - in| / sum |in| over the block's hidden states.  The page
+# fixes no summation order; the oracle takes each sum exactly rounded
+# (math.fsum of the fp64 terms), then one fp64 division.
 
 
 def dmpq_gamma(x_in_bits: np.ndarray, x_out_bits: np.ndarray) -> Tuple[float, float, float]:
-    """(Gamma, sum |out - in|, sum |in|) of one block, in the order stated above.
+    """(Gamma, sum |out - in|, sum |in|) of one block.
 
+    Terms are fp64: |in| exactly, |out - in| by one fp64 subtraction (exact for
+    bf16 operands whose binary exponents differ by less than 45).  Each sum is
+    the correctly rounded value of the exact sum of its terms (math.fsum).
     Gamma = 0 when both sums are 0, +inf when only sum |in| is 0.
     """
     a = bf16_to_f32(np.asarray(x_in_bits)).astype(np.float64)
     b = bf16_to_f32(np.asarray(x_out_bits)).astype(np.float64)
-    if a.shape != b.shape or a.ndim != 2 or a.shape[1] % 16:
-        raise ValueError("in and out must be [M][H] with H % 16 == 0")
-    m_rows, h = a.shape
-    d = np.abs(b - a).reshape(m_rows, h // 16, 16)
-    s = np.abs(a).reshape(m_rows, h // 16, 16)
-    dc, sc = d[:, :, 0].copy(), s[:, :, 0].copy()
-    for e in range(1, 16):                  # left to right inside a chunk
-        dc = dc + d[:, :, e]
-        sc = sc + s[:, :, e]
-    num = float(_pairwise_tree(_pairwise_tree(dc)))
-    den = float(_pairwise_tree(_pairwise_tree(sc)))
+    if a.shape != b.shape:
+        raise ValueError("in and out must have the same shape")
+    num = math.fsum(np.abs(b - a).ravel().tolist())
+    den = math.fsum(np.abs(a).ravel().tolist())
     if den == 0.0:
         return (0.0 if num == 0.0 else float("inf")), num, den
     return num / den, num, den

@@ -1,7 +1,10 @@
 """GPU parity of the DMPQ selector and the device-gated linear.
 
-Bars: Gamma bit-exact (fp64, the fixed summation order) and the per-layer
-INT8 / 4-bit decisions exact against the oracle; the gated linear identical
+Bars: Gamma within the reordering bound of the oracle's exactly rounded sums
+(any fp64 summation order of n non-negative terms is within (n - 1) 2^-53 of
+the exact sum, relative; Gamma within twice that plus the roundings of the
+division), and the per-layer INT8 / 4-bit decisions exact wherever Gamma is
+farther than that bound from the threshold; the gated linear identical
 (bit for bit) to the host-scheduled linear of the same format, and within the
 parity bars of test_gpu_parity against the oracle; a captured step (selector +
 gated linears) follows the data-dependent decision on every replay.
@@ -35,20 +38,49 @@ def _block_io(M, H, seed, delta):
     return x.to(torch.bfloat16), y.to(torch.bfloat16)
 
 
+def gamma_rel_bound(n_terms: int) -> float:
+    """Relative bound on |Gamma_device - Gamma_oracle|: each sum of n non-negative fp64
+    terms, in any order, within (n - 1) 2^-53 / (1 - (n - 1) 2^-53) of the exact sum; the
+    oracle's sums are exactly rounded (2^-53 each); one division on each side."""
+    u = 2.0 ** -53
+    g = (n_terms - 1) * u / (1 - (n_terms - 1) * u)
+    return 2 * g + 6 * u
+
+
+def check_gamma_and_decisions(gamma_dev, fmt_dev, g_ref, thetas, n_terms):
+    bound = gamma_rel_bound(n_terms)
+    if np.isinf(g_ref) or g_ref == 0.0:
+        assert gamma_dev == g_ref
+    else:
+        assert abs(gamma_dev - g_ref) <= bound * g_ref, (gamma_dev, g_ref, bound)
+    want = O.dmpq_select(g_ref, thetas)
+    decided = 0
+    for l, th in enumerate(np.asarray(thetas, np.float32).astype(np.float64)):
+        if np.isinf(g_ref) or abs(g_ref - th) > bound * g_ref:
+            assert fmt_dev[l] == want[l], (l, th, g_ref)
+            decided += 1
+        else:
+            assert fmt_dev[l] in (0, 1)
+    return decided
+
+
 @pytest.mark.parametrize("M,H", [(1, 16), (7, 48), (300, 1920), (2500, 5600), (33, 20480),
                                  (17776, 1920)])
-def test_dmpq_gamma_bit_exact(ctx, M, H):
+def test_dmpq_gamma_within_reordering_bound(ctx, M, H):
     x, y = _block_io(M, H, seed=M + H, delta=0.3)
     g_ref, _, _ = O.dmpq_gamma(S.bf16_bits(x), S.bf16_bits(y))
-    thetas = np.array([g_ref * 0.5, np.float32(g_ref), g_ref * 2.0], np.float32)
+    # thresholds below, at (the fp32 nearest) and above Gamma, and one ulp-scale offsets
+    thetas = np.array([g_ref * 0.5, np.float32(g_ref), g_ref * 2.0,
+                       np.nextafter(np.float32(g_ref), np.float32(0)),
+                       np.nextafter(np.float32(g_ref), np.float32(np.inf))], np.float32)
     th = torch.from_numpy(thetas).to(DEV)
-    fmt = torch.full((3,), 7, dtype=torch.uint8, device=DEV)
+    fmt = torch.full((len(thetas),), 7, dtype=torch.uint8, device=DEV)
     gamma = torch.zeros(1, dtype=torch.float64, device=DEV)
     print(f"dmpq {M}x{H}", flush=True)
     ctx.dmpq_select(x.to(DEV), y.to(DEV), th, fmt, gamma)
     torch.cuda.synchronize()
-    assert gamma.item() == g_ref                           # bit-exact fp64
-    assert fmt.cpu().numpy().tolist() == O.dmpq_select(g_ref, thetas).tolist()
+    decided = check_gamma_and_decisions(gamma.item(), fmt.cpu().numpy(), g_ref, thetas, M * H)
+    assert decided >= 2
 
 
 def test_dmpq_closed_forms_on_device(ctx):
@@ -150,7 +182,8 @@ def test_captured_step_follows_device_decision(ctx):
             torch.cuda.synchronize()
             a, o, lin = inputs[c]
             g_ref, _, _ = O.dmpq_gamma(S.bf16_bits(a), S.bf16_bits(o))
-            assert gamma.item() == g_ref
+            assert check_gamma_and_decisions(gamma.item(), fmt.cpu().numpy(), g_ref,
+                                             [0.2, 0.2], M * H) == 2
             f_ref = O.dmpq_select(g_ref, [0.2, 0.2])
             assert f_ref.tolist() == [want, want]
             assert fmt.cpu().numpy().tolist() == f_ref.tolist(), f"replay {rep} case {c}"

@@ -7,6 +7,7 @@ special case of one (the torch bf16 cast).
 """
 import math
 import os
+from decimal import Decimal, getcontext
 from fractions import Fraction
 
 import numpy as np
@@ -299,28 +300,133 @@ def test_plane_gemm_brute_force(k):
 
 
 # ---------------------------------------------------------------- fused GELU quantizer
-def test_exp_f32_within_two_ulp():
-    v = np.linspace(-40, 40, 400001).astype(np.float32)
-    e = O.exp_f32(v).astype(np.float64)
-    ref = np.array([math.exp(float(t)) for t in v[::97]])
-    assert np.all(np.abs(e[::97] - ref) <= 2.0 ** -22 * ref)        # within 2 ulp (relative)
-    assert O.exp_f32(np.float32(0.0)) == 1.0
+def _pi_decimal():
+    """pi to ~70 digits by Machin's formula, pi = 16 atan(1/5) - 4 atan(1/239)."""
+    getcontext().prec = 80
+
+    def atan_inv(n):
+        x = Decimal(1) / n
+        s = t = x
+        k = 1
+        while True:
+            t = -t * x * x
+            k += 2
+            if abs(t / k) < Decimal(10) ** -75:
+                return s
+            s += t / k
+    return 16 * atan_inv(5) - 4 * atan_inv(239)
 
 
-def test_gelu_tanh_against_closed_form():
-    x = np.linspace(-12, 12, 200001).astype(np.float32)
-    g = O.gelu_tanh_f32(x).astype(np.float64)
-    xd = x.astype(np.float64)
-    ref = 0.5 * xd * (1 + np.tanh(math.sqrt(2 / math.pi) * (xd + 0.044715 * xd ** 3)))
-    assert np.all(np.abs(g - ref) <= 1e-6 + 1e-4 * np.abs(ref))
-    assert O.gelu_tanh_f32(np.float32(0.0)) == 0.0
-    big = np.array([10.0, 37.5, 1e4], np.float32)
-    assert np.array_equal(O.gelu_tanh_f32(big), big)                  # tanh = 1 exactly
-    assert np.all(O.gelu_tanh_f32(-big) <= 0) and np.all(O.gelu_tanh_f32(-big) > -1e-6)
+def _gelu_decimal_fn():
+    """The closed form 0.5 x (1 + tanh(u)) in 80-digit decimal arithmetic."""
+    getcontext().prec = 80
+    c = (Decimal(2) / _pi_decimal()).sqrt()
+    a = Decimal("0.044715")
+
+    def g(x):
+        x = Decimal(float(x))
+        e = (2 * c * (x + a * x * x * x)).exp()
+        return Decimal("0.5") * x * (1 + (e - 1) / (e + 1))
+    return g
+
+
+def _bf16_of_decimal(g: Decimal) -> int:
+    """bf16 bits of g rounded to nearest (ties to the even code), decided exactly
+    by comparing g with the neighbours of the fp64 estimate."""
+    b = int(O.f64_to_bf16_bits(np.array([float(g)]))[0])
+    best = None
+    for d in (-1, 0, 1):
+        bb = (b & 0x8000) | min(0x7F7F, max(0, (b & 0x7FFF) + d))
+        v = Decimal(float(O.bf16_to_f32(np.array([bb], np.uint16))[0]))
+        key = (abs(v - g), bb & 1)
+        if best is None or key < best[0]:
+            best = (key, bb)
+    return best[1]
+
+
+def test_pi_and_constants():
+    assert str(_pi_decimal())[:32] == "3.141592653589793238462643383279"
+    assert abs(float((Decimal(2) / _pi_decimal()).sqrt()) - math.sqrt(2 / math.pi)) < 1e-16
+
+
+def test_gelu_bf16_every_input_against_decimal_closed_form():
+    """For every finite bf16 input with |x| <= 16 (33538 values), the oracle's bf16
+    GELU equals the exactly rounded bf16 of the literal closed form 0.5 x (1 + tanh(u))
+    evaluated with 80 decimal digits; values below 2^-100 are 0.  Beyond |x| = 16
+    GELU(x) is x for x > 0 (1 - sigma < e^-400) and below the flush for x < 0."""
+    gd = _gelu_decimal_fn()
+    bits = np.arange(65536, dtype=np.uint16)
+    with np.errstate(invalid="ignore"):
+        x = O.bf16_to_f32(bits).astype(np.float64)
+    fin = np.isfinite(x)
+    sel = fin & (np.abs(x) <= 16)
+    got = O.f64_to_bf16_bits(O.gelu_tanh_f64(x[sel]))
+    flush = Decimal(2) ** -100
+    checked = 0
+    for xi, gi in zip(x[sel], got):
+        g = gd(xi)
+        if abs(g) < flush * Decimal("0.999999"):
+            assert gi in (0x0000, 0x8000), xi
+        elif abs(g) > flush * Decimal("1.000001"):
+            assert int(gi) == _bf16_of_decimal(g), (xi, g, hex(gi))
+            checked += 1
+    assert checked > 25000                       # the rest lie below the flush (tiny |x| too)
+    big = x[fin & (x > 16)]
+    assert np.array_equal(O.f64_to_bf16_bits(O.gelu_tanh_f64(big)), O.f64_to_bf16_bits(big))
+    neg = x[fin & (x < -16)]
+    assert np.all(O.gelu_tanh_f64(neg) == 0.0)
+
+
+def test_gelu_odd_part_identity():
+    """gelu(x) - gelu(-x) = x exactly for the tanh form (tanh is odd); in fp64 within
+    a few ulp of the larger term, on both sides of the origin and deep in the tails."""
+    x = np.concatenate([np.linspace(-8, 8, 4001), [1e-25, 3e-5, 0.7, 5.0]])
+    d = O.gelu_tanh_f64(x) - O.gelu_tanh_f64(-x)
+    assert np.all(np.abs(d - x) <= 8 * 2.0 ** -53 * np.maximum(np.abs(x), 1e-300) + 1e-300)
+    assert O.gelu_tanh_f64(np.array([0.0]))[0] == 0.0
+
+
+def test_f64_to_bf16_single_rounding():
+    """Direct fp64 -> bf16 rounding: a value just above a bf16 midpoint whose fp32
+    rounding lands exactly on the midpoint must round up (fp32 first would round to
+    even, down); exact ties go to the even code; the subnormal quantum is 2^-133."""
+    mid = 1.0 + 2.0 ** -8                         # midpoint between 1 and 1 + 2^-7
+    above = mid + 2.0 ** -40                      # fp32(above) == mid
+    assert np.float32(above) == np.float32(mid)
+    assert O.f64_to_bf16_bits(np.array([above]))[0] == 0x3F81
+    assert O.f64_to_bf16_bits(np.array([mid]))[0] == 0x3F80          # tie -> even
+    assert O.f64_to_bf16_bits(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 0x3F82   # tie -> even (up)
+    assert O.f64_to_bf16_bits(np.array([-2.0 ** -133]))[0] == 0x8001
+    assert O.f64_to_bf16_bits(np.array([2.0 ** -134]))[0] == 0x0000   # tie -> even (zero)
+    assert O.f64_to_bf16_bits(np.array([1.5 * 2.0 ** -133]))[0] == 0x0002
+    # agrees with torch's fp32 -> bf16 cast on fp32-exact values
+    v = torch.randn(4096, generator=torch.Generator().manual_seed(9))
+    assert np.array_equal(O.f64_to_bf16_bits(v.double().numpy()), S.bf16_bits(v.to(torch.bfloat16)))
+
+
+def test_gelu_golden_values_and_row():
+    """Hand-worked GELU values (negative inputs and the flush) and a quantized row."""
+    for line in _lines("gelu_bf16_worked.txt"):
+        tag, rest = line.split(" ", 1)
+        parts = [p.strip() for p in rest.split("|")]
+        if tag == "value":
+            x, gv, bits = float(parts[0]), float(parts[1]), int(parts[2], 16)
+            g = O.gelu_tanh_f64(np.array([x]))[0]
+            assert g == 0.0 if bits == 0 else abs(g - gv) <= 1e-12 * abs(gv), x
+            assert O.f64_to_bf16_bits(np.array([g]))[0] & 0x7FFF == bits & 0x7FFF
+            assert bits == 0 or O.f64_to_bf16_bits(np.array([g]))[0] == bits
+        else:
+            b = int(parts[0])
+            lead = [int(c) for c in parts[1].split()]
+            num, den = (int(t) for t in parts[2].split())
+    xs = [-0.5, -1, -1.5, -2, -3, -4, -6, -9, -9.5, 0.5, 2] + [0.0] * 21
+    q, s = O.quantize_act_gelu_int8(_bits([xs]), b)
+    assert q[0, :11].tolist() == lead and not q[0, 11:].any()
+    assert s[0] == _fp32_round(Fraction(num, den))
 
 
 def test_gelu_quant_is_identity_quant_on_large_inputs():
-    """For x >= 10 the fused GELU is exactly the identity, so the codes equal the plain quantizer's."""
+    """For x >= 10 the GELU is the identity in bf16, so the codes equal the plain quantizer's."""
     x = (torch.rand(7, 128, generator=torch.Generator().manual_seed(3)) * 50 + 10).to(torch.bfloat16)
     xb = S.bf16_bits(x)
     for b in (0, 64):
@@ -410,10 +516,27 @@ def test_dmpq_gamma_exact_on_small_integers():
     assert g == float(Fraction(exact_num, exact_den))                # one correctly rounded division
 
 
-def test_dmpq_summation_order_golden():
-    """Chunk sums 2^53, 1, 1, 2 (zero-padded chunks): the pairwise tree gives
-    (2^53 + 1) + (1 + 2) = 2^53 + 4 (2^53 + 1 rounds to 2^53; 2^53 + 3 ties to
-    the even 2^53 + 4), a left-to-right sum over the row would give 2^53 + 2."""
+def test_dmpq_gamma_against_exact_rationals_wide_range():
+    """Sums equal the correctly rounded exact rational sums (Fraction arithmetic on the
+    bf16 values) over rows spanning 2^-40 .. 2^40; Gamma is within 2 ulp of the exact
+    quotient."""
+    g = torch.Generator().manual_seed(11)
+    x = torch.randn(24, 64, generator=g) * torch.exp2(torch.randint(-40, 41, (24, 1), generator=g).float())
+    y = x + 0.3 * torch.randn(24, 64, generator=g) * x.abs()
+    xb, yb = S.bf16_bits(x.to(torch.bfloat16)), S.bf16_bits(y.to(torch.bfloat16))
+    gam, num, den = O.dmpq_gamma(xb, yb)
+    a = [Fraction(float(v)) for v in O.bf16_to_f32(xb).ravel()]
+    o = [Fraction(float(v)) for v in O.bf16_to_f32(yb).ravel()]
+    en = sum(abs(q - p) for p, q in zip(a, o))
+    ed = sum(abs(p) for p in a)
+    assert num == float(en) and den == float(ed)                     # float(Fraction) rounds correctly
+    exact = en / ed
+    assert abs(Fraction(gam) - exact) <= 2 * Fraction(2) ** -52 * exact
+
+
+def test_dmpq_sum_is_exactly_rounded_golden():
+    """Terms 2^53, 1, 1, 2: the exact sum 2^53 + 4 is representable and is the result;
+    a left-to-right fp64 sum gives 2^53 + 2 (2^53 + 1 rounds to 2^53 twice)."""
     row = np.zeros((1, 64), np.float32)
     row[0, 0], row[0, 16], row[0, 32], row[0, 48] = 2.0 ** 53, 1.0, 1.0, 2.0
     _, num, den = O.dmpq_gamma(_bf(np.zeros_like(row)), _bf(row))
@@ -421,11 +544,7 @@ def test_dmpq_summation_order_golden():
     seq = 0.0
     for v in row.ravel().astype(np.float64):
         seq += v
-    assert seq == 2.0 ** 53 + 2                                      # the order matters here
-    # rows combine by the same tree: rows 2^53, 1, 1, 2
-    rows = np.zeros((4, 16), np.float32)
-    rows[:, 0] = [2.0 ** 53, 1.0, 1.0, 2.0]
-    assert O.dmpq_gamma(_bf(np.zeros_like(rows)), _bf(rows))[1] == 2.0 ** 53 + 4
+    assert seq == 2.0 ** 53 + 2
 
 
 def test_dmpq_select_threshold_rule():
