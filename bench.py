@@ -331,45 +331,104 @@ class Hip:
             self.lib.hipEventDestroy(h)
 
 
-def cpu_baseline(wl, rows: int):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+def _host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_layer_step(args):
+    """One oracle layer-step on a slice of token rows (a process-pool task): INT8
+    quantizer, masked GEMM and dequant (or the MXFP4 path); returns (ops, seconds)."""
+    from oracle import tabit_oracle as O
+    xb, wq, sw, wf, we, had_block, k, fmt = args
+    t0 = time.perf_counter()
+    if fmt == 0:
+        xq, sa = O.quantize_act_int8(xb, had_block)
+        acc = O.masked_gemm_i32(xq, wq, k)
+        O.dequant(acc, sa, sw)
+        n = wq.shape[0]
+    else:
+        xf, xe = O.mx_quantize_rows(O.bf16_to_f32(xb), had_block)
+        O.mxfp4_gemm(xf, xe, wf, we, 1.0 / max(had_block, 1))
+        n = wf.shape[0]
+    return 2 * xb.shape[0] * n * xb.shape[1], time.perf_counter() - t0
+
+
+def cpu_baseline(wl, rows: int) -> dict:
+    """The oracle, as it stands, on a bounded sample of the same workload, on this
+    host's cores: one layer-step per distinct linear shape (step 0's precision), on
+    `rows` token rows, first in this process (one thread: numpy's integer matmul and
+    the elementwise steps run single-threaded), then in a pool of one process per
+    available core (at most 16) over disjoint row slices of the same shapes.  Runs
+    before the GPU is touched (the pool's processes are started by fork + exec)."""
+    import multiprocessing as mp
     from oracle import tabit_oracle as O
     import tabit_synth as S
     seen = {}
     for li, layer in enumerate(wl.layers):
         key = (layer.M, layer.N, layer.K, int(wl.fmt[0, li]))
         seen.setdefault(key, (li, layer))
-    total_ops, total_s = 0, 0.0
-    parts = []
+    tasks = []      # per shape: (full activation bits, prepared weights, k, fmt)
     for (M, N, K, fmt), (li, layer) in seen.items():
-        r = min(rows, M)
-        x = S.gen_activation(M, K, seed=S.activation_seed(0, K))[:r]
-        w = S.gen_weight(N, K, seed=li)
-        xb, wb = S.bf16_bits(x), S.bf16_bits(w)
+        xb = S.bf16_bits(S.gen_activation(M, K, seed=S.activation_seed(0, K)))
+        wb = S.bf16_bits(S.gen_weight(N, K, seed=li))
+        wq = sw = wf = we = None
         if fmt == 0:
-            wq, sw = O.quantize_weights_int8(wb, wl.had_block)        # offline prep, untimed
-            t0 = time.perf_counter()
-            xq, sa = O.quantize_act_int8(xb, wl.had_block)
-            acc = O.masked_gemm_i32(xq, wq, int(wl.k_bits[0, li]))
-            O.dequant(acc, sa, sw)
-            dt = time.perf_counter() - t0
+            wq, sw = O.quantize_weights_int8(wb, wl.had_block)       # offline prep, untimed
         else:
             wf, we = O.mx_quantize_rows(O.bf16_to_f32(wb), wl.had_block)
-            t0 = time.perf_counter()
-            xf, xe = O.mx_quantize_rows(O.bf16_to_f32(xb), wl.had_block)
-            O.mxfp4_gemm(xf, xe, wf, we, 1.0 / max(wl.had_block, 1))
-            dt = time.perf_counter() - t0
-        total_ops += 2 * r * N * K
-        total_s += dt
-        parts.append(f"{r}x{N}x{K}")
+        tasks.append((xb, wq, sw, wf, we, int(wl.k_bits[0, li]), fmt))
+
+    def job(t, r0, r):
+        xb, wq, sw, wf, we, k, fmt = t
+        rows_ = (np.arange(r0, r0 + r) % xb.shape[0])
+        return (xb[rows_], wq, sw, wf, we, wl.had_block, k, fmt)
+    # one thread
+    ops1 = sec1 = 0.0
+    for t in tasks:
+        o, s = _oracle_layer_step(job(t, 0, min(rows, t[0].shape[0])))
+        ops1 += o
+        sec1 += s
+    # all cores: one process per core, each a disjoint row slice of every shape
+    n_cpu = os.cpu_count() or 1
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = n_cpu
+    procs = max(1, min(16, avail))
+    jobs = [job(t, p * rows, min(rows, t[0].shape[0])) for p in range(procs) for t in tasks]
+    with mp.get_context("spawn").Pool(procs) as pool:
+        # bounded waits: a pool whose workers cannot start would otherwise wait forever
+        pool.map_async(_oracle_layer_step, jobs[:procs]).get(timeout=300)   # start-up, untimed
+        t0 = time.perf_counter()
+        res = pool.map_async(_oracle_layer_step, jobs, chunksize=1).get(timeout=600)
+        wall = time.perf_counter() - t0
+    ops_all = sum(o for o, _ in res)
+    total_ops = 2.0 * sum(l.M * l.N * l.K for l in wl.layers) * wl.steps
+    rate_all = ops_all / wall
     return {
-        "value": total_ops / total_s / 1e12,
+        "value": round(rate_all / 1e12, 6),
         "unit": "TOPS",
-        "cores": 1,
+        "cores": procs,
         "kind": "oracle",
-        "sample": (f"{rows} token rows of step 0 of each distinct linear shape "
-                   f"({', '.join(parts)}): oracle quantizer + GEMM + dequant, "
-                   f"{total_ops / 1e9:.1f} GOP in {total_s:.1f} s; numpy, single thread"),
+        "value_1thread": round(ops1 / sec1 / 1e12, 6),
+        "cores_1thread": 1,
+        "host_cpus": n_cpu,
+        "host_cpus_available": avail,
+        "cpu_model": _host_cpu_model(),
+        "schedule_seconds_extrapolated": round(total_ops / rate_all, 1),
+        "sample": (f"oracle quantizer + masked GEMM + dequant, one layer-step per distinct linear "
+                   f"shape ({', '.join(f'{m}x{n}x{k}' for m, n, k, _ in seen)}) at step 0's "
+                   f"precision on {rows} token rows: {ops1 / 1e9:.1f} GOP in {sec1:.1f} s on one "
+                   f"thread; {procs} processes x the same on disjoint row slices: "
+                   f"{ops_all / 1e9:.1f} GOP in {wall:.1f} s wall; the whole schedule "
+                   f"({total_ops / 1e12:.1f} TOP) extrapolated from the all-core rate"),
     }
 
 
@@ -616,6 +675,68 @@ def gelu_fusion_bench(T, torch, dev) -> dict:
     return {"mode": "gelu_fusion", "shapes": out}
 
 
+def side_measurements(T, torch, dev) -> dict:
+    """Two further claims timed in the default run, beside the headline schedule:
+    (a) the bit-plane GEMM's time against effective precision on the SANA-shaped
+        MLP-down linear (1024 x 2240 x 5600) at k = 0..7, with the least-squares line
+        over the 8 - k retained planes (TASQ: cycles fall with effective precision);
+    (b) the MXFP4 GEMM on the CogVideoX-shaped MLP-up linear (17776 x 7680 x 1920):
+        FP4 flops per second against the 10.1 PFLOP/s dense MXFP4 peak.
+    HIP events around back-to-back launches on the launch stream; seeded inputs."""
+    import tabit_synth as S
+    ctx = T.Context()
+    out = {}
+
+    def timed(fn, n):
+        fn()
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+    # (a) bit-plane k sweep
+    M, N, K = 1024, 2240, 5600
+    x = S.gen_activation(M, K, seed=S.activation_seed(0, K)).to(dev)
+    w = S.gen_weight(N, K, seed=79).to(dev)
+    wts = ctx.quantize_weights(w, 0)
+    xq, sa = ctx.hadamard_quant_act(x, 0)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    us = [timed(lambda: ctx.qgemm_bitserial(xq, sa, wts["w_q"], wts["w_scale"], k, y=y), 20)
+          for k in range(8)]
+    masked = [timed(lambda: ctx.masked_qgemm(xq, sa, wts["w_q"], wts["w_scale"], k, y=y), 20)
+              for k in (0, 4, 7)]
+    planes = np.arange(8, 0, -1, dtype=np.float64)
+    ys = np.asarray(us)
+    slope, icpt = np.polyfit(planes, ys, 1)
+    r2 = 1 - ((ys - (slope * planes + icpt)) ** 2).sum() / ((ys - ys.mean()) ** 2).sum()
+    out["sana_mlp_down_bitplane_k_sweep"] = {
+        "shape": [M, N, K], "k": list(range(8)), "us": [round(v, 2) for v in us],
+        "us_per_retained_plane": round(float(slope), 3), "intercept_us": round(float(icpt), 3),
+        "r2": round(float(r2), 4), "masked_us_k0_k4_k7": [round(v, 2) for v in masked],
+        "plane_tops_k0": round(8 * 2 * M * N * K / us[0] / 1e6, 1)}
+    del x, w, wts, xq, sa, y
+    # (b) MXFP4 GEMM
+    M, N, K = 17776, 7680, 1920
+    x = S.gen_activation(M, K, seed=S.activation_seed(0, K)).to(dev)
+    w = S.gen_weight(N, K, seed=82).to(dev)
+    wts = ctx.quantize_weights(w, 32, int8=False, mx=True)
+    xf, xe = ctx.hadamard_quant_act(x, 32, T.FMT_MXFP4)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    us_mx = timed(lambda: ctx.mxfp4_qgemm(xf, xe, wts["w_fp4"], wts["w_e8m0"], 1.0 / 32, y=y), 10)
+    flops = 2 * M * N * K / us_mx / 1e6
+    out["cogvideox_mlp_up_mxfp4_gemm"] = {
+        "shape": [M, N, K], "us": round(us_mx, 2), "tflops": round(flops, 1),
+        "frac_of_10.1_pflops": round(flops / MXFP4_PEAK_TOPS, 4)}
+    del x, w, wts, xf, xe, y
+    ctx.close()
+    return out
+
+
 def gemm_tiles(T, wl, tuned, path=0):
     """Tile shape (BM, BN) each distinct GEMM shape runs with."""
     out = {}
@@ -644,8 +765,11 @@ def main() -> int:
     ap.add_argument("--path", default="masked", choices=["masked", "bitserial", "planes", "hqdm"])
     ap.add_argument("--had-block", type=int, default=None, help="override the workload's block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=2048, help="token rows per shape in the oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=512,
+                    help="token rows per shape and per process in the oracle sample")
     ap.add_argument("--no-events", action="store_true", help="skip per-GEMM event timing")
+    ap.add_argument("--no-side", action="store_true",
+                    help="skip the side measurements (SANA bit-plane k sweep, CogVideoX MXFP4 GEMM)")
     ap.add_argument("--tune", action="store_true",
                     help="autotune the GEMM tiles per shape during warm-up (default: the library's "
                          "calibrated choice, which keeps counter runs on the same kernels)")
@@ -712,16 +836,7 @@ def main() -> int:
 
     import torch
     import tabit_synth as S
-    import timestep_adaptive_bit_amd as T
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    if args.dmpq:
-        print(json.dumps(dmpq_bench(args, T, torch, dev)), flush=True)
-        return 0
-    if args.gelu_fusion:
-        print(json.dumps(gelu_fusion_bench(T, torch, dev)), flush=True)
-        return 0
     wl = S.WORKLOADS[args.workload]() if args.had_block is None else \
         S.WORKLOADS[args.workload](had_block=args.had_block)
     if args.denoise_steps:
@@ -730,6 +845,23 @@ def main() -> int:
         import dataclasses
         n = min(args.denoise_steps, wl.steps)
         wl = dataclasses.replace(wl, steps=n, k_bits=wl.k_bits[:n], fmt=wl.fmt[:n])
+    # the oracle on the host cores first: its worker processes start before this
+    # process touches the GPU
+    cpu = None
+    if not (args.no_cpu_baseline or args.dmpq or args.gelu_fusion):
+        cpu = cpu_baseline(wl, args.cpu_rows)
+        print(f"cpu_baseline done: {cpu['value']} TOPS on {cpu['cores']} processes", file=sys.stderr,
+              flush=True)
+
+    import timestep_adaptive_bit_amd as T
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.dmpq:
+        print(json.dumps(dmpq_bench(args, T, torch, dev)), flush=True)
+        return 0
+    if args.gelu_fusion:
+        print(json.dumps(gelu_fusion_bench(T, torch, dev)), flush=True)
+        return 0
     b = wl.had_block
     L, Tn = wl.num_layers, wl.steps
     ctx = T.Context()
@@ -957,6 +1089,8 @@ def main() -> int:
     if args.k_sweep:
         detail["k_sweep_us" + ("_cold" if args.cold else "")] = k_sweep(ctx, T, torch, wl, weights, xs,
                                                                         ys, b, cold=args.cold)
+    if not args.no_side:
+        detail["side"] = side_measurements(T, torch, dev)
 
     out = {
         "metric": "masked W8A8 GEMM TOPS and % of INT8 MFMA peak per denoising schedule",
@@ -981,8 +1115,8 @@ def main() -> int:
         "detail": detail,
         "gemm_tiles": gemm_tiles(T, wl, tuned, path),
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
     ctx.close()
     return 0

@@ -122,8 +122,11 @@ int tabit_quantize_weights(tabit_ctx* ctx, const uint16_t* w_bf16, int N, int K,
 int tabit_set_step_schedule(tabit_ctx* ctx, int num_steps, int num_layers,
                             const uint8_t* k_bits, const uint8_t* fmt);
 
-/* Look up (k, fmt) for one (step, layer).  ENOSCHED when no table is
- * installed or the pair is outside it.  Makes no HIP call. */
+/* Look up (k, fmt) for one (step, layer) of the installed table: the mask
+ * M_{t,l} that TASQ section 2 learns per layer and denoising stage (k truncated
+ * LSBs), and the INT8 / 4-bit choice 6Bit-Diffusion section 2A makes per layer
+ * and step.  ENOSCHED when no table is installed or the pair is outside it.
+ * Makes no HIP call. */
 int tabit_schedule_lookup(const tabit_ctx* ctx, int step, int layer, int* k_bits, int* fmt);
 
 /*
@@ -210,12 +213,13 @@ int tabit_plane_qgemm(tabit_ctx* ctx, const int8_t* x_q, const float* x_scale,
  * (GELU, tanh form -- the pages fix none; the DiT convention) is applied while
  * the down projection's input is quantized, so the 4H-wide activation is read
  * once and never written in bf16.  Per element g = bf16_rne(gelu(x)) with
- *   gelu(x) = 0.5 x (1 + tanh(u)) = x / (1 + exp(-z)),
- *   u = sqrt(2/pi) (x + 0.044715 x^3),  z = min(max(2u, -40), 40),
- *   exp(v)  = p(r) 2^n, n = rint(v log2 e), r = (v - n ln2_hi) - n ln2_lo,
- *             p the degree-6 Taylor polynomial of e^r in Horner form,
- * all in fp32 with IEEE operations in that order (constants rounded to fp32);
- * then exactly tabit_hadamard_quant_act (INT8) on g.
+ *   gelu(x) = 0.5 x (1 + tanh(u)) = x / (1 + exp(-2u)),
+ *   u = sqrt(2/pi) (x + 0.044715 x^3),
+ * magnitudes below 2^-100 taken as 0; then exactly tabit_hadamard_quant_act
+ * (INT8) on g.  GELU is evaluated in fp32 with the hardware exp2 and
+ * reciprocal: within 16 ulp (x >= 0) or (16|2u| + 24) ulp (x < 0) of the exact
+ * value (ulp = 2^-24 relative), so g is the correctly rounded bf16 of the
+ * exact GELU except where that lies within this bound of a rounding boundary.
  *   x_bf16 device [M][K] (the up projection's output); x_q int8 [M][K];
  *   x_scale fp32 [M].  Errors as tabit_hadamard_quant_act.
  */
@@ -298,11 +302,13 @@ int tabit_scheduled_linear(tabit_ctx* ctx, int step, int layer, int path,
  *   Gamma  = sum |x_out - x_in| / sum |x_in|   (0 if both sums are 0, +inf if
  *            only sum |x_in| is)
  *   fmt[l] = Gamma > theta[l] ? TABIT_FMT_INT8 : TABIT_FMT_MXFP4
- * The sums run in a fixed fp64 order (terms |x_in| and |x_out - x_in| in fp64;
- * each 16-element chunk left to right; chunk sums of a row, then row sums, by
- * pairwise trees zero-padded to a power of two), so the decision is
- * reproducible bit for bit.  Written on the device: a captured step needs no
- * host round trip; the next step's tabit_gated_linear calls read fmt.
+ * The sums run in fp64 (terms |x_in| and |x_out - x_in| in fp64) in a fixed
+ * order, so a given input always gives the same Gamma; each sum of n terms is
+ * within (n - 1) 2^-53 of the exact sum (relative), so Gamma is within twice
+ * that (plus the division's rounding) of the exact ratio, and a decision can
+ * differ from the exact one only when Gamma is that close to theta[l].
+ * Written on the device: a captured step needs no host round trip; the next
+ * step's tabit_gated_linear calls read fmt.
  *   x_in, x_out  device bf16 [M][H] (block input and output at step t-1),
  *                H % 16 == 0, 16 <= H <= 32768, 16-byte aligned.
  *   theta        device fp32 [n_layers]; fmt device uint8 [n_layers] output

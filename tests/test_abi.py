@@ -224,6 +224,13 @@ def test_scheduled_linear_validation(lib, ctx):
     assert s(layer=1) == T.EINVAL                        # MXFP4 step without the MX copy
     assert s(layer=1, wf=FAKE, we=FAKE, b=64) == T.ERANGE
     assert s(ws=MISALIGNED) == T.EALIGN
+    # every operand is checked before the quantizer is enqueued (these calls would
+    # otherwise launch it on the fake pointers)
+    assert s(wq=MISALIGNED) == T.EALIGN
+    assert s(ws_=FAKE + 2) == T.EALIGN
+    assert s(layer=1, wf=MISALIGNED, we=FAKE) == T.EALIGN
+    assert s(M=1 << 16, K=1 << 15, nbytes=1 << 40) == T.ESHAPE        # M*K = 2^31: over 2 GiB
+    assert s(path=3, N=1 << 24, K=32, nbytes=1 << 20) == T.ESHAPE     # plane-major copy over 2 GiB
     assert s(M=0) == T.OK
 
 

@@ -123,6 +123,83 @@ int gemm_i8_common(tabit_ctx* ctx, int path, const int8_t* x_q, const float* x_s
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// Every argument of one scheduled linear (step, layer) whose table entry is
+// `fmt`, checked before anything is enqueued: shapes, alignment, operand
+// sizes, and the weights the format needs.
+int check_linear(tabit_ctx* ctx, int step, int layer, int path, int fmt, const uint16_t* x_bf16,
+                 int M, int N, int K, int had_block, const int8_t* w_q, const float* w_scale,
+                 const uint8_t* w_fp4, const uint8_t* w_e8m0, const uint16_t* y_bf16) {
+  if (x_bf16 == nullptr || y_bf16 == nullptr) return fail(ctx, TABIT_EINVAL, "null pointer");
+  int st = check_k_shape(ctx, M, K, had_block);
+  if (st != TABIT_OK) return st;
+  if (N < 0 || N % 32 != 0)
+    return fail(ctx, TABIT_ESHAPE, "N must be a non-negative multiple of 32 (got %d)", N);
+  if ((size_t)M * (size_t)K > kMaxOperandBytes || (size_t)N * (size_t)K > kMaxOperandBytes)
+    return fail(ctx, TABIT_ESHAPE, "operands must stay below 2 GiB (M*K = %zu, N*K = %zu)",
+                (size_t)M * (size_t)K, (size_t)N * (size_t)K);
+  if (!aligned(x_bf16, 16) || !aligned(y_bf16, 16))
+    return fail(ctx, TABIT_EALIGN, "x_bf16 and y_bf16 must be 16-byte aligned");
+  if (fmt == TABIT_FMT_INT8) {
+    if (w_q == nullptr || w_scale == nullptr)
+      return fail(ctx, TABIT_EINVAL, "step %d layer %d is INT8 but w_q/w_scale are null", step, layer);
+    if (!aligned(w_q, 16)) return fail(ctx, TABIT_EALIGN, "w_q must be 16-byte aligned");
+    if (!aligned(w_scale, 4)) return fail(ctx, TABIT_EALIGN, "w_scale must be 4-byte aligned");
+    if (path == TABIT_PATH_PLANES && N > 0 && tabit::planes_bytes(N, K) > kMaxOperandBytes)
+      return fail(ctx, TABIT_ESHAPE, "the plane-major copy (%zu bytes) exceeds 2 GiB",
+                  tabit::planes_bytes(N, K));
+  } else {
+    if (w_fp4 == nullptr || w_e8m0 == nullptr)
+      return fail(ctx, TABIT_EINVAL, "step %d layer %d is MXFP4 but w_fp4/w_e8m0 are null", step, layer);
+    if (had_block != 0 && had_block != 32)
+      return fail(ctx, TABIT_ERANGE, "MXFP4 takes had_block 0 or 32 (got %d)", had_block);
+    if (!aligned(w_fp4, 16)) return fail(ctx, TABIT_EALIGN, "w_fp4 must be 16-byte aligned");
+  }
+  return TABIT_OK;
+}
+
+// Enqueue one validated scheduled linear: quantize x into the workspace `ws`
+// (layout of tabit_act_workspace_bytes), then the GEMM of the format and path.
+int enqueue_linear(tabit_ctx* ctx, int path, int fmt, int k, const uint16_t* x_bf16, int M, int N,
+                   int K, int had_block, const int8_t* w_q, const float* w_scale,
+                   const uint8_t* w_fp4, const uint8_t* w_e8m0, uint8_t* ws, uint16_t* y_bf16,
+                   void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int num_cus = tabit::device_num_cus();
+  const size_t mk = (size_t)M * (size_t)K;
+  hipError_t e;
+  if (fmt == TABIT_FMT_INT8) {
+    int8_t* xq = reinterpret_cast<int8_t*>(ws);
+    float* sa = reinterpret_cast<float*>(ws + 2 * align256(mk));
+    if (path == TABIT_PATH_HQDM) {
+      int8_t* xl = reinterpret_cast<int8_t*>(ws + align256(mk));
+      e = tabit::launch_quant_hqdm(x_bf16, M, K, had_block, xq, xl, sa, s);
+      if (e != hipSuccess) return hip_status(ctx, e, "HQ-DM quantizer launch");
+      return hip_status(ctx,
+                        tabit::launch_gemm_hqdm(hqdm_cfg(ctx, M, N, K, num_cus), xq, xl, sa, w_q,
+                                                w_scale, M, N, K, k, y_bf16, nullptr, s),
+                        "HQ-DM GEMM launch");
+    }
+    e = tabit::launch_quant_int8(x_bf16, M, K, had_block, 1.0f, xq, sa, s);
+    if (e != hipSuccess) return hip_status(ctx, e, "quantizer launch");
+    return hip_status(ctx,
+                      launch_int8_family(ctx, path, xq, sa, w_q, w_scale, M, N, K, k, y_bf16,
+                                         nullptr, s, num_cus),
+                      "GEMM launch");
+  }
+  uint8_t* xf = ws;
+  uint8_t* xe = ws + align256(mk / 2);
+  e = tabit::launch_quant_mx(x_bf16, M, K, had_block, xf, xe, s);
+  if (e != hipSuccess) return hip_status(ctx, e, "MX quantizer launch");
+  int cfg = ctx->force_mx_cfg;
+  if (cfg < 0) cfg = ctx->tuned_cfg(2, M, N, K);
+  if (cfg < 0) cfg = tabit::mx_config_choose(M, N, K, num_cus);
+  return hip_status(ctx,
+                    tabit::launch_gemm_mxfp4(cfg, xf, xe, w_fp4, w_e8m0, M, N, K,
+                                             1.0f / (float)(had_block > 0 ? had_block : 1), y_bf16,
+                                             nullptr, s),
+                    "MXFP4 GEMM launch");
+}
+
 }  // namespace
 
 namespace tabit {
@@ -410,47 +487,17 @@ int tabit_scheduled_linear(tabit_ctx* ctx, int step, int layer, int path, const 
   int k = 0, fmt = 0;
   int st = tabit_schedule_lookup(ctx, step, layer, &k, &fmt);
   if (st != TABIT_OK) return st;
-  if (x_bf16 == nullptr || y_bf16 == nullptr || act_ws == nullptr)
-    return fail(ctx, TABIT_EINVAL, "null pointer");
-  st = check_k_shape(ctx, M, K, had_block);
-  if (st != TABIT_OK) return st;
-  if (N < 0 || N % 32 != 0)
-    return fail(ctx, TABIT_ESHAPE, "N must be a non-negative multiple of 32 (got %d)", N);
+  if (act_ws == nullptr) return fail(ctx, TABIT_EINVAL, "null pointer");
   if (!aligned(act_ws, 16)) return fail(ctx, TABIT_EALIGN, "act_ws must be 16-byte aligned");
   if (act_ws_bytes < tabit_act_workspace_bytes(M, K))
     return fail(ctx, TABIT_ESHAPE, "act_ws holds %zu bytes, %zu needed", act_ws_bytes,
                 tabit_act_workspace_bytes(M, K));
-  if (fmt == TABIT_FMT_INT8) {
-    if (w_q == nullptr || w_scale == nullptr)
-      return fail(ctx, TABIT_EINVAL, "step %d layer %d is INT8 but w_q/w_scale are null", step, layer);
-  } else {
-    if (w_fp4 == nullptr || w_e8m0 == nullptr)
-      return fail(ctx, TABIT_EINVAL, "step %d layer %d is MXFP4 but w_fp4/w_e8m0 are null", step, layer);
-    if (had_block != 0 && had_block != 32)
-      return fail(ctx, TABIT_ERANGE, "MXFP4 takes had_block 0 or 32 (got %d)", had_block);
-  }
-  if (M == 0 || N == 0) return TABIT_OK;
-  uint8_t* ws = static_cast<uint8_t*>(act_ws);
-  const size_t mk = (size_t)M * (size_t)K;
-  if (fmt == TABIT_FMT_INT8) {
-    int8_t* xq = reinterpret_cast<int8_t*>(ws);
-    float* sa = reinterpret_cast<float*>(ws + 2 * align256(mk));
-    if (path == TABIT_PATH_HQDM) {
-      int8_t* xl = reinterpret_cast<int8_t*>(ws + align256(mk));
-      st = tabit_hqdm_quant_act(ctx, x_bf16, M, K, had_block, xq, xl, sa, stream);
-      if (st != TABIT_OK) return st;
-      return tabit_hqdm_qgemm(ctx, xq, xl, sa, w_q, w_scale, M, N, K, k, y_bf16, nullptr, stream);
-    }
-    st = tabit_hadamard_quant_act(ctx, x_bf16, M, K, had_block, TABIT_FMT_INT8, xq, sa, stream);
-    if (st != TABIT_OK) return st;
-    return gemm_i8_common(ctx, path, xq, sa, w_q, w_scale, M, N, K, k, y_bf16, nullptr, stream);
-  }
-  uint8_t* xf = ws;
-  uint8_t* xe = ws + align256(mk / 2);
-  st = tabit_hadamard_quant_act(ctx, x_bf16, M, K, had_block, TABIT_FMT_MXFP4, xf, xe, stream);
+  st = check_linear(ctx, step, layer, path, fmt, x_bf16, M, N, K, had_block, w_q, w_scale, w_fp4,
+                    w_e8m0, y_bf16);
   if (st != TABIT_OK) return st;
-  return tabit_mxfp4_qgemm(ctx, xf, xe, w_fp4, w_e8m0, M, N, K,
-                           1.0f / (float)(had_block > 0 ? had_block : 1), y_bf16, nullptr, stream);
+  if (M == 0 || N == 0) return TABIT_OK;
+  return enqueue_linear(ctx, path, fmt, k, x_bf16, M, N, K, had_block, w_q, w_scale, w_fp4, w_e8m0,
+                        static_cast<uint8_t*>(act_ws), y_bf16, stream);
 }
 
 size_t tabit_dmpq_workspace_bytes(int M) { return tabit::dmpq_workspace_bytes(M); }

@@ -9,12 +9,12 @@
 // The decision is written to a device-resident format table, so a captured
 // step needs no host round trip: the gated launches of the next step read it.
 //
-// Summation order (part of the contract, so the decision is reproducible bit
-// for bit): terms in fp64 (|in| exact, out - in one fp64 subtraction); each
-// 16-element chunk summed left to right; a row's chunk sums by a pairwise tree;
-// the row sums by a pairwise tree; trees zero-padded to a power of two.  A
-// butterfly (lane XOR 1, 2, 4, ...) over a power-of-two group computes exactly
-// that pairwise tree in every lane, because fp addition is commutative.
+// Summation (the page fixes no order; any order of the n non-negative fp64
+// terms is within (n - 1) 2^-53 of the exact sum, relative): terms in fp64
+// (|in| exact, out - in one fp64 subtraction); each 16-element chunk summed
+// left to right; a row's chunk sums by a butterfly over the lanes and a tree
+// over the waves; the row sums by a tree of 1024-leaf groups.  The order is
+// fixed, so the same input gives the same Gamma on every run.
 #include "tabit_internal.h"
 
 namespace tabit {

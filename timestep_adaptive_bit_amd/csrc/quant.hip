@@ -108,31 +108,20 @@ __device__ __forceinline__ int row_of(int c, int cr, float inv_cr) {
   return r;
 }
 
-// exp(v), |v| <= 40, in fp32 from exact operations only: n = rint(v log2 e),
-// r = (v - n ln2_hi) - n ln2_lo (Cody-Waite; n ln2_hi is exact), e^r by its
-// degree-6 Taylor polynomial in Horner form, times 2^n.  The constants are the
-// fp32 values nearest to log2 e, ln 2 (split 16 + 24 bits) and 1/j!.
-__device__ __forceinline__ float exp_f32(float v) {
-  const float n = rintf(v * 0x1.715476p+0f);
-  const float r = (v - n * 0x1.62e4p-1f) - n * 0x1.7f7d1cp-20f;
-  float p = 0x1.6c16c2p-10f;
-  p = p * r + 0x1.111112p-7f;
-  p = p * r + 0x1.555556p-5f;
-  p = p * r + 0x1.555556p-3f;
-  p = p * r + 0.5f;
-  p = p * r + 1.0f;
-  p = p * r + 1.0f;
-  return ldexpf(p, (int)n);
-}
-
-// GELU, tanh form: 0.5 x (1 + tanh(u)) = x / (1 + exp(-2u)) with
-// u = sqrt(2/pi) (x + 0.044715 x^3) and 2u clamped to [-40, 40].  Every
-// operation is an IEEE add, multiply, correctly rounded divide or exact
-// scaling, in a fixed order (no contraction).
+// GELU, tanh form: 0.5 x (1 + tanh(u)) = x sigma(z) with z = 2u =
+// x (k1 + k3 x^2), k1 = 2 sqrt(2/pi), k3 = 0.044715 k1, sigma(z) = 1/(1 + e^-z).
+// sigma comes from t = e^-|z| (in (0, 1], never overflows): 1/(1 + t) for
+// z >= 0, t/(1 + t) for z < 0, with the hardware exp2 and reciprocal
+// (v_exp_f32, v_rcp_f32).  In fp32 the result is within 16 ulp (z >= 0) or
+// (16|z| + 24) ulp (z < 0) of the exact GELU, ulp = 2^-24 relative; results
+// of magnitude below 2^-100 become 0 (the deep negative tail, where no fp32
+// evaluation keeps relative accuracy).  +-inf in z gives 0 or x, never NaN.
 __device__ __forceinline__ float gelu_tanh(float x) {
-  const float u = 0x1.988454p-1f * (x + 0x1.6e4e26p-5f * (x * x * x));
-  const float z = fminf(fmaxf(2.0f * u, -40.0f), 40.0f);
-  return x / (1.0f + exp_f32(-z));
+  const float z = x * (0x1.988454p+0f + 0x1.2444f2p-4f * (x * x));
+  const float t = __builtin_amdgcn_exp2f(-fabsf(z) * 0x1.715476p+0f);
+  const float s = __builtin_amdgcn_rcpf(1.0f + t);
+  const float g = x * (z >= 0.0f ? s : t * s);
+  return fabsf(g) < 0x1p-100f ? 0.0f : g;
 }
 
 enum QuantMode { Q_PLAIN = 0, Q_HQDM = 1, Q_GELU = 2 };
