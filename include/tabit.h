@@ -294,6 +294,32 @@ int tabit_scheduled_linear(tabit_ctx* ctx, int step, int layer, int path,
                            void* act_ws, size_t act_ws_bytes, uint16_t* y_bf16, void* stream);
 
 /*
+ * tabit_scheduled_linear for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same lookup, quantizer and GEMM, with the quantized
+ * activations in a static device array owned by the library instead of a
+ * caller workspace.  Nothing is allocated, freed or memset.  The array holds
+ * tabit_noalloc_scratch_bytes() = 64 MiB per GPU (loaded with the library's
+ * code object, kept until the process ends); a call needs
+ *   INT8 (masked, bit-plane, plane-major): align256(M*K) + align256(4*M),
+ *   INT8 on TABIT_PATH_HQDM:               2*align256(M*K) + align256(4*M),
+ *   MXFP4:                                 align256(M*K/2) + align256(M*K/32)
+ * bytes (align256 rounds up to a multiple of 256) and is rejected with
+ * TABIT_ESHAPE, before anything is enqueued, when that exceeds the array.
+ * Every call on one GPU shares that GPU's array: calls whose work overlaps on
+ * one GPU (different streams, or other threads) race and must be ordered by
+ * the caller.  Every byte a call reads from the array is written earlier in
+ * the same call.  Arguments and errors otherwise as tabit_scheduled_linear;
+ * the results equal its results bit for bit.
+ */
+size_t tabit_noalloc_scratch_bytes(void);
+int tabit_scheduled_linear_noalloc(tabit_ctx* ctx, int step, int layer, int path,
+                                   const uint16_t* x_bf16, int M, int N, int K, int had_block,
+                                   const int8_t* w_q, const float* w_scale,
+                                   const uint8_t* w_fp4, const uint8_t* w_e8m0,
+                                   uint16_t* y_bf16, void* stream);
+
+/*
  * DMPQ online format selection (6Bit-Diffusion section 2A): the relative L1
  * input-output change of a transformer block at step t-1 predicts, linearly,
  * the quantization sensitivity of its linear layers at step t; unstable

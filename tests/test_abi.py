@@ -234,6 +234,25 @@ def test_scheduled_linear_validation(lib, ctx):
     assert s(M=0) == T.OK
 
 
+def test_noalloc_validation(lib, ctx):
+    """The no-alloc linear validates like the workspace one and rejects activations
+    larger than its static scratch, all before any HIP call."""
+    def s(step=0, layer=0, path=0, M=8, N=32, K=64, b=0, wq=FAKE, ws_=FAKE, wf=None, we=None):
+        return lib.tabit_scheduled_linear_noalloc(ctx.handle, step, layer, path, FAKE, M, N, K, b,
+                                                  wq, ws_, wf, we, FAKE, None)
+    assert lib.tabit_noalloc_scratch_bytes() == 64 << 20
+    assert s() == T.ENOSCHED
+    ctx.set_step_schedule(np.array([[0, 3]]), np.array([[0, 1]]))
+    assert s(path=5) == T.EINVAL
+    assert s(wq=None) == T.EINVAL
+    assert s(wq=MISALIGNED) == T.EALIGN
+    assert s(layer=1) == T.EINVAL
+    assert s(M=8192, K=8192) == T.ESHAPE                              # 64 MiB of codes + scales
+    assert s(M=4096, K=8192, path=4) == T.ESHAPE                      # HQ-DM: two planes
+    assert s(layer=1, wf=FAKE, we=FAKE, b=32, M=16384, K=8192) == T.ESHAPE   # MX: 64 + 4 MiB
+    assert s(M=0) == T.OK
+
+
 def test_workspace_bytes():
     for M, K in ((1, 32), (64, 1152), (17776, 7680)):
         n = T.act_workspace_bytes(M, K)

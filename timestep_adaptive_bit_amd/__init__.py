@@ -9,7 +9,7 @@ from ._lib import (  # noqa: F401
     Context, Layer, TabitError, load, version, act_workspace_bytes, gemm_config_info,
     gemm_config_choose, mxfp4_config_info, plane_config_info, plane_config_choose,
     weight_planes_bytes,
-    dmpq_workspace_bytes,
+    dmpq_workspace_bytes, noalloc_scratch_bytes,
     header_functions, LIB_PATH,
     OK, EINVAL, ESHAPE, EALIGN, ERANGE, ENOSCHED, EHIP, ENOMEM,
     FMT_INT8, FMT_MXFP4, PATH_MASKED, PATH_BITSERIAL, PATH_PLANES, PATH_HQDM, PATH_MXFP4_GEMM,
@@ -21,5 +21,5 @@ __all__ = [
     "gemm_config_choose", "header_functions", "FMT_INT8", "FMT_MXFP4", "PATH_MASKED",
     "PATH_BITSERIAL", "PATH_PLANES", "OPT_GEMM_CONFIG", "OPT_MXFP4_CONFIG", "OPT_PLANE_CONFIG",
     "plane_config_info", "plane_config_choose", "weight_planes_bytes", "dmpq_workspace_bytes",
-    "PATH_HQDM", "OPT_HQDM_CONFIG", "hqdm_config_info",
+    "PATH_HQDM", "OPT_HQDM_CONFIG", "hqdm_config_info", "noalloc_scratch_bytes",
 ]

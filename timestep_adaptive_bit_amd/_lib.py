@@ -50,6 +50,11 @@ _SIGNATURES = {
     "tabit_scheduled_linear": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_int,
                                         _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p,
                                         _c_void_p, _c_void_p, _c_size_t, _c_void_p, _c_void_p]),
+    "tabit_noalloc_scratch_bytes": (_c_size_t, []),
+    "tabit_scheduled_linear_noalloc": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p,
+                                                _c_int, _c_int, _c_int, _c_int, _c_void_p,
+                                                _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                                _c_void_p]),
     "tabit_run_schedule": (_c_int, [_c_void_p, _c_int, _c_int, _c_void_p, _c_int, _c_void_p,
                                     _c_int, _c_int, _c_void_p, _c_size_t, _c_void_p, _c_void_p]),
     "tabit_autotune_gemm": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -151,6 +156,10 @@ def _dev(t: torch.Tensor, dtype, name: str, shape=None) -> None:
 
 def version() -> str:
     return load().tabit_version().decode()
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(load().tabit_noalloc_scratch_bytes())
 
 
 def act_workspace_bytes(M: int, K: int) -> int:
@@ -477,6 +486,22 @@ class Context:
             _ptr(wq), _ptr(weights.get("w_scale")), _ptr(wf), _ptr(weights.get("w_e8m0")),
             act_ws.data_ptr(), act_ws.numel() * act_ws.element_size(), y.data_ptr(),
             _stream(x.device))
+        self._check(st)
+        return y
+
+    def scheduled_linear_noalloc(self, step: int, layer: int, x: torch.Tensor, weights: dict,
+                                 had_block: int, y: torch.Tensor, path: int = PATH_MASKED):
+        """As scheduled_linear, with the library's static device scratch instead of a
+        workspace; `y` [M, N] bf16 must be given (nothing is allocated here)."""
+        _dev(x, torch.bfloat16, "x")
+        M, K = x.shape
+        N = y.shape[1]
+        _dev(y, torch.bfloat16, "y", (M, N))
+        wq = weights.get("w_planes") if path == PATH_PLANES else weights.get("w_q")
+        st = self._lib.tabit_scheduled_linear_noalloc(
+            self._h, step, layer, path, x.data_ptr(), M, N, K, had_block,
+            _ptr(wq), _ptr(weights.get("w_scale")), _ptr(weights.get("w_fp4")),
+            _ptr(weights.get("w_e8m0")), y.data_ptr(), _stream(x.device))
         self._check(st)
         return y
 

@@ -7,6 +7,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <new>
 
 #include "tabit_internal.h"
@@ -123,6 +124,15 @@ int gemm_i8_common(tabit_ctx* ctx, int path, const int8_t* x_q, const float* x_s
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// Bytes the compact workspace layout of one scheduled linear needs: the codes,
+// then the scales (INT8; two code planes first on the HQ-DM path), or the FP4
+// codes, then the E8M0 bytes (MXFP4), each section 256-byte aligned.
+size_t compact_ws_bytes(int path, int fmt, int M, int K) {
+  const size_t mk = (size_t)M * (size_t)K;
+  if (fmt == TABIT_FMT_MXFP4) return align256(mk / 2) + align256(mk / 32);
+  return (path == TABIT_PATH_HQDM ? 2 : 1) * align256(mk) + align256((size_t)M * 4);
+}
+
 // Every argument of one scheduled linear (step, layer) whose table entry is
 // `fmt`, checked before anything is enqueued: shapes, alignment, operand
 // sizes, and the weights the format needs.
@@ -162,14 +172,16 @@ int check_linear(tabit_ctx* ctx, int step, int layer, int path, int fmt, const u
 int enqueue_linear(tabit_ctx* ctx, int path, int fmt, int k, const uint16_t* x_bf16, int M, int N,
                    int K, int had_block, const int8_t* w_q, const float* w_scale,
                    const uint8_t* w_fp4, const uint8_t* w_e8m0, uint8_t* ws, uint16_t* y_bf16,
-                   void* stream) {
+                   void* stream, bool compact = false) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int num_cus = tabit::device_num_cus();
   const size_t mk = (size_t)M * (size_t)K;
   hipError_t e;
   if (fmt == TABIT_FMT_INT8) {
     int8_t* xq = reinterpret_cast<int8_t*>(ws);
-    float* sa = reinterpret_cast<float*>(ws + 2 * align256(mk));
+    // scales after the HQ-DM path's second plane, or (compact) right after the codes
+    const size_t sa_off = (compact && path != TABIT_PATH_HQDM ? 1 : 2) * align256(mk);
+    float* sa = reinterpret_cast<float*>(ws + sa_off);
     if (path == TABIT_PATH_HQDM) {
       int8_t* xl = reinterpret_cast<int8_t*>(ws + align256(mk));
       e = tabit::launch_quant_hqdm(x_bf16, M, K, had_block, xq, xl, sa, s);
@@ -498,6 +510,66 @@ int tabit_scheduled_linear(tabit_ctx* ctx, int step, int layer, int path, const 
   if (M == 0 || N == 0) return TABIT_OK;
   return enqueue_linear(ctx, path, fmt, k, x_bf16, M, N, K, had_block, w_q, w_scale, w_fp4, w_e8m0,
                         static_cast<uint8_t*>(act_ws), y_bf16, stream);
+}
+
+// Device scratch of tabit_scheduled_linear_noalloc: a file-scope array, so the
+// entry point never allocates.  Each GPU the library runs on holds its own copy
+// (loaded with the code object, kept until the process ends); host code reaches
+// it only through the address hipGetSymbolAddress returns on that device.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+// The current device's address of `scratch`, looked up once per device with
+// that device current.
+hipError_t scratch_on_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+size_t tabit_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+int tabit_scheduled_linear_noalloc(tabit_ctx* ctx, int step, int layer, int path,
+                                   const uint16_t* x_bf16, int M, int N, int K, int had_block,
+                                   const int8_t* w_q, const float* w_scale, const uint8_t* w_fp4,
+                                   const uint8_t* w_e8m0, uint16_t* y_bf16, void* stream) {
+  if (ctx == nullptr) return TABIT_EINVAL;
+  if (!valid_int8_path(path)) return fail(ctx, TABIT_EINVAL, "unknown path %d", path);
+  int k = 0, fmt = 0;
+  int st = tabit_schedule_lookup(ctx, step, layer, &k, &fmt);
+  if (st != TABIT_OK) return st;
+  st = check_linear(ctx, step, layer, path, fmt, x_bf16, M, N, K, had_block, w_q, w_scale, w_fp4,
+                    w_e8m0, y_bf16);
+  if (st != TABIT_OK) return st;
+  const size_t need = compact_ws_bytes(path, fmt, M, K);
+  if (need > kNoAllocScratchBytes)
+    return fail(ctx, TABIT_ESHAPE,
+                "%d x %d activations need %zu bytes of scratch; the static scratch holds %zu",
+                M, K, need, kNoAllocScratchBytes);
+  if (M == 0 || N == 0) return TABIT_OK;
+  void* ws = nullptr;
+  st = hip_status(ctx, scratch_on_current_device(&ws), "scratch address lookup");
+  if (st != TABIT_OK) return st;
+  return enqueue_linear(ctx, path, fmt, k, x_bf16, M, N, K, had_block, w_q, w_scale, w_fp4, w_e8m0,
+                        static_cast<uint8_t*>(ws), y_bf16, stream, /*compact=*/true);
 }
 
 size_t tabit_dmpq_workspace_bytes(int M) { return tabit::dmpq_workspace_bytes(M); }
