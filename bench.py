@@ -773,6 +773,9 @@ def main() -> int:
     ap.add_argument("--tune", action="store_true",
                     help="autotune the GEMM tiles per shape during warm-up (default: the library's "
                          "calibrated choice, which keeps counter runs on the same kernels)")
+    ap.add_argument("--chain-mlp", action="store_true",
+                    help="MLP down projections read the up projection's output through the GELU "
+                         "folded into their quantizer (PixArt and CogVideoX stacks: GELU MLPs)")
     ap.add_argument("--shared-x", action="store_true",
                     help="reuse step 0's activations at every step (same work, faster set-up)")
     ap.add_argument("--gelu-fusion", action="store_true",
@@ -828,6 +831,10 @@ def main() -> int:
         copy_calibration(args.copy_calibration)
         return 0
 
+    if args.chain_mlp and args.workload not in ("c2", "c5"):
+        print("--chain-mlp applies to the GELU-MLP stacks (c2, c5); SANA and SDXL use gated MLPs",
+              file=sys.stderr)
+        return 2
     if args.gpus != 1:
         print("bench.py measures one GPU: the linear shards by tokens with no communication, "
               "so it runs and reports one GPU's share only (--gpus 1).",
@@ -908,6 +915,11 @@ def main() -> int:
         layers[li].w_fp4 = wt["w_fp4"].data_ptr() if "w_fp4" in wt else None
         layers[li].w_e8m0 = wt["w_e8m0"].data_ptr() if "w_e8m0" in wt else None
         layers[li].y_bf16 = ys[li].data_ptr()
+        if args.chain_mlp and layer.name.endswith("mlp_down"):
+            # the down projection reads the up projection's output through the GELU
+            # folded into its quantizer (the layer before it in the block)
+            assert wl.layers[li - 1].name.endswith("mlp_up")
+            layers[li].input_from, layers[li].input_act = li, T.ACT_GELU
     x_ptrs = (ctypes.c_void_p * (Tn * L))()
     for t in range(Tn):
         for li, layer in enumerate(wl.layers):
@@ -1109,6 +1121,8 @@ def main() -> int:
                    "tokens": sorted({l.M for l in wl.layers}), "had_block": b,
                    "path": args.path, "step": "one full denoising schedule (quantizer + GEMM per layer-step)",
                    "launch": "hip_graph" if args.graph else "eager",
+                   "mlp": "chained through the GELU-fused quantizer" if args.chain_mlp
+                   else "each layer reads its own synthetic input",
                    "int8_layer_steps": int((wl.fmt == 0).sum()), "mxfp4_layer_steps": int((wl.fmt == 1).sum())},
         "frac_of_int8_peak": round(value / INT8_PEAK_TOPS, 4),
         "roofline": roofline,

@@ -215,16 +215,18 @@ int tabit_plane_qgemm(tabit_ctx* ctx, const int8_t* x_q, const float* x_scale,
  * once and never written in bf16.  Per element g = bf16_rne(gelu(x)) with
  *   gelu(x) = 0.5 x (1 + tanh(u)) = x / (1 + exp(-2u)),
  *   u = sqrt(2/pi) (x + 0.044715 x^3),
- * magnitudes below 2^-100 taken as 0; then exactly tabit_hadamard_quant_act
- * (INT8) on g.  GELU is evaluated in fp32 with the hardware exp2 and
- * reciprocal: within 16 ulp (x >= 0) or (16|2u| + 24) ulp (x < 0) of the exact
- * value (ulp = 2^-24 relative), so g is the correctly rounded bf16 of the
- * exact GELU except where that lies within this bound of a rounding boundary.
- *   x_bf16 device [M][K] (the up projection's output); x_q int8 [M][K];
- *   x_scale fp32 [M].  Errors as tabit_hadamard_quant_act.
+ * magnitudes below 2^-100 taken as 0; then exactly tabit_hadamard_quant_act on
+ * g in the format `fmt` (INT8, or MXFP4 with had_block 0 or 32 for layer-steps
+ * scheduled to 4 bits; 6Bit-Diffusion section 2A).  GELU is evaluated in fp32
+ * with the hardware exp2 and reciprocal: within 16 ulp (x >= 0) or
+ * (16|2u| + 24) ulp (x < 0) of the exact value (ulp = 2^-24 relative), so g is
+ * the correctly rounded bf16 of the exact GELU except where that lies within
+ * this bound of a rounding boundary.
+ *   x_bf16 device [M][K] (the up projection's output); x_q and x_scale as
+ *   tabit_hadamard_quant_act for `fmt`.  Errors as tabit_hadamard_quant_act.
  */
 int tabit_gelu_quant_act(tabit_ctx* ctx, const uint16_t* x_bf16, int M, int K, int had_block,
-                         int8_t* x_q, float* x_scale, void* stream);
+                         int fmt, void* x_q, void* x_scale, void* stream);
 
 /*
  * HQ-DM single-Hadamard activation quantizer (HQ-DM section 2.1: only the
@@ -364,6 +366,9 @@ int tabit_gated_linear(tabit_ctx* ctx, const uint8_t* fmt_dev, int k_bits, int p
                        const uint8_t* w_e8m0, void* act_ws, size_t act_ws_bytes, uint16_t* y_bf16,
                        void* stream);
 
+/* Activation applied to a layer's input inside its quantizer (tabit_layer). */
+enum tabit_act { TABIT_ACT_NONE = 0, TABIT_ACT_GELU = 1 };
+
 /* One linear layer of a stack, for tabit_run_schedule. */
 typedef struct tabit_layer {
   int M, N, K;               /* tokens, output and input features                     */
@@ -373,6 +378,12 @@ typedef struct tabit_layer {
   const uint8_t* w_fp4;      /* device [N][K/2] MXFP4 copy (NULL if never MXFP4)      */
   const uint8_t* w_e8m0;     /* device [N][K/32]                                      */
   uint16_t* y_bf16;          /* device [M][N] output                                  */
+  int input_from;            /* 0: the input is x_bf16[step][layer]; j + 1: the       */
+                             /* output y_bf16 of layer j (< this layer) of the same   */
+                             /* step, e.g. the MLP's up projection for its down one   */
+  int input_act;             /* TABIT_ACT_NONE, or TABIT_ACT_GELU: the quantizer      */
+                             /* applies GELU first (tabit_gelu_quant_act); not on     */
+                             /* TABIT_PATH_HQDM                                       */
 } tabit_layer;
 
 /*
@@ -381,7 +392,11 @@ typedef struct tabit_layer {
  * tabit_scheduled_linear(t, l, ...) (TASQ section 2: the per-(layer, stage)
  * precision is applied by reading the table, with no weight copy).
  *   x_bf16      host array [num_steps][num_layers] of device pointers to the
- *               layer inputs ([M][K] bf16 each).
+ *               layer inputs ([M][K] bf16 each); ignored (may be NULL) for
+ *               layers whose input_from names an earlier layer.  A chained
+ *               layer reads that layer's y_bf16 of the same step, through the
+ *               GELU-fused quantizer when input_act = TABIT_ACT_GELU (the MLP:
+ *               up projection -> GELU -> down projection).
  *   gemm_events NULL, or a host array of 2 * num_steps * num_layers hipEvent_t
  *               (passed as void*): events[2i] and events[2i+1] become the start
  *               and stop events of the GEMM dispatch of layer-step i

@@ -492,6 +492,13 @@ def quantize_act_gelu_int8(x_bits: np.ndarray, had_block: int) -> Tuple[np.ndarr
     return quantize_act_int8(f64_to_bf16_bits(g), had_block)
 
 
+def quantize_act_gelu_mx(x_bits: np.ndarray, had_block: int) -> Tuple[np.ndarray, np.ndarray]:
+    """The same input for a down projection scheduled to 4 bits (6Bit-Diffusion section
+    2A): bf16(gelu(x)), then mx_quantize_rows."""
+    g = gelu_tanh_f64(bf16_to_f32(np.asarray(x_bits)))
+    return mx_quantize_rows(bf16_to_f32(f64_to_bf16_bits(g)), had_block)
+
+
 # --------------------------------------------------------------------------
 # HQ-DM single Hadamard: rotate only the activations, keep the weights as they are
 # --------------------------------------------------------------------------

@@ -152,3 +152,42 @@ def check_gelu_quant(x_bits: np.ndarray, had_block: int, q: np.ndarray, s: np.nd
                 break
         assert ok, f"row {m}: no admissible choice of the {len(elems)} ambiguous elements gives the kernel's codes"
     return {"ambiguous_elements": len(amb), "ambiguous_rows": len(by_row), "exact_rows": len(exact_rows)}
+
+
+def check_gelu_quant_mx(x_bits: np.ndarray, had_block: int, packed: np.ndarray,
+                        e8m0: np.ndarray) -> dict:
+    """As check_gelu_quant, for the MXFP4 format: each 32-element block (its own E8M0
+    scale) must equal the oracle's MX quantization of some admissible choice of its
+    ambiguous elements (equal inputs sharing one value); blocks without an ambiguous
+    element must match bit for bit."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    M, K = x_bits.shape
+    ref_bits, amb = admissible_bf16(x_bits)
+    p_ref, e_ref = O.mx_quantize_rows(O.bf16_to_f32(ref_bits), had_block)
+    blk_amb = {}
+    for m, k, c in amb:
+        blk_amb.setdefault((m, k // 32), {}).setdefault(int(x_bits[m, k]), (c, []))[1].append(k)
+    mask = np.ones((M, K // 32), dtype=bool)
+    for (m, j) in blk_amb:
+        mask[m, j] = False
+    pb = np.asarray(packed).reshape(M, K // 32, 16)
+    pr = p_ref.reshape(M, K // 32, 16)
+    np.testing.assert_array_equal(pb[mask], pr[mask])
+    np.testing.assert_array_equal(np.asarray(e8m0)[mask], e_ref[mask])
+    for (m, j), keys in blk_amb.items():
+        if len(keys) > MAX_KEYS_PER_BLOCK:
+            raise AssertionError(f"row {m} block {j}: too many distinct ambiguous inputs")
+        groups = list(keys.values())
+        base = _bits_to_f64(ref_bits[m, 32 * j:32 * j + 32]).astype(np.float32)
+        rows = []
+        for combo in itertools.product(*[c for c, _ in groups]):
+            blk = base.copy()
+            for (_, ks), cb in zip(groups, combo):
+                for k in ks:
+                    blk[k - 32 * j] = np.float32(_bits_to_f64(cb))
+            rows.append(blk)
+        pc, ec = O.mx_quantize_rows(np.stack(rows), had_block)
+        ok = any(np.array_equal(pc[i], pb[m, j]) and ec[i, 0] == e8m0[m, j] for i in range(len(rows)))
+        assert ok, f"row {m} block {j}: no admissible choice gives the kernel's MX bytes"
+    return {"ambiguous_elements": len(amb), "ambiguous_blocks": len(blk_amb),
+            "exact_blocks": int(mask.sum())}

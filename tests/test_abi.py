@@ -144,13 +144,38 @@ def test_gated_linear_validation(lib, ctx):
 
 
 def test_gelu_quant_validation(lib, ctx):
-    def q(M=4, K=64, b=0, xq=FAKE, sc=FAKE):
-        return lib.tabit_gelu_quant_act(ctx.handle, FAKE, M, K, b, xq, sc, None)
+    def q(M=4, K=64, b=0, fmt=0, xq=FAKE, sc=FAKE):
+        return lib.tabit_gelu_quant_act(ctx.handle, FAKE, M, K, b, fmt, xq, sc, None)
     assert q(xq=None) == T.EINVAL
+    assert q(fmt=2) == T.EINVAL
     assert q(b=16) == T.ERANGE
+    assert q(fmt=1, b=64) == T.ERANGE                  # MXFP4 takes b in {0, 32}
     assert q(K=48) == T.ESHAPE
     assert q(xq=MISALIGNED) == T.EALIGN
     assert q(M=0) == T.OK
+
+
+def test_run_schedule_chain_validation(lib, ctx):
+    """Chained inputs (MLP up -> GELU -> down) are validated before any launch."""
+    ctx.set_step_schedule(np.zeros((1, 2), np.uint8))
+
+    def run(from1=1, act1=T.ACT_GELU, k1=256, path=0, m1=8):
+        layers = (T.Layer * 2)()
+        layers[0].M, layers[0].N, layers[0].K = 8, 256, 64
+        layers[1].M, layers[1].N, layers[1].K = m1, 64, k1
+        for l in layers:
+            l.w_q, l.w_scale, l.y_bf16 = FAKE, FAKE, FAKE
+        layers[1].input_from, layers[1].input_act = from1, act1
+        x_ptrs = (ctypes.c_void_p * 2)(FAKE, None)
+        return lib.tabit_run_schedule(ctx.handle, 0, 1, layers, 2, x_ptrs, 0, path, FAKE, 1 << 30,
+                                      None, None)
+    assert run(from1=2) == T.EINVAL                    # not an earlier layer
+    assert run(from1=-1) == T.EINVAL
+    assert run(act1=7) == T.EINVAL
+    assert run(k1=128) == T.ESHAPE                     # layer 0's output is 8 x 256
+    assert run(m1=16) == T.ESHAPE
+    assert run(path=4) == T.EINVAL                     # no GELU-fused HQ-DM quantizer
+    assert run(from1=0) == T.EINVAL                    # external input missing (NULL)
 
 
 def test_hqdm_validation(lib, ctx):

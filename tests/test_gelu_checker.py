@@ -82,3 +82,21 @@ def test_checker_rejects_planted_mistakes(b):
     qe, se = O.quantize_act_int8(O.f64_to_bf16_bits(np.where(np.abs(ge) < 2.0 ** -100, 0.0, ge)), b)
     with pytest.raises(AssertionError):
         V.check_gelu_quant(xb, b, qe, se)
+
+
+@pytest.mark.parametrize("b", [0, 32])
+def test_mx_checker_accepts_admissible_and_rejects_mistakes(b):
+    xb = _inputs(16, 512, seed=13 + b)
+    p, e = O.quantize_act_gelu_mx(xb, b)
+    V.check_gelu_quant_mx(xb, b, p, e)
+    pm, em = O.mx_quantize_rows(O.bf16_to_f32(_fp32_model(xb)), b)
+    info = V.check_gelu_quant_mx(xb, b, pm, em)
+    assert info["ambiguous_elements"] > 0
+    bad = p.copy()
+    bad[4, 37] ^= 0x01                                    # one E2M1 code off
+    with pytest.raises(AssertionError):
+        V.check_gelu_quant_mx(xb, b, bad, e)
+    e2 = e.copy()
+    e2[2, 3] += 1                                         # one block scale off
+    with pytest.raises(AssertionError):
+        V.check_gelu_quant_mx(xb, b, p, e2)

@@ -136,3 +136,26 @@ def test_gelu_quant_valid_full_size_sampled_rows(ctx, M, K, b):
     rows = np.unique(np.r_[0, 1, 2, 3, M - 1, np.random.default_rng(2).choice(M, 91, replace=False)])
     info = V.check_gelu_quant(S.bf16_bits(x)[rows], b, _np(q)[rows], _np(s)[rows])
     print(f"  {info}", flush=True)
+
+
+@pytest.mark.parametrize("M,K,b", [(37, 640, 0), (37, 640, 32), (300, 4608, 32), (129, 2560, 0)])
+def test_gelu_quant_mx_valid(ctx, M, K, b):
+    """The MXFP4 form of the fused quantizer: every 32-element block (own E8M0 scale)
+    from an admissible choice of bf16 neighbours; other blocks bit-exact."""
+    from tests import gelu_validity as V
+    x = _gelu_inputs(M, K, seed=M * 7 + K + b)
+    print(f"gelu_quant mx {M}x{K} b={b}", flush=True)
+    p, e = ctx.gelu_quant_act(x.to(DEV), b, fmt=T.FMT_MXFP4)
+    info = V.check_gelu_quant_mx(S.bf16_bits(x), b, _np(p), _np(e))
+    print(f"  {info}", flush=True)
+
+
+def test_gelu_quant_mx_valid_full_size_sampled_rows(ctx):
+    from tests import gelu_validity as V
+    M, K, b = 17776, 7680, 32
+    x = _gelu_inputs(M, K, seed=91)
+    print(f"gelu_quant mx full {M}x{K}", flush=True)
+    p, e = ctx.gelu_quant_act(x.to(DEV), b, fmt=T.FMT_MXFP4)
+    rows = np.unique(np.r_[0, 1, 2, 3, M - 1, np.random.default_rng(4).choice(M, 91, replace=False)])
+    info = V.check_gelu_quant_mx(S.bf16_bits(x)[rows], b, _np(p)[rows], _np(e)[rows])
+    print(f"  {info}", flush=True)

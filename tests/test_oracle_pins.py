@@ -415,7 +415,7 @@ def test_gelu_golden_values_and_row():
             assert g == 0.0 if bits == 0 else abs(g - gv) <= 1e-12 * abs(gv), x
             assert O.f64_to_bf16_bits(np.array([g]))[0] & 0x7FFF == bits & 0x7FFF
             assert bits == 0 or O.f64_to_bf16_bits(np.array([g]))[0] == bits
-        else:
+        elif tag == "row":
             b = int(parts[0])
             lead = [int(c) for c in parts[1].split()]
             num, den = (int(t) for t in parts[2].split())
@@ -423,6 +423,21 @@ def test_gelu_golden_values_and_row():
     q, s = O.quantize_act_gelu_int8(_bits([xs]), b)
     assert q[0, :11].tolist() == lead and not q[0, 11:].any()
     assert s[0] == _fp32_round(Fraction(num, den))
+
+
+def test_gelu_mx_golden_block():
+    """Hand-worked MXFP4 codes of the golden row's GELU values (the 4-bit format of
+    6Bit-Diffusion section 2A, OCP MX v1.0 encoding)."""
+    for line in _lines("gelu_bf16_worked.txt"):
+        if line.startswith("mx "):
+            parts = [p.strip() for p in line.split(" ", 1)[1].split("|")]
+            b = int(parts[0])
+            lead = [int(v, 16) for v in parts[1].split()]
+            e8 = int(parts[2])
+    xs = [-0.5, -1, -1.5, -2, -3, -4, -6, -9, -9.5, 0.5, 2] + [0.0] * 21
+    p, e = O.quantize_act_gelu_mx(_bits([xs]), b)
+    assert p[0, :6].tolist() == lead and not p[0, 6:].any()
+    assert e[0].tolist() == [e8]
 
 
 def test_gelu_quant_is_identity_quant_on_large_inputs():
@@ -433,6 +448,10 @@ def test_gelu_quant_is_identity_quant_on_large_inputs():
         q1, s1 = O.quantize_act_gelu_int8(xb, b)
         q2, s2 = O.quantize_act_int8(xb, b)
         assert np.array_equal(q1, q2) and np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+    for b in (0, 32):
+        p1, e1 = O.quantize_act_gelu_mx(xb, b)
+        p2, e2 = O.mx_quantize_rows(O.bf16_to_f32(xb), b)
+        assert np.array_equal(p1, p2) and np.array_equal(e1, e2)
 
 
 # ---------------------------------------------------------------- HQ-DM single Hadamard

@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     OK, EINVAL, ESHAPE, EALIGN, ERANGE, ENOSCHED, EHIP, ENOMEM,
     FMT_INT8, FMT_MXFP4, PATH_MASKED, PATH_BITSERIAL, PATH_PLANES, PATH_HQDM, PATH_MXFP4_GEMM,
     OPT_GEMM_CONFIG, OPT_MXFP4_CONFIG, OPT_PLANE_CONFIG, OPT_HQDM_CONFIG, hqdm_config_info,
+    ACT_NONE, ACT_GELU,
 )
 
 __all__ = [
@@ -22,4 +23,5 @@ __all__ = [
     "PATH_BITSERIAL", "PATH_PLANES", "OPT_GEMM_CONFIG", "OPT_MXFP4_CONFIG", "OPT_PLANE_CONFIG",
     "plane_config_info", "plane_config_choose", "weight_planes_bytes", "dmpq_workspace_bytes",
     "PATH_HQDM", "OPT_HQDM_CONFIG", "hqdm_config_info", "noalloc_scratch_bytes",
+    "ACT_NONE", "ACT_GELU",
 ]

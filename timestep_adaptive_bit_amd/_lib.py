@@ -23,6 +23,7 @@ FMT_INT8, FMT_MXFP4 = 0, 1
 PATH_MASKED, PATH_BITSERIAL, PATH_PLANES, PATH_HQDM = 0, 1, 3, 4
 OPT_GEMM_CONFIG, OPT_MXFP4_CONFIG, OPT_PLANE_CONFIG, OPT_HQDM_CONFIG = 0, 1, 2, 3
 PATH_MXFP4_GEMM = 2
+ACT_NONE, ACT_GELU = 0, 1
 
 _c_int, _c_void_p, _c_size_t, _c_float = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
 _PINT = ctypes.POINTER(ctypes.c_int)
@@ -75,8 +76,8 @@ _SIGNATURES = {
     "tabit_mfma_probe_sink_ints": (_c_size_t, [_c_int]),
     "tabit_weight_planes_bytes": (_c_size_t, [_c_int, _c_int]),
     "tabit_dmpq_workspace_bytes": (_c_size_t, [_c_int]),
-    "tabit_gelu_quant_act": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p,
-                                      _c_void_p, _c_void_p]),
+    "tabit_gelu_quant_act": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int,
+                                      _c_void_p, _c_void_p, _c_void_p]),
     "tabit_hqdm_quant_act": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p,
                                       _c_void_p, _c_void_p, _c_void_p]),
     "tabit_hqdm_qgemm": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -96,7 +97,8 @@ class Layer(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int), ("N", ctypes.c_int), ("K", ctypes.c_int),
                 ("w_q", ctypes.c_void_p), ("w_scale", ctypes.c_void_p),
                 ("w_fp4", ctypes.c_void_p), ("w_e8m0", ctypes.c_void_p),
-                ("y_bf16", ctypes.c_void_p)]
+                ("y_bf16", ctypes.c_void_p), ("input_from", ctypes.c_int),
+                ("input_act", ctypes.c_int)]
 
 
 _lib = None
@@ -376,18 +378,25 @@ class Context:
         return self._gemm_i8(self._lib.tabit_qgemm_bitserial, x_q, x_scale, w_q, w_scale, k_bits, y,
                              acc, want_y, want_acc)
 
-    def gelu_quant_act(self, x: torch.Tensor, had_block: int, x_q=None, x_scale=None):
-        """Down projection's input codes with the GELU folded in: int8 [M, K] + fp32 [M]."""
+    def gelu_quant_act(self, x: torch.Tensor, had_block: int, x_q=None, x_scale=None,
+                       fmt: int = FMT_INT8):
+        """Down projection's input codes with the GELU folded in: int8 [M, K] + fp32 [M], or
+        (fmt = FMT_MXFP4) fp4 [M, K/2] + e8m0 [M, K/32]."""
         _dev(x, torch.bfloat16, "x")
         M, K = x.shape
-        if x_q is None:
-            x_q = torch.empty((M, K), dtype=torch.int8, device=x.device)
-        if x_scale is None:
-            x_scale = torch.empty((M,), dtype=torch.float32, device=x.device)
-        _dev(x_q, torch.int8, "x_q", (M, K))
-        _dev(x_scale, torch.float32, "x_scale", (M,))
-        st = self._lib.tabit_gelu_quant_act(self._h, x.data_ptr(), M, K, had_block, x_q.data_ptr(),
-                                            x_scale.data_ptr(), _stream(x.device))
+        dev = x.device
+        if fmt == FMT_INT8:
+            x_q = torch.empty((M, K), dtype=torch.int8, device=dev) if x_q is None else x_q
+            x_scale = torch.empty((M,), dtype=torch.float32, device=dev) if x_scale is None else x_scale
+            _dev(x_q, torch.int8, "x_q", (M, K))
+            _dev(x_scale, torch.float32, "x_scale", (M,))
+        else:
+            x_q = torch.empty((M, K // 2), dtype=torch.uint8, device=dev) if x_q is None else x_q
+            x_scale = torch.empty((M, K // 32), dtype=torch.uint8, device=dev) if x_scale is None else x_scale
+            _dev(x_q, torch.uint8, "x_q", (M, K // 2))
+            _dev(x_scale, torch.uint8, "x_scale", (M, K // 32))
+        st = self._lib.tabit_gelu_quant_act(self._h, x.data_ptr(), M, K, had_block, fmt,
+                                            x_q.data_ptr(), x_scale.data_ptr(), _stream(dev))
         self._check(st)
         return x_q, x_scale
 

@@ -417,21 +417,32 @@ int tabit_mxfp4_qgemm(tabit_ctx* ctx, const uint8_t* x_fp4, const uint8_t* x_e8m
 }
 
 int tabit_gelu_quant_act(tabit_ctx* ctx, const uint16_t* x_bf16, int M, int K, int had_block,
-                         int8_t* x_q, float* x_scale, void* stream) {
+                         int fmt, void* x_q, void* x_scale, void* stream) {
   if (ctx == nullptr) return TABIT_EINVAL;
   if (x_bf16 == nullptr || x_q == nullptr || x_scale == nullptr)
     return fail(ctx, TABIT_EINVAL, "null pointer");
+  if (fmt != TABIT_FMT_INT8 && fmt != TABIT_FMT_MXFP4)
+    return fail(ctx, TABIT_EINVAL, "unknown fmt %d", fmt);
   int st = check_k_shape(ctx, M, K, had_block);
   if (st != TABIT_OK) return st;
+  if (fmt == TABIT_FMT_MXFP4 && had_block != 0 && had_block != 32)
+    return fail(ctx, TABIT_ERANGE, "MXFP4 takes had_block 0 or 32 (got %d)", had_block);
   if ((size_t)M * (size_t)K > kMaxOperandBytes)
     return fail(ctx, TABIT_ESHAPE, "activations must stay below 2 GiB");
-  if (!aligned(x_bf16, 16) || !aligned(x_q, 16) || !aligned(x_scale, 4))
+  if (!aligned(x_bf16, 16) || !aligned(x_q, 16) || (fmt == TABIT_FMT_INT8 && !aligned(x_scale, 4)))
     return fail(ctx, TABIT_EALIGN, "misaligned pointer");
   if (M == 0) return TABIT_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fmt == TABIT_FMT_INT8)
+    return hip_status(ctx,
+                      tabit::launch_quant_gelu_int8(x_bf16, M, K, had_block,
+                                                    static_cast<int8_t*>(x_q),
+                                                    static_cast<float*>(x_scale), s),
+                      "gelu_quant_act launch");
   return hip_status(ctx,
-                    tabit::launch_quant_gelu_int8(x_bf16, M, K, had_block, x_q, x_scale,
-                                                  static_cast<hipStream_t>(stream)),
-                    "gelu_quant_act launch");
+                    tabit::launch_quant_gelu_mx(x_bf16, M, K, had_block, static_cast<uint8_t*>(x_q),
+                                                static_cast<uint8_t*>(x_scale), s),
+                    "gelu_quant_act (mxfp4) launch");
 }
 
 int tabit_hqdm_quant_act(tabit_ctx* ctx, const uint16_t* x_bf16, int M, int K, int had_block,
@@ -675,6 +686,19 @@ int tabit_run_schedule(tabit_ctx* ctx, int first_step, int num_steps, const tabi
     const tabit_layer& L = layers[l];
     int st = check_k_shape(ctx, L.M, L.K, had_block);
     if (st != TABIT_OK) return st;
+    if (L.input_from < 0 || L.input_from > l)
+      return fail(ctx, TABIT_EINVAL, "layer %d: input_from %d must name an earlier layer (1..%d) or 0",
+                  l, L.input_from, l);
+    if (L.input_act != TABIT_ACT_NONE && L.input_act != TABIT_ACT_GELU)
+      return fail(ctx, TABIT_EINVAL, "layer %d: unknown input_act %d", l, L.input_act);
+    if (L.input_from > 0) {
+      const tabit_layer& P = layers[L.input_from - 1];
+      if (P.M != L.M || P.N != L.K)
+        return fail(ctx, TABIT_ESHAPE, "layer %d: input from layer %d is %d x %d, needs %d x %d", l,
+                    L.input_from - 1, P.M, P.N, L.M, L.K);
+    }
+    if (L.input_act == TABIT_ACT_GELU && path == TABIT_PATH_HQDM)
+      return fail(ctx, TABIT_EINVAL, "layer %d: the HQ-DM path has no GELU-fused quantizer", l);
     if (L.N < 0 || L.N % 32 != 0)
       return fail(ctx, TABIT_ESHAPE, "layer %d: N must be a non-negative multiple of 32", l);
     if (L.y_bf16 == nullptr || !aligned(L.y_bf16, 16))
@@ -687,7 +711,8 @@ int tabit_run_schedule(tabit_ctx* ctx, int first_step, int num_steps, const tabi
                   act_ws_bytes, tabit_act_workspace_bytes(L.M, L.K));
     for (int t = first_step; t < first_step + num_steps; ++t) {
       const size_t i = (size_t)t * ctx->layers + l;
-      const uint16_t* x = x_bf16[(size_t)(t - first_step) * num_layers + l];
+      const uint16_t* x = L.input_from > 0 ? layers[L.input_from - 1].y_bf16
+                                           : x_bf16[(size_t)(t - first_step) * num_layers + l];
       if (x == nullptr || !aligned(x, 16))
         return fail(ctx, TABIT_EINVAL, "step %d layer %d: missing or misaligned input", t, l);
       if (ctx->fmt[i] == TABIT_FMT_INT8) {
@@ -709,7 +734,8 @@ int tabit_run_schedule(tabit_ctx* ctx, int first_step, int num_steps, const tabi
       const tabit_layer& L = layers[l];
       const size_t li = (size_t)(t - first_step) * num_layers + l;
       const size_t i = (size_t)t * ctx->layers + l;
-      const uint16_t* x = x_bf16[li];
+      const uint16_t* x = L.input_from > 0 ? layers[L.input_from - 1].y_bf16 : x_bf16[li];
+      const bool gelu = L.input_act == TABIT_ACT_GELU;
       hipEvent_t e0 = gemm_events ? static_cast<hipEvent_t>(gemm_events[2 * li]) : nullptr;
       hipEvent_t e1 = gemm_events ? static_cast<hipEvent_t>(gemm_events[2 * li + 1]) : nullptr;
       if (L.M == 0 || L.N == 0) continue;
@@ -726,7 +752,8 @@ int tabit_run_schedule(tabit_ctx* ctx, int first_step, int num_steps, const tabi
                                       L.w_scale, L.M, L.N, L.K, ctx->k_bits[i], L.y_bf16, nullptr,
                                       s, e0, e1);
         } else {
-          e = tabit::launch_quant_int8(x, L.M, L.K, had_block, 1.0f, xq, sa, s);
+          e = gelu ? tabit::launch_quant_gelu_int8(x, L.M, L.K, had_block, xq, sa, s)
+                   : tabit::launch_quant_int8(x, L.M, L.K, had_block, 1.0f, xq, sa, s);
           if (e != hipSuccess) return hip_status(ctx, e, "run_schedule quantizer launch");
           e = launch_int8_family(ctx, path, xq, sa, L.w_q, L.w_scale, L.M, L.N, L.K, ctx->k_bits[i],
                                  L.y_bf16, nullptr, s, num_cus, e0, e1);
@@ -735,7 +762,8 @@ int tabit_run_schedule(tabit_ctx* ctx, int first_step, int num_steps, const tabi
       } else {
         uint8_t* xf = ws;
         uint8_t* xe = ws + align256(mk / 2);
-        e = tabit::launch_quant_mx(x, L.M, L.K, had_block, xf, xe, s);
+        e = gelu ? tabit::launch_quant_gelu_mx(x, L.M, L.K, had_block, xf, xe, s)
+                 : tabit::launch_quant_mx(x, L.M, L.K, had_block, xf, xe, s);
         if (e != hipSuccess) return hip_status(ctx, e, "run_schedule MX quantizer launch");
         int cfg = ctx->force_mx_cfg;
         if (cfg < 0) cfg = ctx->tuned_cfg(2, L.M, L.N, L.K);

@@ -275,7 +275,10 @@ __device__ __forceinline__ uint32_t drop_negative_zero(uint32_t x) {
   return mag | (x & ((mag + 0x77777777u) & 0x88888888u));
 }
 
-template <int B, int CPT>
+// GELU: each input element becomes bf16(gelu(x)) first (the MLP's activation
+// folded into the quantizer of the down projection's input, as in
+// quant_int8_kernel's Q_GELU mode).
+template <int B, int CPT, bool GELU>
 __global__ void __launch_bounds__(QT)
 quant_mx_kernel(const uint16_t* __restrict__ x, long long nchunks, uint8_t* __restrict__ qf,
                 uint8_t* __restrict__ e8, const uint8_t* __restrict__ gate) {
@@ -289,6 +292,10 @@ quant_mx_kernel(const uint16_t* __restrict__ x, long long nchunks, uint8_t* __re
     float v[16];
     if (valid) {
       load_chunk(x + c * 16, v);
+      if constexpr (GELU) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = __uint_as_float((uint32_t)tile_bf16(gelu_tanh(v[e])) << 16);
+      }
     } else {
 #pragma unroll
       for (int e = 0; e < 16; ++e) v[e] = 0.0f;
@@ -397,19 +404,34 @@ hipError_t launch_quant_hqdm(const uint16_t* x, int M, int K, int had_block, int
   return launch_int8_rows<Q_HQDM>(x, M, K, had_block, div, q_hi, scale, stream, gate, q_lo);
 }
 
-hipError_t launch_quant_mx(const uint16_t* x, int M, int K, int had_block, uint8_t* q_fp4,
-                           uint8_t* e8m0, hipStream_t stream, const uint8_t* gate) {
+namespace {
+
+template <bool GELU>
+hipError_t launch_mx(const uint16_t* x, int M, int K, int had_block, uint8_t* q_fp4,
+                     uint8_t* e8m0, hipStream_t stream, const uint8_t* gate) {
   if (M <= 0) return hipSuccess;
   constexpr int CPT = 1;   // one chunk per thread: 7-36% faster than 2-8 on MI355X
   const long long nchunks = (long long)M * K / 16;
   const long long per_wg = (long long)QT * CPT;
   const int grid = (int)((nchunks + per_wg - 1) / per_wg);
   if (had_block == 32) {
-    quant_mx_kernel<32, CPT><<<grid, QT, 0, stream>>>(x, nchunks, q_fp4, e8m0, gate);
+    quant_mx_kernel<32, CPT, GELU><<<grid, QT, 0, stream>>>(x, nchunks, q_fp4, e8m0, gate);
   } else {
-    quant_mx_kernel<0, CPT><<<grid, QT, 0, stream>>>(x, nchunks, q_fp4, e8m0, gate);
+    quant_mx_kernel<0, CPT, GELU><<<grid, QT, 0, stream>>>(x, nchunks, q_fp4, e8m0, gate);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_mx(const uint16_t* x, int M, int K, int had_block, uint8_t* q_fp4,
+                           uint8_t* e8m0, hipStream_t stream, const uint8_t* gate) {
+  return launch_mx<false>(x, M, K, had_block, q_fp4, e8m0, stream, gate);
+}
+
+hipError_t launch_quant_gelu_mx(const uint16_t* x, int M, int K, int had_block, uint8_t* q_fp4,
+                                uint8_t* e8m0, hipStream_t stream, const uint8_t* gate) {
+  return launch_mx<true>(x, M, K, had_block, q_fp4, e8m0, stream, gate);
 }
 
 }  // namespace tabit

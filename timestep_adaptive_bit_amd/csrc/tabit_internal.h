@@ -40,6 +40,11 @@ hipError_t launch_quant_mx(const uint16_t* x, int M, int K, int had_block,
                            uint8_t* q_fp4, uint8_t* e8m0, hipStream_t stream,
                            const uint8_t* gate = nullptr);
 
+// MXFP4 quantization of bf16(gelu(x)) (the MLP's GELU folded in).
+hipError_t launch_quant_gelu_mx(const uint16_t* x, int M, int K, int had_block,
+                                uint8_t* q_fp4, uint8_t* e8m0, hipStream_t stream,
+                                const uint8_t* gate = nullptr);
+
 // ---------------------------------------------------------------- INT8 GEMM
 struct GemmConfig {
   int bm, bn, k_groups;   // wave groups splitting one tile's K stages (1 = none)
