@@ -23,9 +23,11 @@
 // under the compute.  One barrier per stage.  The step's LSB mask is applied to the weight
 // fragments as they come out of LDS (four v_and per 16-byte fragment).  The
 // matrix-core op is v_mfma_i32_32x32x32_i8 (it sustains ~90% of the chip's INT8
-// rate with a few independent accumulators per wave).  The
-// epilogue scales in fp32, rounds to bf16 and transposes through LDS for
-// 16-byte row-contiguous stores.
+// rate with a few independent accumulators per wave), with the weight fragment
+// as its first operand so that every lane ends with runs of four consecutive
+// output columns.  The epilogue scales in fp32 (the tile's scales were copied
+// into LDS at the start), rounds pairs to bf16 with the packed conversion and
+// stores 8 bytes per run straight from registers: no transpose, no barrier.
 //
 // K split inside the workgroup (KW > 1), for shapes whose tiles fit in one
 // round over the CUs (a few tokens, or a long K): KW groups of WM x WN waves
@@ -41,7 +43,11 @@ namespace tabit {
 namespace {
 
 using tile::v4i;
+using tile::v4u;
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 using tile::BKB;
 
 template <int BM, int BN, int WM, int WN, int RB, int NST, int KW, bool BITSERIAL>
@@ -64,9 +70,14 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
   static_assert(NW * KW * 64 <= 1024, "at most 1024 threads per workgroup");
   static_assert(NST == 2 || (BM % (8 * NW) == 0 && BN % (8 * NW) == 0),
                 "deeper rings count copies per wave: every wave copies the same share");
-  // the ring, or the bf16 staging of the epilogue when that is larger
-  constexpr int SMEM = KW * NST * STAGE > BM * BN * 2 ? KW * NST * STAGE : BM * BN * 2;
-  __shared__ __attribute__((aligned(1024))) int8_t smem[SMEM];
+  // the ring (the K groups' partial sums reuse it), then the tile's scales when they fit:
+  // SA of its BM rows, SB of its BN columns (padded to whole waves of 64 entries)
+  constexpr int RING = KW * NST * STAGE;
+  constexpr int NSCALE = BM + (BN + 63) / 64 * 64;
+  constexpr bool SCALES_IN_LDS = RING + NSCALE * 4 <= 160 * 1024;
+  static_assert(BM % 64 == 0 && NSCALE / 64 <= NW * KW, "one scale wave per 64 entries");
+  __shared__ __attribute__((aligned(1024))) int8_t smem[RING + (SCALES_IN_LDS ? NSCALE * 4 : 0)];
+  float* s_scale = reinterpret_cast<float*>(smem + RING);
 
   int tm, tn;
   tile::tile_coords<4>(tiles_m, tiles_n, tm, tn);
@@ -80,6 +91,25 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
   const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
   const auto rsa = tile::make_rsrc(A, (unsigned)M * (unsigned)K);
   const auto rsb = tile::make_rsrc(B, (unsigned)N * (unsigned)K);
+
+  if constexpr (SCALES_IN_LDS) {
+    // the epilogue's scales, copied once by 4-byte buffer loads straight into LDS
+    // (rows and columns past M and N read as 0); the first stage's wait covers them
+    const int w_all = tid >> 6;
+    if (w_all < NSCALE / 64) {
+      const int t = w_all * 64 + lane;
+      if (t < BM) {   // BM is a multiple of 64: the wave's entries are all rows
+        const auto rs = tile::make_rsrc(SA, (unsigned)M * 4u);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (tile::lds_ptr_t)(s_scale + w_all * 64), 4,
+                                                 (unsigned)(m0 + t) * 4u, 0, 0, 0);
+      } else {
+        const auto rs = tile::make_rsrc(SB, (unsigned)N * 4u);
+        const unsigned off = t - BM < BN ? (unsigned)(n0 + t - BM) * 4u : tile::kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (tile::lds_ptr_t)(s_scale + w_all * 64), 4,
+                                                 off, 0, 0, 0);
+      }
+    }
+  }
 
   const uint32_t m8 = (0xFFu << kbits) & 0xFFu;
   const int mask32 = (int)(m8 * 0x01010101u);
@@ -142,7 +172,7 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
           const v4i bm = b[cur][j] & mask32;   // TASQ LSB mask on the staged weight tile
 #pragma unroll
           for (int i = 0; i < FM; ++i)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[cur][i], bm, acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bm, a[cur][i], acc[i][j], 0, 0, 0);
         }
       } else {
         for (int p = 7; p >= kbits; --p) {
@@ -152,11 +182,40 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
             const v4i bp = b[cur][j] & pm;
 #pragma unroll
             for (int i = 0; i < FM; ++i)
-              acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[cur][i], bp, acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bp, a[cur][i], acc[i][j], 0, 0, 0);
           }
         }
       }
     }
+  }
+
+  // the epilogue's scales when they are not in LDS: loaded here, so that their
+  // latency overlaps the K groups' exchange below
+  const int row_w = m0 + wm * WTM, col_w = n0 + wn * WTN;
+  float sa_i[FM];
+  float4 sw_g[FN][4];
+  if (Y != nullptr && (KW == 1 || group == 0)) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int t = wm * WTM + i * 32 + (lane & 31);
+      if constexpr (SCALES_IN_LDS) sa_i[i] = s_scale[t];
+      else sa_i[i] = m0 + t < M ? SA[m0 + t] : 0.0f;
+    }
+    const bool sb16 = (reinterpret_cast<uintptr_t>(SB) & 15) == 0;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int gn = n0 + wn * WTN + j * 32 + g * 8 + khalf * 4;   // first column of the half-run
+        if constexpr (SCALES_IN_LDS) {
+          sw_g[j][g] = float4{};        // read from LDS where used
+        } else if (sb16 && gn + 3 < N) {
+          sw_g[j][g] = *reinterpret_cast<const float4*>(SB + gn);
+        } else {
+          sw_g[j][g] = make_float4(gn < N ? SB[gn] : 0.0f, gn + 1 < N ? SB[gn + 1] : 0.0f,
+                                   gn + 2 < N ? SB[gn + 2] : 0.0f, gn + 3 < N ? SB[gn + 3] : 0.0f);
+        }
+      }
   }
 
   if constexpr (KW > 1) {
@@ -195,50 +254,65 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
   const bool out = KW == 1 || group == 0;   // the waves that hold the tile's sums
 
   // ------------------------------------------------------------ epilogue
-  // 32x32 output layout: lane l, register r holds row (r/4)*8 + (l/32)*4 + r%4, col l%32.
-  const int row_w = m0 + wm * WTM, col_w = n0 + wn * WTN;
-  if (ACC != nullptr && out) {
+  // The weights are the MFMA's first operand, so block (i, j) holds Y^T: lane l,
+  // register r is output row m = i*32 + l%32 and column n = j*32 + (r/4)*8 +
+  // (l/32)*4 + r%4 of the wave tile -- four consecutive columns per group g = r/4
+  // of four registers; lanes l and l + 32 hold the two halves of an 8-column run.
+  // int32 results go out as 16 bytes per run.  bf16 results: each run is packed
+  // to two words, then one v_permlane32_swap per word pairs runs g and g + 1, so
+  // lane l holds run g's 8 columns and lane l + 32 run g + 1's: 16-byte stores
+  // straight from registers, no staging, no barrier.  (Plain stores: 8-byte or
+  // nontemporal pieces of a line measured 1.1x and 3x slower.)
+  if (!out) return;
+  if (ACC != nullptr) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int gm = row_w + i * 32 + (r >> 2) * 8 + khalf * 4 + (r & 3);
-          const int gn = col_w + j * 32 + (lane & 31);
-          if (gm < M && gn < N) ACC[(size_t)gm * N + gn] = acc[i][j][r];
+        for (int g = 0; g < 4; ++g) {
+          const int gm = row_w + i * 32 + (lane & 31);
+          const int gn = col_w + j * 32 + g * 8 + khalf * 4;
+          if (gm < M && gn < N)
+            *reinterpret_cast<v4i*>(ACC + (size_t)gm * N + gn) =
+                v4i{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
         }
   }
   if (Y != nullptr) {
-    // per-row scales: this lane's rows come in runs of 4 (r%4), so load float4s
-    float sa_r[FM][16], sb_c[FN];
-    const bool sa16 = (reinterpret_cast<uintptr_t>(SA) & 15) == 0;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int j = 0; j < FN; ++j) {
+      v2u pk[FM][4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int gm = row_w + i * 32 + g * 8 + khalf * 4;
-        if (sa16 && gm + 3 < M) {
-          const float4 v = *reinterpret_cast<const float4*>(SA + gm);
-          sa_r[i][g * 4 + 0] = v.x;
-          sa_r[i][g * 4 + 1] = v.y;
-          sa_r[i][g * 4 + 2] = v.z;
-          sa_r[i][g * 4 + 3] = v.w;
-        } else {
+        const float4 sw =
+            SCALES_IN_LDS ? *reinterpret_cast<const float4*>(s_scale + BM + wn * WTN + j * 32 + g * 8 +
+                                                              khalf * 4)
+                          : sw_g[j][g];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sa_r[i][g * 4 + e] = gm + e < M ? SA[gm + e] : 0.0f;
+        for (int i = 0; i < FM; ++i) {
+          // y = bf16_rne(((float)acc * sa) * sw): two fp32 multiplies in this order,
+          // then the packed round-to-nearest-even conversion
+          const v2f lo = v2f{((float)acc[i][j][4 * g] * sa_i[i]) * sw.x,
+                             ((float)acc[i][j][4 * g + 1] * sa_i[i]) * sw.y};
+          const v2f hi = v2f{((float)acc[i][j][4 * g + 2] * sa_i[i]) * sw.z,
+                             ((float)acc[i][j][4 * g + 3] * sa_i[i]) * sw.w};
+          pk[i][g] = v2u{__builtin_bit_cast(unsigned, __builtin_convertvector(lo, v2bf)),
+                         __builtin_bit_cast(unsigned, __builtin_convertvector(hi, v2bf))};
         }
       }
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int gn = col_w + j * 32 + (lane & 31);
-      sb_c[j] = gn < N ? SB[gn] : 0.0f;
+      for (int g = 0; g < 4; g += 2)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          // lanes 32-63 of run g's words trade places with lanes 0-31 of run g + 1's
+          const auto s0 = __builtin_amdgcn_permlane32_swap(pk[i][g][0], pk[i][g + 1][0], false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(pk[i][g][1], pk[i][g + 1][1], false, false);
+          const int gm = row_w + i * 32 + (lane & 31);
+          const int gn = col_w + j * 32 + (g + khalf) * 8;
+          if (gm < M && gn < N)
+            *reinterpret_cast<v4u*>(Y + (size_t)gm * N + gn) = v4u{s0[0], s1[0], s0[1], s1[1]};
+        }
     }
-    __syncthreads();  // every wave is done reading the last stage (or the partial sums)
-    uint16_t* st = reinterpret_cast<uint16_t*>(smem) + wave * WTM * WTN;
-    tile::store_tile32_bf16<WTM, WTN>(st, lane, Y, row_w, col_w, M, N, [&](int i, int j, int r) {
-      return tile::bf16_rne(((float)acc[i][j][r] * sa_r[i][r]) * sb_c[j]);
-    }, out);
   }
 }
 
