@@ -737,6 +737,51 @@ def side_measurements(T, torch, dev) -> dict:
     return out
 
 
+def vendor_compare(T, torch, dev, reps: int = 20) -> dict:
+    """This library's masked INT8 GEMM (bf16 output, k = 0) against the vendor INT8 GEMM
+    that torch exposes (torch._int_mm: int8 x int8 -> int32, hipBLASLt on ROCm) on the
+    workloads' DiT shapes and two large squares, same operands, hot, `reps` launches
+    each between HIP events; the vendor call gets the transposed-weight view it needs."""
+    import tabit_synth as S
+    shapes = {"pixart qkv": (4096, 3456, 1152), "pixart out": (4096, 1152, 1152),
+              "pixart mlp-up": (4096, 4608, 1152), "pixart mlp-down": (4096, 1152, 4608),
+              "sana qkv": (1024, 6720, 2240), "sdxl h640 geglu-up": (16384, 5120, 640),
+              "cogvideox mlp-up": (17776, 7680, 1920), "cogvideox mlp-down": (17776, 1920, 7680),
+              "square 8192": (8192, 8192, 8192), "16384x16384x4096": (16384, 16384, 4096)}
+    ctx = T.Context()
+    out = {}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+    for name, (M, N, K) in shapes.items():
+        xq = torch.from_numpy(S.gen_int8((M, K), seed=1)).to(dev)
+        wq = torch.from_numpy(S.gen_int8((N, K), seed=2)).to(dev)
+        sa = torch.from_numpy(S.gen_scales(M, seed=3)).to(dev)
+        sw = torch.from_numpy(S.gen_scales(N, seed=4)).to(dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ours = timed(lambda: ctx.masked_qgemm(xq, sa, wq, sw, 0, y=y))
+        wt = wq.t()
+        vendor = timed(lambda: torch._int_mm(xq, wt))
+        ops = 2 * M * N * K
+        out[name] = {"shape": [M, N, K], "tabit_us": round(ours, 2),
+                     "tabit_tops": round(ops / ours / 1e6, 1), "vendor_us": round(vendor, 2),
+                     "vendor_tops": round(ops / vendor / 1e6, 1),
+                     "tabit_over_vendor": round(vendor / ours, 3)}
+        del xq, wq, y, wt
+    ctx.close()
+    return {"mode": "vendor_compare", "reps": reps, "note": "tabit writes bf16 (scaled), "
+            "the vendor GEMM int32 (unscaled)", "shapes": out}
+
+
 def gemm_tiles(T, wl, tuned, path=0):
     """Tile shape (BM, BN) each distinct GEMM shape runs with."""
     out = {}
@@ -780,6 +825,8 @@ def main() -> int:
                     help="reuse step 0's activations at every step (same work, faster set-up)")
     ap.add_argument("--gelu-fusion", action="store_true",
                     help="only time the MLP-down input quantizer with the GELU folded in vs unfused")
+    ap.add_argument("--vendor-compare", action="store_true",
+                    help="only time the masked GEMM against the vendor INT8 GEMM (torch._int_mm)")
     ap.add_argument("--dmpq", action="store_true",
                     help="only run the CogVideoX-shaped schedule with the online INT8/4-bit selector")
     ap.add_argument("--dmpq-steps", type=int, default=0, help="denoising steps for --dmpq (0 = 50)")
@@ -855,7 +902,7 @@ def main() -> int:
     # the oracle on the host cores first: its worker processes start before this
     # process touches the GPU
     cpu = None
-    if not (args.no_cpu_baseline or args.dmpq or args.gelu_fusion):
+    if not (args.no_cpu_baseline or args.dmpq or args.gelu_fusion or args.vendor_compare):
         cpu = cpu_baseline(wl, args.cpu_rows)
         print(f"cpu_baseline done: {cpu['value']} TOPS on {cpu['cores']} processes", file=sys.stderr,
               flush=True)
@@ -868,6 +915,9 @@ def main() -> int:
         return 0
     if args.gelu_fusion:
         print(json.dumps(gelu_fusion_bench(T, torch, dev)), flush=True)
+        return 0
+    if args.vendor_compare:
+        print(json.dumps(vendor_compare(T, torch, dev)), flush=True)
         return 0
     b = wl.had_block
     L, Tn = wl.num_layers, wl.steps

@@ -26,8 +26,9 @@
 // rate with a few independent accumulators per wave), with the weight fragment
 // as its first operand so that every lane ends with runs of four consecutive
 // output columns.  The epilogue scales in fp32 (the tile's scales were copied
-// into LDS at the start), rounds pairs to bf16 with the packed conversion and
-// stores 8 bytes per run straight from registers: no transpose, no barrier.
+// into LDS at the start), rounds pairs to bf16 with the packed conversion,
+// writes each pair of runs to its wave's LDS staging as 16 bytes, from where
+// rows go out as full-line nontemporal stores.
 //
 // K split inside the workgroup (KW > 1), for shapes whose tiles fit in one
 // round over the CUs (a few tokens, or a long K): KW groups of WM x WN waves
@@ -70,14 +71,16 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
   static_assert(NW * KW * 64 <= 1024, "at most 1024 threads per workgroup");
   static_assert(NST == 2 || (BM % (8 * NW) == 0 && BN % (8 * NW) == 0),
                 "deeper rings count copies per wave: every wave copies the same share");
-  // the ring (the K groups' partial sums reuse it), then the tile's scales when they fit:
+  // the ring (the K groups' partial sums and the epilogue's bf16 staging reuse it,
+  // the staging extending it where larger), then the tile's scales when they fit:
   // SA of its BM rows, SB of its BN columns (padded to whole waves of 64 entries)
   constexpr int RING = KW * NST * STAGE;
+  constexpr int BASE = RING > BM * BN * 2 ? RING : BM * BN * 2;
   constexpr int NSCALE = BM + (BN + 63) / 64 * 64;
-  constexpr bool SCALES_IN_LDS = RING + NSCALE * 4 <= 160 * 1024;
+  constexpr bool SCALES_IN_LDS = BASE + NSCALE * 4 <= 160 * 1024;
   static_assert(BM % 64 == 0 && NSCALE / 64 <= NW * KW, "one scale wave per 64 entries");
-  __shared__ __attribute__((aligned(1024))) int8_t smem[RING + (SCALES_IN_LDS ? NSCALE * 4 : 0)];
-  float* s_scale = reinterpret_cast<float*>(smem + RING);
+  __shared__ __attribute__((aligned(1024))) int8_t smem[BASE + (SCALES_IN_LDS ? NSCALE * 4 : 0)];
+  float* s_scale = reinterpret_cast<float*>(smem + BASE);
 
   int tm, tn;
   tile::tile_coords<4>(tiles_m, tiles_n, tm, tn);
@@ -260,11 +263,10 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
   // of four registers; lanes l and l + 32 hold the two halves of an 8-column run.
   // int32 results go out as 16 bytes per run.  bf16 results: each run is packed
   // to two words, then one v_permlane32_swap per word pairs runs g and g + 1, so
-  // lane l holds run g's 8 columns and lane l + 32 run g + 1's: 16-byte stores
-  // straight from registers, no staging, no barrier.  (Plain stores: 8-byte or
-  // nontemporal pieces of a line measured 1.1x and 3x slower.)
-  if (!out) return;
-  if (ACC != nullptr) {
+  // lane l holds run g's 8 columns and lane l + 32 run g + 1's, written to the
+  // LDS staging as 16 bytes (8 writes per lane for a 64 x 64 wave tile instead
+  // of 64 two-byte ones).
+  if (ACC != nullptr && out) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -279,6 +281,15 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
         }
   }
   if (Y != nullptr) {
+    // stage the wave's bf16 tile in LDS (its own WTM x WTN region over the ring:
+    // every wave must be done reading the last stage or the partial sums first),
+    // one 16-byte write per run pair, then read it back row by row for full-line
+    // nontemporal stores (128 contiguous bytes per row per 64 columns: partial-line
+    // or write-allocating stores measured up to 3x and 1.3x slower)
+    constexpr int CH = WTN / 8, SW = CH & -CH;   // 16-byte chunks per staged row; swizzle span
+    __syncthreads();
+    if (!out) return;                            // K groups 1.. hold no output
+    uint16_t* st = reinterpret_cast<uint16_t*>(smem) + wave * WTM * WTN;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       v2u pk[FM][4];
@@ -304,14 +315,27 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
       for (int g = 0; g < 4; g += 2)
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-          // lanes 32-63 of run g's words trade places with lanes 0-31 of run g + 1's
+          // lanes 32-63 of run g's words trade places with lanes 0-31 of run g + 1's:
+          // lane l then holds the 8 columns of run g + l / 32 of its row
           const auto s0 = __builtin_amdgcn_permlane32_swap(pk[i][g][0], pk[i][g + 1][0], false, false);
           const auto s1 = __builtin_amdgcn_permlane32_swap(pk[i][g][1], pk[i][g + 1][1], false, false);
-          const int gm = row_w + i * 32 + (lane & 31);
-          const int gn = col_w + j * 32 + (g + khalf) * 8;
-          if (gm < M && gn < N)
-            *reinterpret_cast<v4u*>(Y + (size_t)gm * N + gn) = v4u{s0[0], s1[0], s0[1], s1[1]};
+          const int lr = i * 32 + (lane & 31);
+          const int ch = (j * 32 + (g + khalf) * 8) >> 3;
+          *reinterpret_cast<v4u*>(st + lr * WTN + ((ch ^ (lr & (SW - 1))) << 3)) =
+              v4u{s0[0], s1[0], s0[1], s1[1]};
         }
+    }
+    // the region is the wave's own: LDS operations of one wave complete in order
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int it = 0; it < WTM * CH / 64; ++it) {
+      const int idx = it * 64 + lane;
+      const int lr = idx / CH, ch = idx % CH;
+      const int gm = row_w + lr, gn = col_w + ch * 8;
+      const v4u v = *reinterpret_cast<const v4u*>(st + lr * WTN + ((ch ^ (lr & (SW - 1))) << 3));
+      if (gm < M && gn < N) __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(Y + (size_t)gm * N + gn));
     }
   }
 }
