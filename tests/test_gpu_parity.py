@@ -62,7 +62,8 @@ def edge_activation(M, K, seed):
 
 
 # ------------------------------------------------------------ quantizers
-QUANT_SHAPES = [(1, 32), (17, 128), (33, 1024), (64, 1152), (9, 1920), (129, 2240), (300, 4608), (37, 5600),
+QUANT_SHAPES = [(1, 32), (17, 128), (33, 1024), (64, 1152), (9, 640), (77, 768), (130, 1280), (4099, 1152),
+                (9, 1920), (129, 2240), (300, 4608), (37, 5600),
                 (23, 6400), (5, 7680)]
 
 

@@ -25,7 +25,10 @@ namespace tabit {
 namespace {
 
 using tile::v4i;
+using tile::v4u;
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int RB = 128;   // packed bytes per row per stage (256 elements)
@@ -168,14 +171,18 @@ gemm_mxfp4_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ AE,
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const v8i b8 = {b[cur][j][0], b[cur][j][1], b[cur][j][2], b[cur][j][3], 0, 0, 0, 0};
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc[i][j], 4, 4, 0,
-                                                                       ea[cur][i], 0, eb[cur][j]);
+          // the weights as the first operand: lanes end with runs of four output columns
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b8, a8, acc[i][j], 4, 4, 0,
+                                                                       eb[cur][j], 0, ea[cur][i]);
         }
       }
     }
     if (more) store_scales((kt + 1) & 1);
   }
 
+  // Block (i, j) holds Y^T: lane l, register r is row i*32 + l%32 and column
+  // j*32 + (r/4)*8 + (l/32)*4 + r%4 of the wave tile (four consecutive columns
+  // per group of four registers), as in the INT8 GEMM's epilogue.
   const int row_w = m0 + wm * WTM, col_w = n0 + wn * WTN;
   if (ACC != nullptr) {
 #pragma unroll
@@ -183,18 +190,56 @@ gemm_mxfp4_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ AE,
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int gm = row_w + i * 32 + (r >> 2) * 8 + khalf * 4 + (r & 3);
-          const int gn = col_w + j * 32 + (lane & 31);
-          if (gm < M && gn < N) ACC[(size_t)gm * N + gn] = acc[i][j][r];
+        for (int g = 0; g < 4; ++g) {
+          const int gm = row_w + i * 32 + (lane & 31);
+          const int gn = col_w + j * 32 + g * 8 + khalf * 4;
+          if (gm < M && gn < N)
+            *reinterpret_cast<float4*>(ACC + (size_t)gm * N + gn) =
+                make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                            acc[i][j][4 * g + 3]);
         }
   }
   if (Y != nullptr) {
+    // bf16 pairs by the packed conversion; v_permlane32_swap pairs runs g and g + 1
+    // so each lane holds 8 columns of its row, written to the wave's LDS staging as
+    // 16 bytes; rows leave as full-line nontemporal stores
+    constexpr int CH = WTN / 8, SW = CH & -CH;
     __syncthreads();  // every wave is done reading the last stage
     uint16_t* st = reinterpret_cast<uint16_t*>(smem) + wave * WTM * WTN;
-    tile::store_tile32_bf16<WTM, WTN>(st, lane, Y, row_w, col_w, M, N, [&](int i, int j, int r) {
-      return tile::bf16_rne(acc[i][j][r] * out_scale);
-    });
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        unsigned pk[4][2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const v2f lo = v2f{acc[i][j][4 * g] * out_scale, acc[i][j][4 * g + 1] * out_scale};
+          const v2f hi = v2f{acc[i][j][4 * g + 2] * out_scale, acc[i][j][4 * g + 3] * out_scale};
+          pk[g][0] = __builtin_bit_cast(unsigned, __builtin_convertvector(lo, v2bf));
+          pk[g][1] = __builtin_bit_cast(unsigned, __builtin_convertvector(hi, v2bf));
+        }
+#pragma unroll
+        for (int g = 0; g < 4; g += 2) {
+          const auto s0 = __builtin_amdgcn_permlane32_swap(pk[g][0], pk[g + 1][0], false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(pk[g][1], pk[g + 1][1], false, false);
+          const int lr = i * 32 + (lane & 31);
+          const int ch = (j * 32 + (g + khalf) * 8) >> 3;
+          *reinterpret_cast<v4u*>(st + lr * WTN + ((ch ^ (lr & (SW - 1))) << 3)) =
+              v4u{s0[0], s1[0], s0[1], s1[1]};
+        }
+      }
+    // the region is the wave's own: LDS operations of one wave complete in order
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int it = 0; it < WTM * CH / 64; ++it) {
+      const int idx = it * 64 + lane;
+      const int lr = idx / CH, ch = idx % CH;
+      const int gm = row_w + lr, gn = col_w + ch * 8;
+      const v4u v = *reinterpret_cast<const v4u*>(st + lr * WTN + ((ch ^ (lr & (SW - 1))) << 3));
+      if (gm < M && gn < N) __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(Y + (size_t)gm * N + gn));
+    }
   }
 }
 
