@@ -9,15 +9,21 @@
 // natively (32-element blocks, E8M0 scales applied inside the MFMA).
 //
 // v_mfma_scale_f32_32x32x64_f8f6f4 with both operands E2M1: lane l supplies
-// 16 bytes = 32 consecutive K elements of row (l % 32) -- exactly one MX block
-// -- and that block's E8M0 byte as its scale operand.  The tile skeleton is
-// the INT8 GEMM's: packed operand stages of 128 bytes (256 elements) copied
-// global->LDS by buffer loads into a double-buffered ring, one barrier per
-// stage; each wave reads the next K-step's fragments and scale bytes from LDS
-// while the matrix cores work on the current one.  The 8 scale bytes per row
-// and stage go through registers (two words per row) into a small LDS table
-// next to the data (their loads are issued before the stage's copies so
-// waiting for them never waits for the copies).
+// 16 bytes = 32 K elements of row (l % 32) -- exactly one MX block -- and a
+// scale word whose byte opsel is that block's E8M0 scale.  Operands move
+// global->LDS in stages of 128 packed bytes (256 elements) per row by buffer
+// loads straight into LDS, through a ring of two or three stages with the
+// next one or two in flight while the matrix cores work on the current one;
+// a stage's 8 scale bytes per row come along as a small table in LDS (4-byte
+// copies, when K is a multiple of 128) or, otherwise, as per-lane byte loads
+// into registers.  Each wave reads the next K-step's fragments from LDS while
+// the matrix cores work on the current one.
+//
+// What keeps the copies in flight: one LDS array (with several, the compiler
+// orders every read of an array after all copies into it still in flight), a
+// barrier that waits only for LDS traffic (the copies a stage needs are waited
+// for explicitly, by count), and every iteration issuing its stage, also past
+// the end of K, so the count is the same on every path.
 #include "tabit_internal.h"
 #include "tile_common.h"
 
@@ -34,24 +40,57 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int RB = 128;   // packed bytes per row per stage (256 elements)
 constexpr int SPR = 8;    // scale bytes per row per stage
 
-template <int BM, int BN, int WM, int WN>
+// E2M1 x E2M1 block-scaled MFMA; byte sel (0..3) of each scale word is the
+// scale of the lane's block (sel is a constant once the K-step loop unrolls)
+__device__ __forceinline__ v16f mfma_fp4(int sel, v8i a, v8i b, v16f c, int sa, int sb) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 1, sa, 1, sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 2, sa, 2, sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 3, sa, 3, sb);
+  }
+}
+
+// One 4-byte copy of a stage's scale table: 32 rows (two lanes per row) of
+// operand rows row0 + r, bytes g .. g + 3 of each (g < row length or nothing).
+__device__ __forceinline__ void copy_scale_rows(__amdgpu_buffer_rsrc_t rs, int8_t* dst, int r,
+                                                int rows_valid, int row0, int ksb, int g) {
+  const unsigned off = r < rows_valid && g < ksb ? (unsigned)(row0 + r) * ksb + g : tile::kOOB;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (tile::lds_ptr_t)dst, 4, off, 0, 0, 0);
+}
+
+template <int BM, int BN, int WM, int WN, int NST, bool SW4>
 __global__ void __launch_bounds__(WM* WN * 64)
 gemm_mxfp4_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ AE,
                   const uint8_t* __restrict__ B, const uint8_t* __restrict__ BE, int M, int N,
                   int K, float out_scale, uint16_t* __restrict__ Y, float* __restrict__ ACC,
                   int tiles_m, int tiles_n, const uint8_t* __restrict__ gate) {
   if (gate != nullptr && *gate != 1) return;   // device-selected format is not MXFP4
-  constexpr int NT = WM * WN * 64, NW = WM * WN;
+  constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int KS = RB / 32;                     // 32-byte (64-element) K-steps per stage
   constexpr int DATA = (BM + BN) * RB;
-  constexpr int SCL = (BM + BN) * SPR;
+  constexpr int DPW = DATA / 1024 / NW;           // copies per wave per stage
+  // a stage's scale table: BM + BN rows of 8 bytes (the stage's 32-element
+  // blocks), copied 32 rows per instruction (whole instructions per wave, the
+  // last ones past the table reading out of range into padding); without
+  // 4-byte aligned scale words each lane loads its rows' bytes into registers
+  constexpr int SIN = (BM + BN) / 32;
+  constexpr int SCW = SW4 ? (SIN + NW - 1) / NW : 0;
+  constexpr int SCL = SCW * NW * 256;             // LDS bytes of a stage's scale table
+  constexpr int SPW = SW4 ? SCW : (FM + FN) * 4;  // scale loads per wave per stage
+  constexpr int PER_STAGE = DPW + SPW;
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold whole 32x32 blocks");
-  // the two stages, or the bf16 staging of the epilogue when that is larger
-  constexpr int SMEM = 2 * DATA > BM * BN * 2 ? 2 * DATA : BM * BN * 2;
-  __shared__ __attribute__((aligned(1024))) int8_t smem[SMEM];
-  __shared__ __attribute__((aligned(16))) uint8_t sscale[2][SCL];
+  static_assert(NST == 2 || NST == 3, "two or three LDS stages");
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0,
+                "the waits count loads per wave: every wave copies the same share");
+  static_assert((NST - 1) * PER_STAGE < 64, "vmcnt range");
+  // the stages (or the bf16 staging of the epilogue when that is larger), then
+  // the stages' scale tables
+  constexpr int SMEM = NST * DATA > BM * BN * 2 ? NST * DATA : BM * BN * 2;
+  static_assert(SMEM + NST * SCL <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) int8_t smem[SMEM + NST * SCL];
 
   int tm, tn;
   tile::tile_coords<4>(tiles_m, tiles_n, tm, tn);
@@ -63,57 +102,75 @@ gemm_mxfp4_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ AE,
   const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
   const auto rsa = tile::make_rsrc(A, (unsigned)M * (unsigned)KB);
   const auto rsb = tile::make_rsrc(B, (unsigned)N * (unsigned)KB);
+  const auto rsae = tile::make_rsrc(AE, (unsigned)M * (unsigned)KSB);
+  const auto rsbe = tile::make_rsrc(BE, (unsigned)N * (unsigned)KSB);
 
-  // Scale table of a stage: row r (0..BM-1 from AE, then BN rows from BE)
-  // holds its 8 scale bytes; a thread moves whole rows, as two words when the
-  // row's bytes are 4-byte aligned and all inside K (else byte by byte, 127 =
-  // 2^0 past the end or past the last row).
-  constexpr int RPT = (BM + BN + NT - 1) / NT;   // scale rows per thread
-  static_assert(SPR == 8, "two words per row and stage");
-  const bool words = (KSB & 3) == 0;
-  uint32_t sreg[RPT][2];
-  auto load_scales = [&](int kt) {
+  // Lane l reads rows ra0 + 32 i of A and rb0 + 32 j of B.  At K-step ks of a
+  // stage the lanes of half h = l / 32 take 16-byte chunk 4 h + ks (32 FP4
+  // values, one MX block), the same chunk for both operands, so a lane's four
+  // block scales of a stage are the 4 consecutive scale bytes 4 h .. 4 h + 3 of
+  // the stage's 8; byte ks of that word is the MFMA's scale at K-step ks.
+  const int ra0 = wm * WTM + (lane & 31), rb0 = wn * WTN + (lane & 31);
+  const int khalf = lane >> 5;
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "rows ra0 + 32 i and rb0 + 32 j share a swizzle");
+  const int sw = tile::swz<RB>(ra0);
+  const int nk = (KB + RB - 1) / RB;
+
+  // scale-word offsets of the lane's rows (past M or N: out of range, reads 0)
+  unsigned eoff[FM + FN];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int r = i * NT + tid;
-      const uint8_t* src = nullptr;
-      if (r < BM) {
-        if (r < rows_a) src = AE + (size_t)(m0 + r) * KSB;
-      } else if (r < BM + BN && r - BM < rows_b) {
-        src = BE + (size_t)(n0 + r - BM) * KSB;
-      }
-      const int g0 = kt * SPR;
-      uint32_t lo = 0x7F7F7F7Fu, hi = 0x7F7F7F7Fu;
-      if (src != nullptr) {
-        if (words && g0 + SPR <= KSB) {
-          lo = *reinterpret_cast<const uint32_t*>(src + g0);
-          hi = *reinterpret_cast<const uint32_t*>(src + g0 + 4);
-        } else {
-          lo = hi = 0u;
+  for (int i = 0; i < FM; ++i)
+    eoff[i] = ra0 + i * 32 < rows_a ? (unsigned)(m0 + ra0 + i * 32) * KSB + khalf * 4 : tile::kOOB;
 #pragma unroll
-          for (int j = 0; j < SPR; ++j) {
-            const uint32_t v = g0 + j < KSB ? src[g0 + j] : 127u;
-            if (j < 4) lo |= v << (8 * j);
-            else hi |= v << (8 * (j - 4));
-          }
-        }
-      }
-      sreg[i][0] = lo;
-      sreg[i][1] = hi;
+  for (int j = 0; j < FN; ++j)
+    eoff[FM + j] = rb0 + j * 32 < rows_b ? (unsigned)(n0 + rb0 + j * 32) * KSB + khalf * 4
+                                         : tile::kOOB;
+  // Scale bytes past the row's end read as 0 (E8M0 2^-127; their FP4 values are
+  // zeros).  With K a multiple of 128 a lane's word lies wholly inside or
+  // outside the row and is one load; otherwise it comes as 4 byte loads, kept
+  // apart until the stage is used (assembling them at once would wait for them).
+  typedef int Scales[FM + FN][SW4 ? 1 : 4];
+  auto load_scales = [&](int kt, Scales& e) {
+    const int g = kt * SPR + khalf * 4;
+#pragma unroll
+    for (int r = 0; r < FM + FN; ++r) {
+      const auto rs = r < FM ? rsae : rsbe;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        e[r][q] = __builtin_amdgcn_raw_buffer_load_b8(rs, g + q < KSB ? eoff[r] + kt * SPR + q : tile::kOOB,
+                                                      0, 0);
     }
   };
-  auto store_scales = [&](int buf) {
+  auto scale_word = [&](const Scales& e, int r) {
+    return e[r][0] | (e[r][1] << 8) | (e[r][2] << 16) | (e[r][3] << 24);
+  };
+  // 4-byte copies into the stage's table: lane L of copy j moves bytes
+  // 4 (L % 2) .. 4 (L % 2) + 3 of row 32 j + L / 2 (rows of A, then of B)
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto copy_scales = [&](int kt, int buf) {
+    const int g = kt * SPR + (lane & 1) * 4;
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int r = i * NT + tid;
-      if (r < BM + BN)
-        *reinterpret_cast<uint2*>(&sscale[buf][r * SPR]) = make_uint2(sreg[i][0], sreg[i][1]);
+    for (int q = 0; q < SCW; ++q) {
+      const int j = q * NW + wave_u;   // wave-uniform
+      int8_t* dst = smem + SMEM + buf * SCL + j * 256;
+      if (j * 32 < BM)
+        copy_scale_rows(rsae, dst, j * 32 + (lane >> 1), rows_a, m0, KSB, g);
+      else   // rows past BN in the padding copies
+        copy_scale_rows(rsbe, dst, j * 32 - BM + (lane >> 1), rows_b, n0, KSB, g);
     }
   };
-  auto issue = [&](int kt) {
-    int8_t* dst = smem + (kt & 1) * DATA;
+  // A stage's loads: its scale words, then its copies into LDS buffer buf.  The
+  // waits below count on every load of a stage being issued before any load
+  // of the next (vmcnt retires loads in issue order); the compiler fences keep
+  // that order.
+  auto issue = [&](int kt, int buf, Scales& e) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if constexpr (SW4) copy_scales(kt, buf);
+    else load_scales(kt, e);
+    int8_t* dst = smem + buf * DATA;
     tile::dma_stage<BM, NW, RB>(rsa, dst, m0, rows_a, KB, kt * RB, wave, lane);
     tile::dma_stage<BN, NW, RB>(rsb, dst + BM * RB, n0, rows_b, KB, kt * RB, wave, lane);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
   };
 
   v16f acc[FM][FN];
@@ -122,62 +179,65 @@ gemm_mxfp4_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ AE,
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = v16f{};
 
-  const int ra0 = wm * WTM + (lane & 31), rb0 = wn * WTN + (lane & 31);
-  const int khalf = lane >> 5;
-  const int nk = (KB + RB - 1) / RB;
-
-  load_scales(0);
-  issue(0);
-  store_scales(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    tile::wait_vmcnt0();
-    __syncthreads();
-    const bool more = kt + 1 < nk;
-    if (more) {
-      load_scales(kt + 1);     // before the copies: waiting on these never waits on the copies
-      issue(kt + 1);
-    }
-    const int8_t* sa = smem + (kt & 1) * DATA;
-    const int8_t* sb = sa + BM * RB;
-    const uint8_t* ssa = sscale[kt & 1];
-    const uint8_t* ssb = ssa + BM * SPR;
-    // fragments and scale bytes of K-step ks + 1 are read from LDS while the
-    // matrix cores work on K-step ks
-    v4i a[2][FM], b[2][FN];
-    int ea[2][FM], eb[2][FN];
-    auto load = [&](int ks, int buf) {
-      const int c = ks * 2 + khalf;     // 16-byte chunk = one 32-element MX block
+  // Stage t's scales in registers e[t % NST], its data in LDS buffer t % NST.
+  // Every iteration issues the stage NST-1 ahead, also past the last one
+  // (out-of-range loads return zeros into a buffer no one reads), so every
+  // path carries the same loads in flight: at the top of iteration kt only
+  // the NST-2 stages after kt may still be pending.
+  Scales e[NST];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = ra0 + i * 32;
-        a[buf][i] = *reinterpret_cast<const v4i*>(sa + tile::lds_off<RB>(r, c));
-        ea[buf][i] = ssa[r * SPR + c];
+  for (int t = 0; t < NST - 1; ++t) issue(t, t, e[t]);
+  for (int k0 = 0; k0 < nk; k0 += NST) {
+#pragma unroll
+    for (int s = 0; s < NST; ++s) {
+      const int kt = k0 + s;
+      if (kt >= nk) break;   // uniform
+      tile::wait_vmcnt<(NST - 2) * PER_STAGE>();
+      tile::lds_barrier();   // stage kt visible to all; the buffer of stage kt-1 free
+      issue(kt + NST - 1, (s + NST - 1) % NST, e[(s + NST - 1) % NST]);
+      int ew[FM + FN];
+      if constexpr (SW4) {
+        const int8_t* ss = smem + SMEM + s * SCL + khalf * 4;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) ew[i] = *reinterpret_cast<const int*>(ss + (ra0 + i * 32) * SPR);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          ew[FM + j] = *reinterpret_cast<const int*>(ss + (BM + rb0 + j * 32) * SPR);
+      } else {
+#pragma unroll
+        for (int r = 0; r < FM + FN; ++r) ew[r] = scale_word(e[s], r);
       }
+      const int8_t* sa = smem + s * DATA + ra0 * RB;
+      const int8_t* sb = smem + s * DATA + BM * RB + rb0 * RB;
+      // fragments of K-step ks + 1 are read from LDS while the matrix cores
+      // work on K-step ks; rows ra0 + 32 i and rb0 + 32 j share one swizzle,
+      // so a K-step's chunk offset is one value for both operands
+      v4i a[2][FM], b[2][FN];
+      auto load = [&](int ks, int buf) {
+        const int co = ((khalf * 4 + ks) ^ sw) << 4;
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int r = rb0 + j * 32;
-        b[buf][j] = *reinterpret_cast<const v4i*>(sb + tile::lds_off<RB>(r, c));
-        eb[buf][j] = ssb[r * SPR + c];
-      }
-    };
-    load(0, 0);
+        for (int i = 0; i < FM; ++i) a[buf][i] = *reinterpret_cast<const v4i*>(sa + i * 32 * RB + co);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < KS) load(ks + 1, cur ^ 1);
+        for (int j = 0; j < FN; ++j) b[buf][j] = *reinterpret_cast<const v4i*>(sb + j * 32 * RB + co);
+      };
+      load(0, 0);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const v8i a8 = {a[cur][i][0], a[cur][i][1], a[cur][i][2], a[cur][i][3], 0, 0, 0, 0};
+      for (int ks = 0; ks < KS; ++ks) {
+        const int cur = ks & 1;
+        if (ks + 1 < KS) load(ks + 1, cur ^ 1);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const v8i b8 = {b[cur][j][0], b[cur][j][1], b[cur][j][2], b[cur][j][3], 0, 0, 0, 0};
-          // the weights as the first operand: lanes end with runs of four output columns
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b8, a8, acc[i][j], 4, 4, 0,
-                                                                       eb[cur][j], 0, ea[cur][i]);
+        for (int i = 0; i < FM; ++i) {
+          const v8i a8 = {a[cur][i][0], a[cur][i][1], a[cur][i][2], a[cur][i][3], 0, 0, 0, 0};
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const v8i b8 = {b[cur][j][0], b[cur][j][1], b[cur][j][2], b[cur][j][3], 0, 0, 0, 0};
+            // the weights as the first operand: lanes end with runs of four
+            // output columns
+            acc[i][j] = mfma_fp4(ks, b8, a8, acc[i][j], ew[FM + j], ew[i]);
+          }
         }
       }
     }
-    if (more) store_scales((kt + 1) & 1);
   }
 
   // Block (i, j) holds Y^T: lane l, register r is row i*32 + l%32 and column
@@ -244,36 +304,40 @@ gemm_mxfp4_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ AE,
 }
 
 struct CfgDesc {
-  int bm, bn, wm, wn;
+  int bm, bn, wm, wn, nst;
   float rate;   // relative throughput per CU on its tiles (fitted to MI355X sweeps)
 };
-// Eight waves of 32 x 64 or 64 x 64 on the large tiles (2-6% faster on the
-// CogVideoX shapes than four waves of 64 x 64); 12- and 16-wave tiles with
-// 256 rows spill here.  Rates: median per-tile rates of a graph-replayed sweep
-// over seven DiT shapes.
-// index, BM, BN, WM, WN, rate
-#define TABIT_MX_CONFIGS(X)       \
-  X(0, 128, 128, 4, 2, 1.00f)     \
-  X(1, 256, 128, 4, 2, 1.02f)     \
-  X(2, 128, 64, 2, 2, 0.84f)      \
-  X(3, 64, 64, 2, 2, 0.69f)
-#define TABIT_DESC(I, BM, BN, WM, WN, RATE) {BM, BN, WM, WN, RATE},
+// Eight waves of 32 x 64 or 64 x 64 on the large tiles.  The 256 x 128 tile
+// runs three stages (two in flight; 156 KB of LDS), the others two.  Rates:
+// per-CU tile rates measured on the CogVideoX MLP-up, MLP-down and QKV linears
+// (17776 x {7680, 1920, 5760} x {1920, 7680, 1920}) and PixArt's MLP-up
+// (4096 x 4608 x 1152): the 256 x 128 tile runs 1.09-1.25x the 128 x 128
+// tile's rate per CU on the large shapes, equal on the small one.
+// index, BM, BN, WM, WN, LDS stages, rate
+#define TABIT_MX_CONFIGS(X)          \
+  X(0, 128, 128, 4, 2, 2, 1.00f)     \
+  X(1, 256, 128, 4, 2, 3, 1.15f)     \
+  X(2, 128, 64, 2, 2, 2, 0.84f)      \
+  X(3, 64, 64, 2, 2, 2, 0.69f)
+#define TABIT_DESC(I, BM, BN, WM, WN, NST, RATE) {BM, BN, WM, WN, NST, RATE},
 constexpr CfgDesc kCfgs[] = {TABIT_MX_CONFIGS(TABIT_DESC)};
 #undef TABIT_DESC
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int NST>
 hipError_t launch_cfg(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq, const uint8_t* we,
                       int M, int N, int K, float out_scale, uint16_t* y, float* acc,
                       hipStream_t s, hipEvent_t ev0, hipEvent_t ev1, const uint8_t* gate) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const dim3 grid(tiles_m * tiles_n), block(WM * WN * 64);
+  // a stage's scale words are 4-byte aligned when K is a multiple of 128
+  auto kern = K % 128 == 0 ? gemm_mxfp4_kernel<BM, BN, WM, WN, NST, true>
+                           : gemm_mxfp4_kernel<BM, BN, WM, WN, NST, false>;
   if (ev0 != nullptr || ev1 != nullptr)   // timestamps of this dispatch itself
-    hipExtLaunchKernelGGL(gemm_mxfp4_kernel<BM, BN, WM, WN>, grid, block, 0, s, ev0, ev1, 0, xq, xe,
-                          wq, we, M, N, K, out_scale, y, acc, tiles_m, tiles_n, gate);
+    hipExtLaunchKernelGGL(kern, grid, block, 0, s, ev0, ev1, 0, xq, xe, wq, we, M, N, K, out_scale,
+                          y, acc, tiles_m, tiles_n, gate);
   else
-    gemm_mxfp4_kernel<BM, BN, WM, WN><<<grid, block, 0, s>>>(xq, xe, wq, we, M, N, K, out_scale, y,
-                                                             acc, tiles_m, tiles_n, gate);
+    kern<<<grid, block, 0, s>>>(xq, xe, wq, we, M, N, K, out_scale, y, acc, tiles_m, tiles_n, gate);
   return hipGetLastError();
 }
 
@@ -308,10 +372,10 @@ hipError_t launch_gemm_mxfp4(int cfg, const uint8_t* xq, const uint8_t* xe, cons
                              const uint8_t* we, int M, int N, int K, float out_scale, uint16_t* y,
                              float* acc, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1,
                              const uint8_t* gate) {
-#define TABIT_CASE(I, BM, BN, WM, WN, RATE) \
-  case I:                                           \
-    return launch_cfg<BM, BN, WM, WN>(xq, xe, wq, we, M, N, K, out_scale, y, acc, stream, \
-                                      ev0, ev1, gate);
+#define TABIT_CASE(I, BM, BN, WM, WN, NST, RATE) \
+  case I:                                                \
+    return launch_cfg<BM, BN, WM, WN, NST>(xq, xe, wq, we, M, N, K, out_scale, y, acc, stream, \
+                                           ev0, ev1, gate);
   switch (cfg) {
     TABIT_MX_CONFIGS(TABIT_CASE)
     default: return hipErrorInvalidValue;

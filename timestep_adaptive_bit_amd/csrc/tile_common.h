@@ -73,6 +73,20 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ void wait_vmcnt0() { wait_vmcnt<0>(); }
 
+// Workgroup barrier for a ring of LDS stages filled by buffer loads into LDS.
+// __syncthreads() (its release fence) also waits for every vector-memory load
+// in flight, those copies included, which would drain the stages the ring
+// keeps in flight.  Here each wave waits only for its own LDS reads and writes
+// (a buffer's last readers are done before anyone refills it); the copies a
+// stage needs are waited for by count (wait_vmcnt) before the barrier.  The
+// signal fences keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt at their maxima
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
