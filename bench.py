@@ -227,6 +227,27 @@ def single_gemm(shape, reps: int) -> None:
     print(json.dumps({"single_gemm": [M, N, K], "config": cfg, "launches": reps}))
 
 
+def single_mxfp4(shape, reps: int) -> None:
+    """`reps` launches of one MXFP4 GEMM (M, N, K, tile config) on seeded
+    synthetic FP4 codes and E8M0 scales, for counter passes over a single kernel."""
+    import torch
+    import timestep_adaptive_bit_amd as T
+    M, N, K, cfg = shape
+    ctx = T.Context()
+    g = torch.Generator(device="cuda:0").manual_seed(3)
+    xf = torch.randint(0, 256, (M, K // 2), dtype=torch.uint8, device="cuda:0", generator=g)
+    xe = torch.randint(117, 137, (M, K // 32), dtype=torch.uint8, device="cuda:0", generator=g)
+    wf = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device="cuda:0", generator=g)
+    we = torch.randint(117, 137, (N, K // 32), dtype=torch.uint8, device="cuda:0", generator=g)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    ctx.set_option(T.OPT_MXFP4_CONFIG, cfg)
+    for _ in range(reps):
+        ctx.mxfp4_qgemm(xf, xe, wf, we, 1.0 / 32, y=y)
+    torch.cuda.synchronize()
+    ctx.close()
+    print(json.dumps({"single_mxfp4": [M, N, K], "config": cfg, "launches": reps}))
+
+
 def summarize_pmc(dirs) -> None:
     """Mean of every collected counter per kernel over the rocprofv3 --pmc
     databases under `dirs` (one pass per directory), with the mean duration."""
@@ -267,6 +288,8 @@ def summarize_pmc(dirs) -> None:
         if "SQ_LDS_IDX_ACTIVE" in m and m["SQ_LDS_IDX_ACTIVE"]:
             print(f"  -> LDS bank-conflict cycles per LDS-active cycle "
                   f"{m.get('SQ_LDS_BANK_CONFLICT', 0) / m['SQ_LDS_IDX_ACTIVE']:.4f}")
+        if "SQ_INSTS_VALU_MFMA_MOPS_F6F4" in m:
+            print(f"  -> FP4 MFMA flops executed {m['SQ_INSTS_VALU_MFMA_MOPS_F6F4'] * 512 / 1e9:.2f} G")
         if "SQ_INSTS_VALU_MFMA_MOPS_I8" in m:
             print(f"  -> INT8 MFMA ops executed {m['SQ_INSTS_VALU_MFMA_MOPS_I8'] * 512 / 1e9:.2f} G; "
                   f"LDS bytes read {m.get('SQ_INSTS_LDS_LOAD_BANDWIDTH', 0) * 64 / 1e9:.2f} GB")
@@ -852,12 +875,17 @@ def main() -> int:
                     default=None, help="only print MFMA and quantizer HBM counter evidence")
     ap.add_argument("--single-gemm", nargs=4, type=int, metavar=("M", "N", "K", "CFG"),
                     default=None, help="only launch one masked GEMM --reps times (counter passes)")
-    ap.add_argument("--reps", type=int, default=3, help="launches for --single-gemm")
+    ap.add_argument("--single-mxfp4", nargs=4, type=int, metavar=("M", "N", "K", "CFG"),
+                    help="only run REPS launches of one MXFP4 GEMM (for counter passes)")
+    ap.add_argument("--reps", type=int, default=3, help="launches for --single-gemm / --single-mxfp4")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR", default=None,
                     help="only print per-kernel means of the counters under the given directories")
     args = ap.parse_args()
     if args.single_gemm:
         single_gemm(args.single_gemm, args.reps)
+        return 0
+    if args.single_mxfp4:
+        single_mxfp4(args.single_mxfp4, args.reps)
         return 0
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc)

@@ -69,7 +69,7 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
   static_assert(KW >= 1 && (KW - 1) * BM * BN * 4 <= KW * NST * STAGE,
                 "the K groups' partial accumulators must fit in the LDS stages");
   static_assert(NW * KW * 64 <= 1024, "at most 1024 threads per workgroup");
-  static_assert(NST == 2 || (BM % (8 * NW) == 0 && BN % (8 * NW) == 0),
+  static_assert(NST == 2 || (BM % (1024 / RB * NW) == 0 && BN % (1024 / RB * NW) == 0),
                 "deeper rings count copies per wave: every wave copies the same share");
   // the ring (the K groups' partial sums and the epilogue's bf16 staging reuse it,
   // the staging extending it where larger), then the tile's scales when they fit:

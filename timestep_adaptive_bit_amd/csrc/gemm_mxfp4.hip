@@ -305,21 +305,24 @@ gemm_mxfp4_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ AE,
 
 struct CfgDesc {
   int bm, bn, wm, wn, nst;
-  float rate;   // relative throughput per CU on its tiles (fitted to MI355X sweeps)
+  float rate;     // relative throughput per CU on its tiles (fitted to MI355X sweeps)
+  int k128;       // only for K a multiple of 128 (its byte-scale variant spills)
 };
-// Eight waves of 32 x 64 or 64 x 64 on the large tiles.  The 256 x 128 tile
-// runs three stages (two in flight; 156 KB of LDS), the others two.  Rates:
-// per-CU tile rates measured on the CogVideoX MLP-up, MLP-down and QKV linears
-// (17776 x {7680, 1920, 5760} x {1920, 7680, 1920}) and PixArt's MLP-up
-// (4096 x 4608 x 1152): the 256 x 128 tile runs 1.09-1.25x the 128 x 128
-// tile's rate per CU on the large shapes, equal on the small one.
-// index, BM, BN, WM, WN, LDS stages, rate
-#define TABIT_MX_CONFIGS(X)          \
-  X(0, 128, 128, 4, 2, 2, 1.00f)     \
-  X(1, 256, 128, 4, 2, 3, 1.15f)     \
-  X(2, 128, 64, 2, 2, 2, 0.84f)      \
-  X(3, 64, 64, 2, 2, 2, 0.69f)
-#define TABIT_DESC(I, BM, BN, WM, WN, NST, RATE) {BM, BN, WM, WN, NST, RATE},
+// The 256 x 256 tile: sixteen waves of 64 x 64, two stages (136 KB of LDS);
+// the 256 x 128 tile: eight waves of 64 x 64, three stages (156 KB); the
+// others eight or four waves, two stages.  Rates: per-CU tile rates measured
+// on the CogVideoX MLP-up, MLP-down and QKV linears (17776 x {7680, 1920,
+// 5760} x {1920, 7680, 1920}), PixArt's MLP-up (4096 x 4608 x 1152) and
+// 8192^3: 256 x 256 runs 1.30-1.56x the 128 x 128 tile's rate per CU, 256 x
+// 128 0.97-1.21x.
+// index, BM, BN, WM, WN, LDS stages, rate, K multiple of 128 only
+#define TABIT_MX_CONFIGS(X)             \
+  X(0, 128, 128, 4, 2, 2, 1.00f, 0)     \
+  X(1, 256, 128, 4, 2, 3, 1.12f, 0)     \
+  X(2, 128, 64, 2, 2, 2, 0.84f, 0)      \
+  X(3, 64, 64, 2, 2, 2, 0.69f, 0)       \
+  X(4, 256, 256, 4, 4, 2, 1.40f, 1)
+#define TABIT_DESC(I, BM, BN, WM, WN, NST, RATE, K128) {BM, BN, WM, WN, NST, RATE, K128},
 constexpr CfgDesc kCfgs[] = {TABIT_MX_CONFIGS(TABIT_DESC)};
 #undef TABIT_DESC
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
@@ -349,14 +352,15 @@ GemmConfig mx_config(int index) { return GemmConfig{kCfgs[index].bm, kCfgs[index
 
 // Same model as the INT8 GEMM's: the busiest CU runs ceil(tiles / CUs) tiles;
 // cost = that x BM x BN / rate, rates fitted to sweeps of every configuration
-// over the 4-bit layers' shapes on MI355X.
+// over the 4-bit layers' shapes on MI355X.  Tiles marked for K a multiple of
+// 128 are left out for other K.
 int mx_config_choose(int M, int N, int K, int num_cus) {
-  (void)K;
   if (num_cus <= 0) num_cus = 256;
   int best = 0;
   double best_cost = 1e300;
   for (int i = 0; i < kNumCfgs; ++i) {
     const CfgDesc& c = kCfgs[i];
+    if (c.k128 && K % 128 != 0) continue;
     const long long tiles = (long long)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
     const long long per_cu = (tiles + num_cus - 1) / num_cus;
     const double cost = (double)per_cu * c.bm * c.bn / c.rate;
@@ -372,7 +376,7 @@ hipError_t launch_gemm_mxfp4(int cfg, const uint8_t* xq, const uint8_t* xe, cons
                              const uint8_t* we, int M, int N, int K, float out_scale, uint16_t* y,
                              float* acc, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1,
                              const uint8_t* gate) {
-#define TABIT_CASE(I, BM, BN, WM, WN, NST, RATE) \
+#define TABIT_CASE(I, BM, BN, WM, WN, NST, RATE, K128) \
   case I:                                                \
     return launch_cfg<BM, BN, WM, WN, NST>(xq, xe, wq, we, M, N, K, out_scale, y, acc, stream, \
                                            ev0, ev1, gate);

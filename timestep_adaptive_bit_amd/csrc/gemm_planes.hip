@@ -168,7 +168,7 @@ gemm_planes_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
     if (NST >= 4 && ahead >= 2) tile::wait_vmcnt<(NST >= 4 ? 2 : 0) * DPW>();
     else if (NST >= 3 && ahead >= 1) tile::wait_vmcnt<(NST >= 3 ? 1 : 0) * DPW>();
     else tile::wait_vmcnt<0>();
-    __syncthreads();   // stage kt visible to all; stage kt-1's buffer is free
+    tile::lds_barrier();   // stage kt visible to all; stage kt-1's buffer is free
     if constexpr (KW > 1) {
       if (kt >= nk) continue;   // this group's range is done (the barrier above still counts it)
     }
@@ -176,12 +176,14 @@ gemm_planes_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
     const int8_t* sa = ring + (kt % NST) * STAGE;
     const int8_t* sp = sa + SA_BYTES;
     // this lane's row of every retained plane: 4 words = the stage's 4 K-steps
-    uint4 pw[FN][8];
+    // (read as a vector type: a HIP uint4 struct load loses the access's alias
+    // information, and the compiler then orders it after every copy in flight)
+    tile::v4u pw[FN][8];
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int b = 0; b < 8; ++b)
-        if (b >= kbits) pw[j][b] = *reinterpret_cast<const uint4*>(sp + (b * BN + rb0 + j * 32) * 16);
+        if (b >= kbits) pw[j][b] = *reinterpret_cast<const tile::v4u*>(sp + (b * BN + rb0 + j * 32) * 16);
 #pragma unroll
     for (int ks = 0; ks < GPS; ++ks) {
       v4i a[FM], bw[FN];
@@ -195,8 +197,7 @@ gemm_planes_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
           if (b < kbits) continue;   // uniform: dropped planes are neither read nor merged
-          const uint4 q = pw[j][b];
-          const uint32_t x = ks == 0 ? q.x : ks == 1 ? q.y : ks == 2 ? q.z : q.w;
+          const uint32_t x = pw[j][b][ks];
           const uint32_t mb = 0x01010101u << b;
           d0 |= __builtin_amdgcn_alignbit(x, x, rot[0 - b + 7]) & mb;
           d1 |= __builtin_amdgcn_alignbit(x, x, rot[1 - b + 7]) & mb;
