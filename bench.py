@@ -1175,6 +1175,13 @@ def main() -> int:
     if int8_ops > 0 and not args.no_events:
         detail["quantizer_and_gaps_ms_per_step"] = round(ms_per_step - detail["gemm_int8_ms_per_step"]
                                                          - detail.get("gemm_mxfp4_ms_per_step", 0.0), 3)
+        if mx_ops > 0:
+            # the mixed ideal: every INT8 layer-step at the INT8 peak, every MXFP4 one at the FP4 peak
+            ideal_ms = (int8_ops / INT8_PEAK_TOPS + mx_ops / MXFP4_PEAK_TOPS) / 1e9
+            gemm_ms = detail["gemm_int8_ms_per_step"] + detail["gemm_mxfp4_ms_per_step"]
+            detail["mixed_ideal_gemm_ms_per_step"] = round(ideal_ms, 3)
+            detail["gemms_frac_of_mixed_ideal"] = round(ideal_ms / gemm_ms, 4)
+            detail["schedule_frac_of_mixed_ideal"] = round(ideal_ms / ms_per_step, 4)
     detail["quantizer"] = quant_bandwidth(ctx, T, torch, wl, xs, b, act_ws)
     if args.k_sweep:
         detail["k_sweep_us" + ("_cold" if args.cold else "")] = k_sweep(ctx, T, torch, wl, weights, xs,
