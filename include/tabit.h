@@ -452,6 +452,14 @@ int tabit_gemm_config_info(int index, int* bm, int* bn, int* k_groups);
 /* As tabit_gemm_config_info, for the MXFP4 GEMM's tile configurations. */
 int tabit_mxfp4_config_info(int index, int* bm, int* bn);
 
+/* The MXFP4 GEMM configuration the library picks for M x N x K on a device
+ * with num_cus compute units (<= 0: 256) when neither an option nor tuning
+ * forces one: the busiest-CU model (ceil(tiles / CUs) x tile area / the tile's
+ * measured rate); tiles whose variant for K not a multiple of 128 spills are
+ * left out for such K.  EINVAL for negative sizes or K < 1.  Makes no HIP
+ * call. */
+int tabit_mxfp4_config_choose(int M, int N, int K, int num_cus);
+
 /* As tabit_mxfp4_config_info, for the plane-major GEMM's tile configurations;
  * *k_groups (may be NULL) receives the number of wave groups that split the K
  * stages of one tile inside its workgroup (1 = no split; the groups' int32

@@ -334,6 +334,29 @@ def test_product_path_fails_loudly_without_library(monkeypatch, tmp_path):
         T._lib.load()
 
 
+def test_mxfp4_chooser_rules():
+    """The MXFP4 chooser takes the 256x256 tile on the CogVideoX linears (K a multiple
+    of 128), never for K that is not (its byte-scale variant spills), and always a
+    valid index; negative sizes and K < 1 are rejected."""
+    import random
+    n = T.mxfp4_config_info()
+    info = [T.mxfp4_config_info(i) for i in range(n)]
+    for (M, N, K) in [(17776, 7680, 1920), (17776, 1920, 7680), (17776, 5760, 1920)]:
+        assert info[T.mxfp4_config_choose(M, N, K)] == (256, 256), (M, N, K)
+    rng = random.Random(11)
+    for _ in range(2000):
+        M = rng.choice([1, 17, 64, 256, 1024, 4096, 17776]) + rng.randrange(0, 300)
+        N = 32 * rng.randrange(1, 320)
+        K = 32 * rng.randrange(1, 400)
+        c = T.mxfp4_config_choose(M, N, K, rng.choice([0, 80, 256, 304]))
+        assert 0 <= c < n
+        if K % 128:
+            assert info[c] != (256, 256), (M, N, K)
+    for bad in [(-1, 32, 32), (32, -1, 32), (32, 32, 0)]:
+        with pytest.raises(T.TabitError):
+            T.mxfp4_config_choose(*bad)
+
+
 def test_int8_chooser_split_rules():
     """Over seeded random shapes: a K-split tile only when the same tile's
     workgroups fit in one round over the CUs, two-group tiles only from 32 K

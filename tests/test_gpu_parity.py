@@ -203,7 +203,8 @@ def _check_mx(y_gpu, acc_gpu, xf, xe, wf, we, scale):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 32, 32), (17, 96, 96), (300, 416, 2240), (129, 64, 1920),
-                                   (520, 288, 544)])
+                                   (520, 288, 544), (600, 544, 1024), (257, 288, 128),
+                                   (513, 800, 384)])
 def test_mxfp4_gemm(ctx, M, N, K):
     """Every MXFP4 tile configuration against the exact fp64 product."""
     rng = np.random.default_rng(M * N + K)

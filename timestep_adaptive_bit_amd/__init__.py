@@ -7,7 +7,8 @@ raises if the library has not been built.
 """
 from ._lib import (  # noqa: F401
     Context, Layer, TabitError, load, version, act_workspace_bytes, gemm_config_info,
-    gemm_config_choose, mxfp4_config_info, plane_config_info, plane_config_choose,
+    gemm_config_choose, mxfp4_config_info, mxfp4_config_choose, plane_config_info,
+    plane_config_choose,
     weight_planes_bytes,
     dmpq_workspace_bytes, noalloc_scratch_bytes,
     header_functions, LIB_PATH,
@@ -22,6 +23,7 @@ __all__ = [
     "gemm_config_choose", "header_functions", "FMT_INT8", "FMT_MXFP4", "PATH_MASKED",
     "PATH_BITSERIAL", "PATH_PLANES", "OPT_GEMM_CONFIG", "OPT_MXFP4_CONFIG", "OPT_PLANE_CONFIG",
     "plane_config_info", "plane_config_choose", "weight_planes_bytes", "dmpq_workspace_bytes",
+    "mxfp4_config_choose",
     "PATH_HQDM", "OPT_HQDM_CONFIG", "hqdm_config_info", "noalloc_scratch_bytes",
     "ACT_NONE", "ACT_GELU",
 ]

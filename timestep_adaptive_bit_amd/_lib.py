@@ -71,6 +71,7 @@ _SIGNATURES = {
                                    _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
     "tabit_plane_config_info": (_c_int, [_c_int, _PINT, _PINT, _PINT]),
     "tabit_plane_config_choose": (_c_int, [_c_int, _c_int, _c_int, _c_int]),
+    "tabit_mxfp4_config_choose": (_c_int, [_c_int, _c_int, _c_int, _c_int]),
     "tabit_mfma_peak_probe": (_c_int, [_c_void_p, _c_int, _c_int, _c_void_p, _c_size_t,
                                        ctypes.POINTER(ctypes.c_double), _c_void_p]),
     "tabit_mfma_probe_sink_ints": (_c_size_t, [_c_int]),
@@ -227,6 +228,14 @@ def plane_config_info(index: int = -1):
 def plane_config_choose(M: int, N: int, K: int, num_cus: int = 0) -> int:
     """Index of the plane-major GEMM configuration the library picks for M x N x K."""
     st = int(load().tabit_plane_config_choose(M, N, K, num_cus))
+    if st < 0:
+        raise TabitError(st, "bad shape")
+    return st
+
+
+def mxfp4_config_choose(M: int, N: int, K: int, num_cus: int = 0) -> int:
+    """Index of the MXFP4 GEMM configuration the library picks for M x N x K."""
+    st = int(load().tabit_mxfp4_config_choose(M, N, K, num_cus))
     if st < 0:
         raise TabitError(st, "bad shape")
     return st

@@ -889,6 +889,11 @@ int tabit_mxfp4_config_info(int index, int* bm, int* bn) {
   return TABIT_OK;
 }
 
+int tabit_mxfp4_config_choose(int M, int N, int K, int num_cus) {
+  if (M < 0 || N < 0 || K < 1) return TABIT_EINVAL;
+  return tabit::mx_config_choose(M, N, K, num_cus);
+}
+
 int tabit_plane_config_info(int index, int* bm, int* bn, int* k_groups) {
   if (index < 0) return tabit::plane_config_count();
   if (index >= tabit::plane_config_count() || bm == nullptr || bn == nullptr) return TABIT_EINVAL;
