@@ -295,6 +295,27 @@ def summarize_pmc(dirs) -> None:
                   f"LDS bytes read {m.get('SQ_INSTS_LDS_LOAD_BANDWIDTH', 0) * 64 / 1e9:.2f} GB")
 
 
+def summarize_k_fetch(root: str, group: int) -> None:
+    """Mean FETCH_SIZE (KiB, as the counter reports) per k of a --k-sweep counter
+    run: per GEMM kernel, its last 8 x `group` dispatches are the sweep's k = 0..7
+    blocks (2 warm-up launches, then group - 2 timed), warm-ups left out."""
+    import sqlite3
+    rows = {}
+    for db in sorted(glob.glob(os.path.join(root, "**", "*.db"), recursive=True)):
+        c = sqlite3.connect(db)
+        for d, name, v in c.execute("select dispatch_id, kernel_name, value from counters_collection "
+                                    "where counter_name = 'FETCH_SIZE' order by dispatch_id"):
+            k = name.replace("void ", "").replace("tabit::(anonymous namespace)::", "").split("(")[0]
+            rows.setdefault(k, []).append(v)
+    for k in sorted(rows):
+        v = rows[k]
+        if not k.startswith("gemm_") or len(v) < 8 * group:
+            continue
+        tail = v[-8 * group:]
+        per_k = [sum(tail[j * group + 2:(j + 1) * group]) / (group - 2) for j in range(8)]
+        print(f"{k}  FETCH KiB per k = 0..7: " + " ".join(f"{x:.1f}" for x in per_k))
+
+
 def copy_calibration(mib: int) -> None:
     """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
     import torch
@@ -875,6 +896,8 @@ def main() -> int:
                     default=None, help="only print MFMA and quantizer HBM counter evidence")
     ap.add_argument("--single-gemm", nargs=4, type=int, metavar=("M", "N", "K", "CFG"),
                     default=None, help="only launch one masked GEMM --reps times (counter passes)")
+    ap.add_argument("--summarize-k-fetch", nargs=2, metavar=("DIR", "GROUP"), default=None,
+                    help="per-k mean FETCH_SIZE of a --k-sweep counter run (GROUP dispatches per k)")
     ap.add_argument("--single-mxfp4", nargs=4, type=int, metavar=("M", "N", "K", "CFG"),
                     help="only run REPS launches of one MXFP4 GEMM (for counter passes)")
     ap.add_argument("--reps", type=int, default=3, help="launches for --single-gemm / --single-mxfp4")
@@ -886,6 +909,9 @@ def main() -> int:
         return 0
     if args.single_mxfp4:
         single_mxfp4(args.single_mxfp4, args.reps)
+        return 0
+    if args.summarize_k_fetch:
+        summarize_k_fetch(args.summarize_k_fetch[0], int(args.summarize_k_fetch[1]))
         return 0
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc)
