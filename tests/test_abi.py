@@ -335,14 +335,17 @@ def test_product_path_fails_loudly_without_library(monkeypatch, tmp_path):
 
 
 def test_mxfp4_chooser_rules():
-    """The MXFP4 chooser takes the 256x256 tile on the CogVideoX linears (K a multiple
-    of 128), never for K that is not (its byte-scale variant spills), and always a
-    valid index; negative sizes and K < 1 are rejected."""
+    """The MXFP4 chooser takes the 256x256 tile on the wide CogVideoX linears and
+    256x192 where N = 1920 (K a multiple of 128), never 256x256 for K that is not
+    (its byte-scale variant spills), and always a valid index; negative sizes and
+    K < 1 are rejected."""
     import random
     n = T.mxfp4_config_info()
     info = [T.mxfp4_config_info(i) for i in range(n)]
-    for (M, N, K) in [(17776, 7680, 1920), (17776, 1920, 7680), (17776, 5760, 1920)]:
+    for (M, N, K) in [(17776, 7680, 1920), (17776, 5760, 1920)]:
         assert info[T.mxfp4_config_choose(M, N, K)] == (256, 256), (M, N, K)
+    for (M, N, K) in [(17776, 1920, 7680), (17776, 1920, 1920)]:
+        assert info[T.mxfp4_config_choose(M, N, K)] == (256, 192), (M, N, K)
     rng = random.Random(11)
     for _ in range(2000):
         M = rng.choice([1, 17, 64, 256, 1024, 4096, 17776]) + rng.randrange(0, 300)
