@@ -222,6 +222,27 @@ def test_mxfp4_gemm(ctx, M, N, K):
         ctx.set_option(T.OPT_MXFP4_CONFIG, -1)
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 416, 1024), (129, 96, 2240)])
+def test_mxfp4_gemm_acc_only(ctx, M, N, K):
+    """The fp32 accumulator alone (no bf16 output, so no epilogue barrier), every tile
+    configuration, twice in a row, against the exact fp64 product."""
+    rng = np.random.default_rng(M + N * K)
+    xf = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    wf = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    xe = rng.integers(118, 136, size=(M, K // 32), dtype=np.uint8)
+    we = rng.integers(118, 136, size=(N, K // 32), dtype=np.uint8)
+    d = [torch.from_numpy(a).to(DEV) for a in (xf, xe, wf, we)]
+    try:
+        for cfg in range(T.mxfp4_config_info()):
+            ctx.set_option(T.OPT_MXFP4_CONFIG, cfg)
+            for _ in range(2):
+                y, acc = ctx.mxfp4_qgemm(*d, 1 / 32, want_y=False, want_acc=True)
+                assert y is None
+                _check_mx(None, _np(acc).astype(np.float64), xf, xe, wf, we, 1 / 32)
+    finally:
+        ctx.set_option(T.OPT_MXFP4_CONFIG, -1)
+
+
 # ------------------------------------------------------------ whole linear, schedule driver
 def test_single_linear_config_full(ctx):
     """64 tokens x 1152, W 1152x1152, b = 64, 4 steps k = [0, 2, 4, 3], both paths, in full."""

@@ -240,6 +240,10 @@ gemm_mxfp4_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ AE,
     }
   }
 
+  // the stages issued past K may still be landing (zeros) in LDS: drain them
+  // before the workgroup ends or anything below reuses LDS
+  tile::wait_vmcnt0();
+
   // Block (i, j) holds Y^T: lane l, register r is row i*32 + l%32 and column
   // j*32 + (r/4)*8 + (l/32)*4 + r%4 of the wave tile (four consecutive columns
   // per group of four registers), as in the INT8 GEMM's epilogue.
