@@ -49,7 +49,6 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-using tile::BKB;
 
 template <int BM, int BN, int WM, int WN, int RB, int NST, int KW, bool BITSERIAL>
 __global__ void __launch_bounds__(WM* WN * KW * 64)

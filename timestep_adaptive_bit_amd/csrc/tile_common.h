@@ -12,7 +12,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int BKB = 128;                  // bytes of K per LDS stage row (MXFP4 kernel)
 constexpr unsigned kOOB = 0x80000000u;    // buffer offset past any operand: loads return 0
 constexpr int kRsrcFlags = 0x00020000;    // raw buffer descriptor word 3 for gfx9-family parts
 
@@ -114,40 +113,11 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
   tn = in_g / gsz;
 }
 
-// Stage a wave's WTM x WTN bf16 result in LDS and write it out as 16-byte,
-// row-contiguous stores.  16-byte column chunks are XOR-swizzled by the row so
-// the MFMA-layout writes (lane l: rows 4*(l/16)+r, column l%16) and the
-// row-contiguous reads avoid bank conflicts.  `val(i, j, r)` gives the bf16 of
-// fragment (i, j), register r.
-template <int WTM, int WTN, typename F>
-__device__ __forceinline__ void store_tile_bf16(uint16_t* st, int lane, uint16_t* __restrict__ Y,
-                                                int row0, int col0, int M, int N, F val) {
-  constexpr int FM = WTM / 16, FN = WTN / 16, CH = WTN / 8;
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int lr = i * 16 + 4 * (lane >> 4) + r;
-        const int lc = j * 16 + (lane & 15);
-        const int ch = (lc >> 3) ^ (lr & (CH - 1));
-        st[lr * WTN + ch * 8 + (lc & 7)] = val(i, j, r);
-      }
-  __syncthreads();
-#pragma unroll
-  for (int it = 0; it < WTM * CH / 64; ++it) {
-    const int idx = it * 64 + lane;
-    const int lr = idx / CH, ch = idx % CH;
-    const int gm = row0 + lr, gn = col0 + ch * 8;
-    const uint4 v = *reinterpret_cast<const uint4*>(st + lr * WTN + ((ch ^ (lr & (CH - 1))) * 8));
-    if (gm < M && gn < N) *reinterpret_cast<uint4*>(Y + (size_t)gm * N + gn) = v;
-  }
-}
-
-// As store_tile_bf16, for the 32x32 MFMA output layout: fragment (i, j) is a
-// 32 x 32 block; lane l, register r holds row (r/4)*8 + (l/32)*4 + r%4, column
-// l%32.  `val(i, j, r)` gives the bf16 of fragment (i, j), register r.  The
+// Epilogue of a wave tile WTM x WTN through its LDS staging `st`: MFMA-layout
+// writes of the bf16 values, one barrier, then row-contiguous 16-byte global
+// stores.  For the 32x32 MFMA output layout: fragment (i, j) is a 32 x 32
+// block; lane l, register r holds row (r/4)*8 + (l/32)*4 + r%4, column l%32.
+// `val(i, j, r)` gives the bf16 of fragment (i, j), register r.  The
 // chunk swizzle XORs within aligned groups of SW chunks, SW the largest power
 // of two dividing the row's chunk count (12 chunks of a 96-wide tile: 4).  The
 // global stores are nontemporal (1.6-5% faster on MI355X than plain stores for
