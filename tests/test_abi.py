@@ -385,3 +385,36 @@ def test_int8_chooser_split_rules():
         assert -(-stages // kg) < stages or stages == 1, (M, N, K, info[c])
         if kg == 2:
             assert stages >= 32, (M, N, K, info[c])
+
+
+def test_int8_chooser_deep_ring_rule():
+    """The three-stage 128 x 192 and 128 x 96 tiles (the second table entry of
+    each shape with one K group) replace the two-stage tile only when its
+    workgroups fit in one round and K has 16 to 31 stages; from 32 stages the
+    two-group split takes over, below 16 the two-stage tile stays."""
+    n = T.gemm_config_info()
+    info = [T.gemm_config_info(i) for i in range(n)]
+
+    def entries(shape):
+        return [i for i in range(n) if info[i] == shape]
+
+    two192, deep192 = entries((128, 192, 1))
+    two96, deep96 = entries((128, 96, 1))
+    assert T.gemm_config_choose(1024, 5600, 2240, 256) == deep192    # 18 stages, 240 tiles
+    assert T.gemm_config_choose(1024, 2240, 2240, 256) == deep96     # 18 stages, 192 tiles
+    assert T.gemm_config_choose(4096, 1152, 1152, 256) == two192     # 9 stages
+    assert T.gemm_config_choose(4096, 1280, 1280, 256) == two192     # 10 stages
+    assert info[T.gemm_config_choose(4096, 1152, 4608, 256)] == (128, 192, 2)   # 36 stages
+    import random
+    rng = random.Random(9)
+    for _ in range(2000):
+        M = rng.choice([1, 64, 256, 512, 1024, 2048, 4096]) + rng.randrange(0, 64)
+        N = 32 * rng.randrange(1, 320)
+        K = 32 * rng.randrange(1, 1024)
+        cus = rng.choice([0, 80, 256, 304])
+        c = T.gemm_config_choose(M, N, K, cus)
+        if c in (deep192, deep96):
+            bm, bn, _ = info[c]
+            stages = -(-K // 128)
+            assert 16 <= stages < 32, (M, N, K, cus)
+            assert -(-M // bm) * -(-N // bn) <= (cus or 256), (M, N, K, cus)

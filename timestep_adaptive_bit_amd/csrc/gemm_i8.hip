@@ -20,7 +20,8 @@
 // register staging; rows and chunks out of range arrive as zeros) into an
 // NST-deep ring of LDS stages: up to NST-1 stages are in flight, so the
 // copy latency (an L2 miss costs about as much as a stage of MFMAs) hides
-// under the compute.  One barrier per stage.  The step's LSB mask is applied to the weight
+// under the compute.  One barrier per stage; it waits only for LDS accesses,
+// each wave having first waited by count for its own copies of the stage.  The step's LSB mask is applied to the weight
 // fragments as they come out of LDS (four v_and per 16-byte fragment).  The
 // matrix-core op is v_mfma_i32_32x32x32_i8 (it sustains ~90% of the chip's INT8
 // rate with a few independent accumulators per wave), with the weight fragment
@@ -68,8 +69,10 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
   static_assert(KW >= 1 && (KW - 1) * BM * BN * 4 <= KW * NST * STAGE,
                 "the K groups' partial accumulators must fit in the LDS stages");
   static_assert(NW * KW * 64 <= 1024, "at most 1024 threads per workgroup");
-  static_assert(NST == 2 || (BM % (1024 / RB * NW) == 0 && BN % (1024 / RB * NW) == 0),
-                "deeper rings count copies per wave: every wave copies the same share");
+  // Deeper rings wait by count: DPW is the smallest per-wave share of a
+  // stage's copies; a wave that copies one block more (blocks that do not
+  // split evenly) then also waits for one copy of the next stage, which is
+  // only stricter.
   // the ring (the K groups' partial sums and the epilogue's bf16 staging reuse it,
   // the staging extending it where larger), then the tile's scales when they fit:
   // SA of its BM rows, SB of its BN columns (padded to whole waves of 64 entries)
@@ -146,7 +149,9 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
     if (NST >= 4 && ahead >= 2) tile::wait_vmcnt<(NST >= 4 ? 2 : 0) * DPW>();
     else if (NST >= 3 && ahead >= 1) tile::wait_vmcnt<(NST >= 3 ? 1 : 0) * DPW>();
     else tile::wait_vmcnt<0>();
-    __syncthreads();   // stage kt visible to all; stage kt-1's buffer free for reuse
+    // stage kt visible to all; stage kt-1's buffer free for reuse (the copies
+    // of later stages stay in flight: __syncthreads would wait for them too)
+    tile::lds_barrier();
     if constexpr (KW > 1) {
       if (kt >= nk) continue;   // this group's range is done (the barrier above still counts it)
     }
@@ -342,7 +347,7 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
 struct CfgDesc {
   int bm, bn, wm, wn, rb, nst, kw;
   float rate;       // relative throughput per CU on its tiles (fitted to MI355X sweeps)
-  int min_stages;   // K-split variants: taken only from this many K stages on
+  int min_stages;   // K-split and deeper-ring variants: taken only from this many K stages on
 };
 // Twelve or sixteen waves per large tile (wave tiles of 64 x 64 or 64 x 96):
 // on MI355X these beat the same tiles with eight waves of 128 x 64 by 3-15%
@@ -359,6 +364,12 @@ struct CfgDesc {
 // with its own ring) pay only on long K: PixArt MLP-down 4096 x 1152 x 4608
 // 31.8 -> 29.3 us, 4096 x 1280 x 5120 35.7 -> 33.9 us, SANA MLP-down
 // 1024 x 2240 x 5600 42.7 -> 38.9 us, but 11.8 -> 12.8 us at K = 1152.
+// The three-stage 128 x 192 and 128 x 96 tiles keep two stages in flight
+// instead of one; they replace the two-stage tile from 16 K stages on (below
+// the K split's 32): SANA MLP-up 1024 x 5600 x 2240 24.5-25.1 -> 21.6-21.9 us,
+// SANA out 1024 x 2240 x 2240 (128 x 96) 13.7 -> 12.8-13.0 us; at 9-10 stages
+// (4096 x 1152 x 1152, 4096 x 1280 x 1280) they are 3-5% slower, and a
+// three-stage 128 x 128 tile was 11% slower at 1024 x 6720 x 2240.
 // index, BM, BN, WM, WN, stage row bytes, LDS stages, K groups, rate, min stages
 #define TABIT_I8_CONFIGS(X)                    \
   X(0, 256, 256, 4, 4, 128, 2, 1, 1.00f, 0)     \
@@ -371,7 +382,9 @@ struct CfgDesc {
   X(7, 64, 64, 2, 2, 128, 2, 3, 0.48f, 2)       \
   X(8, 128, 192, 2, 3, 128, 2, 2, 0.71f, 32)   \
   X(9, 128, 96, 2, 3, 128, 2, 2, 0.58f, 32)    \
-  X(10, 64, 64, 2, 2, 128, 2, 4, 0.48f, 2)
+  X(10, 64, 64, 2, 2, 128, 2, 4, 0.48f, 2)      \
+  X(11, 128, 192, 4, 3, 128, 3, 1, 0.71f, 16)   \
+  X(12, 128, 96, 4, 3, 128, 3, 1, 0.58f, 16)
 #define TABIT_DESC(I, BM, BN, WM, WN, RB, NST, KW, RATE, MS) {BM, BN, WM, WN, RB, NST, KW, RATE, MS},
 constexpr CfgDesc kCfgs[] = {TABIT_I8_CONFIGS(TABIT_DESC)};
 #undef TABIT_DESC
@@ -416,7 +429,7 @@ int gemm_config_choose(int M, int N, int K, int num_cus) {
   double best_cost = 1e300;
   for (int i = 0; i < kNumCfgs; ++i) {
     const CfgDesc& c = kCfgs[i];
-    if (c.kw != 1) continue;
+    if (c.kw != 1 || c.nst != 2) continue;
     const long long per_cu = (tiles_of(c) + num_cus - 1) / num_cus;
     const double cost = (double)per_cu * c.bm * c.bn / c.rate;
     if (cost < best_cost * 0.999) {
@@ -446,7 +459,15 @@ int gemm_config_choose(int M, int N, int K, int num_cus) {
       pick_kw = c.kw;
     }
   }
-  return pick;
+  if (pick != best) return pick;
+  // no split taken (for these tiles: fewer than 32 stages): the same tile's
+  // deeper ring from its minimum stage count on
+  for (int i = 0; i < kNumCfgs; ++i) {
+    const CfgDesc& c = kCfgs[i];
+    if (c.kw == 1 && c.nst > 2 && c.bm == b.bm && c.bn == b.bn && c.rb == b.rb && S >= c.min_stages)
+      return i;
+  }
+  return best;
 }
 
 hipError_t launch_gemm_i8(int cfg, bool bitserial, const int8_t* xq, const float* sa,
