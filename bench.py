@@ -41,11 +41,35 @@ GEMM_SOURCES = [os.path.join(ROOT, "timestep_adaptive_bit_amd", "csrc", f)
                 for f in ("gemm_i8.hip", "tile_common.h")]
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and with whitespace runs collapsed: edits to
+    comments or layout leave the kernel, and so its counters, unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        if text.startswith("//", i):
+            i = text.find("\n", i)
+            i = n if i < 0 else i
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif text[i] == '"':           # string literal: kept as written
+            j = i + 1
+            while j < n and text[j] != '"':
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(text[i])
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def gemm_source_hash() -> str:
     h = hashlib.sha256()
     for f in GEMM_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -32,3 +32,17 @@ def test_recorded_traffic_matches_the_gemm_sources():
     else:
         assert bench.recorded_traffic(rec["workload"], rec["path"]) is None
     assert bench.recorded_traffic("no such workload", rec["path"]) is None
+
+
+def test_source_hash_ignores_comments_only():
+    """The traffic record stays valid across comment and layout edits of the
+    GEMM sources, and not across code edits."""
+    sys.path.insert(0, ROOT)
+    import bench
+    src = "int f(int a) { // sum\n  return a + 1; /* one */ }\nconst char* s = \"// kept\";\n"
+    base = bench._code_only(src)
+    assert bench._code_only(src.replace("// sum", "// total").replace("/* one */", "")) == base
+    assert bench._code_only(src.replace("a + 1", "a + 2")) != base
+    assert bench._code_only(src.replace("\"// kept\"", "\"// gone\"")) != base
+    assert "// kept" in base and "sum" not in base
+

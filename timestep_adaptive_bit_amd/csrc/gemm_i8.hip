@@ -16,12 +16,12 @@
 //
 // Both operands are K-contiguous ([M][K] and [N][K]).  A workgroup of WM x WN
 // waves computes a BM x BN tile; K advances in 128-byte stages copied straight
-// from global memory into a double-buffered LDS tile by buffer loads (no
-// register staging; rows and chunks out of range arrive as zeros) into an
-// NST-deep ring of LDS stages: up to NST-1 stages are in flight, so the
-// copy latency (an L2 miss costs about as much as a stage of MFMAs) hides
-// under the compute.  One barrier per stage; it waits only for LDS accesses,
-// each wave having first waited by count for its own copies of the stage.  The step's LSB mask is applied to the weight
+// from global memory by buffer loads (no register staging; rows and chunks out
+// of range arrive as zeros) into an NST-deep ring of LDS stages: up to NST-1
+// stages are in flight, so the copy latency (an L2 miss costs about as much as
+// a stage of MFMAs) hides under the compute.  One barrier per stage; it waits
+// only for LDS accesses, each wave having first waited by count for its own
+// copies of the stage.  The step's LSB mask is applied to the weight
 // fragments as they come out of LDS (four v_and per 16-byte fragment).  The
 // matrix-core op is v_mfma_i32_32x32x32_i8 (it sustains ~90% of the chip's INT8
 // rate with a few independent accumulators per wave), with the weight fragment
@@ -63,7 +63,7 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA,
   constexpr int FM = WTM / 32, FN = WTN / 32;   // 32 x 32 MFMA blocks per wave
   constexpr int KS = RB / 32;                   // MFMA K-steps (32 bytes) per stage
   constexpr int STAGE = (BM + BN) * RB;
-  constexpr int DPW = STAGE / 1024 / NW;        // DMA instructions per wave per stage
+  constexpr int DPW = STAGE / 1024 / NW;        // DMA instructions per wave per stage (at least)
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold whole 32x32 blocks");
   static_assert(NST >= 2 && NST <= 4, "2 to 4 LDS stages");
   static_assert(KW >= 1 && (KW - 1) * BM * BN * 4 <= KW * NST * STAGE,
